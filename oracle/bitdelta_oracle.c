@@ -1,0 +1,266 @@
+/*
+ * BitDelta oracle: plain, slow, obviously correct CPU reference.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no source, header, table or helper with
+ * the GPU library, and it includes nothing from it.
+ *
+ * Source of the method: "BitDelta: Serving 14 Zen Models from One GPU
+ * Cluster" (hanzo.blog, 2026-02-28; the same post in Indonesian, Simplified
+ * Chinese and Arabic).  Sections cited below by their English headings:
+ *   [MF]  "Mathematical Foundation": the task delta, the 1-bit code
+ *         W_ft ~= W_base + alpha * sign(Delta), alpha = (1/n)||Delta||_1.
+ *   [SA]  "Serving Architecture": step 3 of the request flow rebuilds
+ *         W_eff = W_base + alpha * sign(Delta); the conceptual
+ *         fused_bitdelta_linear sketch (unpack to {-1,+1}, add
+ *         alpha[:,None] * signs, then a plain linear y = x W_eff^T).
+ *   [ID]  "Infrastructure Details": storage format, signs packed 8 per byte
+ *         ([4096,4096] -> [4096,512]) and fp32 alpha, one per output row.
+ *
+ * Readings where the post is silent (each one is listed in the design notes):
+ *   R1 sign(0): Delta >= 0 (including -0) is stored as bit 1 = +1; bit 0 = -1.
+ *   R2 bit order: column j of a row is bit (j & 7) of byte (j >> 3).
+ *   R3 Delta_ij is the fp32 difference fl32(W_ft - W_base).
+ *   R4 alpha: the |Delta| values are summed in fp64 in a fixed order (below),
+ *      and the mean is rounded once to fp32, the storage format of [ID].
+ *      Per-row mode (one alpha per output row, [ID]) and per-matrix mode
+ *      (one scalar, [MF]) are both provided.
+ *   R5 W_eff = bf16_rne(fl32(f32(W_base) + (+/-alpha))): the sketch's mixed
+ *      dtypes are resolved by adding in fp32 and rounding once to bf16.
+ *   R6 linear: y = x W_eff^T accumulated in fp64 (products of two bf16 values
+ *      are exact in fp64).  The GPU returns bf16; tests compare against y64.
+ *
+ * Fixed summation order for alpha (R4).  For row r with C columns, split the
+ * columns into 8-column groups g = 0 .. C/8-1.  There are 256 fp64 partial
+ * sums p[0..255], all +0.  Groups are visited in increasing g; group g adds
+ * its eight |Delta| values, in increasing column order, into p[g mod 256].
+ * Then for s = 128, 64, ..., 1: p[k] = p[k] + p[k+s] for k < s.  S_r = p[0].
+ * Per-row:    alpha_r = (float)(S_r / C)                (fp64 divide, one RNE)
+ * Per-matrix: q[0..255] = +0; for r increasing, q[r mod 256] += S_r; the same
+ *             halving tree; alpha = (float)(q[0] / (R*C)).
+ *
+ * Parity pins for every function here live in the CPU test tier: hand-built
+ * bytes and ties, closed-form means, an exact rational (math.fsum) mean,
+ * Laplace statistics, least-squares optimality of alpha, and brute-force
+ * exact-rational matrix products on tiny inputs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- bf16 <-> fp32 from the IEEE 754 binary32 layout ------------------- */
+
+/* bf16 is the upper 16 bits of a binary32; widening is exact. */
+float oracle_f32_from_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 to the nearest bf16, ties to even.  NaN becomes the
+ * canonical quiet NaN 0x7FC0; Inf stays Inf; overflow rounds to Inf;
+ * subnormals are kept (no flush to zero). */
+uint16_t oracle_bf16_from_f32(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return 0x7FC0;
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* ---- helpers ------------------------------------------------------------ */
+
+static float w_ft_at(const void *w_ft, int ft_is_f32, int64_t idx)
+{
+    if (ft_is_f32)
+        return ((const float *)w_ft)[idx];
+    return oracle_f32_from_bf16(((const uint16_t *)w_ft)[idx]);
+}
+
+/* The halving tree over 256 fp64 partial sums used by R4. */
+static double halving_tree_256(double *p)
+{
+    for (int s = 128; s >= 1; s >>= 1)
+        for (int k = 0; k < s; ++k)
+            p[k] = p[k] + p[k + s];
+    return p[0];
+}
+
+/* Signed scale for one weight: bit 1 -> +alpha, bit 0 -> -alpha ([SA]
+ * sketch: unpack to {-1,+1} then multiply by alpha; the product is exact). */
+static float signed_alpha(const uint8_t *sign_row, int64_t j, float a)
+{
+    int bit = (sign_row[j >> 3] >> (j & 7)) & 1;
+    return bit ? a : -a;
+}
+
+/* ---- compress: Delta, sign, pack, alpha ([MF], [ID]) -------------------- */
+
+/* w_base: bf16 bits [R, C]; w_ft: fp32 or bf16 [R, C]; signs out [R, C/8];
+ * alpha out [R] (per_matrix = 0) or [1] (per_matrix = 1).
+ * row_sum_out (may be NULL): the fp64 S_r of every row.
+ * Returns 0, or -1 when C is not a multiple of 8 or a size is negative. */
+int oracle_compress(const uint16_t *w_base, const void *w_ft, int ft_is_f32,
+                    int64_t R, int64_t C, int per_matrix,
+                    uint8_t *signs, float *alpha, double *row_sum_out)
+{
+    if (R < 0 || C <= 0 || C % 8 != 0)
+        return -1;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    if (!S)
+        return -2;
+    int64_t groups = C / 8;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        double p[256];
+        for (int k = 0; k < 256; ++k)
+            p[k] = 0.0;
+        for (int64_t g = 0; g < groups; ++g) {
+            uint8_t byte = 0;
+            for (int i = 0; i < 8; ++i) {
+                int64_t j = 8 * g + i;
+                int64_t idx = r * C + j;
+                float d = w_ft_at(w_ft, ft_is_f32, idx) - oracle_f32_from_bf16(w_base[idx]);
+                if (d >= 0.0f)
+                    byte |= (uint8_t)(1u << i);
+                p[g % 256] = p[g % 256] + (double)fabsf(d);
+            }
+            signs[r * groups + g] = byte;
+        }
+        S[r] = halving_tree_256(p);
+    }
+
+    if (!per_matrix) {
+        for (int64_t r = 0; r < R; ++r)
+            alpha[r] = (float)(S[r] / (double)C);
+    } else {
+        double q[256];
+        for (int k = 0; k < 256; ++k)
+            q[k] = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            q[r % 256] = q[r % 256] + S[r];
+        double T = halving_tree_256(q);
+        alpha[0] = (float)(T / ((double)R * (double)C));
+    }
+    if (row_sum_out)
+        memcpy(row_sum_out, S, sizeof(double) * (size_t)R);
+    free(S);
+    return 0;
+}
+
+/* ---- reconstruct: W_eff = W_base + alpha * sign(Delta) ([MF], [SA]) ----- */
+
+static uint16_t weff_at(const uint16_t *w_base, const uint8_t *signs, const float *alpha,
+                        int per_matrix, int64_t C, int64_t r, int64_t j)
+{
+    float a = per_matrix ? alpha[0] : alpha[r];
+    float w = oracle_f32_from_bf16(w_base[r * C + j]);
+    float e = w + signed_alpha(signs + r * (C / 8), j, a);
+    return oracle_bf16_from_f32(e);
+}
+
+int oracle_reconstruct(const uint16_t *w_base, const uint8_t *signs, const float *alpha,
+                       int per_matrix, int64_t R, int64_t C, uint16_t *w_eff)
+{
+    if (R < 0 || C <= 0 || C % 8 != 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t j = 0; j < C; ++j)
+            w_eff[r * C + j] = weff_at(w_base, signs, alpha, per_matrix, C, r, j);
+    return 0;
+}
+
+/* ---- linear: y = x W_eff^T in fp64 ([SA] sketch, last line) ------------- */
+
+/* x: bf16 [M, C].  rows: the output rows (W rows) to compute, n_rows of them
+ * (NULL means all R rows in order).  y64 out [M, n_rows]; scale out
+ * [M, n_rows] = sum_j |x_mj| * |W_eff_rj| (the normaliser of the tolerance).
+ * W_eff rows are rebuilt one at a time with the reconstruct formula. */
+int oracle_linear_rows(const uint16_t *x, int64_t M, const uint16_t *w_base,
+                       const uint8_t *signs, const float *alpha, int per_matrix,
+                       int64_t R, int64_t C, const int64_t *rows, int64_t n_rows,
+                       double *y64, double *scale)
+{
+    if (M < 0 || R < 0 || C <= 0 || C % 8 != 0)
+        return -1;
+    if (!rows)
+        n_rows = R;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        int64_t r = rows ? rows[t] : t;
+        double *we = (double *)malloc(sizeof(double) * (size_t)C);
+        for (int64_t j = 0; j < C; ++j)
+            we[j] = (double)oracle_f32_from_bf16(weff_at(w_base, signs, alpha, per_matrix, C, r, j));
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, sc = 0.0;
+            for (int64_t j = 0; j < C; ++j) {
+                double xv = (double)oracle_f32_from_bf16(x[m * C + j]);
+                acc += xv * we[j];
+                sc += fabs(xv) * fabs(we[j]);
+            }
+            y64[m * n_rows + t] = acc;
+            if (scale)
+                scale[m * n_rows + t] = sc;
+        }
+        free(we);
+    }
+    return 0;
+}
+
+/* ---- grouped: each token uses its own variant's signs and alpha ---------
+ * ([SA] diagram: one HBM-resident W_base read by every variant in the delta
+ * cache).  signs [V, R, C/8]; alpha [V, R] (per-row) or [V] (per-matrix).
+ * A token whose id is outside [0, V) gets y = 0 and scale = 0.  Columns of
+ * the outputs are the W rows listed in `rows` (NULL = all R). */
+int oracle_linear_grouped_rows(const uint16_t *x, int64_t M, const int32_t *ids, int32_t V,
+                               const uint16_t *w_base, const uint8_t *signs,
+                               const float *alpha, int per_matrix, int64_t R, int64_t C,
+                               const int64_t *rows, int64_t n_rows,
+                               double *y64, double *scale)
+{
+    if (M < 0 || R < 0 || C <= 0 || C % 8 != 0 || V <= 0)
+        return -1;
+    if (!rows)
+        n_rows = R;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        int32_t v = ids[m];
+        for (int64_t t = 0; t < n_rows; ++t) {
+            double acc = 0.0, sc = 0.0;
+            if (v >= 0 && v < V) {
+                int64_t r = rows ? rows[t] : t;
+                const uint8_t *sv = signs + (int64_t)v * R * (C / 8);
+                const float *av = per_matrix ? alpha + v : alpha + (int64_t)v * R;
+                for (int64_t j = 0; j < C; ++j) {
+                    double xv = (double)oracle_f32_from_bf16(x[m * C + j]);
+                    double w = (double)oracle_f32_from_bf16(weff_at(w_base, sv, av, per_matrix, C, r, j));
+                    acc += xv * w;
+                    sc += fabs(xv) * fabs(w);
+                }
+            }
+            y64[m * n_rows + t] = acc;
+            if (scale)
+                scale[m * n_rows + t] = sc;
+        }
+    }
+    return 0;
+}
+
+/* Threads the OpenMP runtime will use (reported next to oracle timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n); }
+#else
+int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
+#endif

@@ -1,0 +1,348 @@
+"""Pins of the oracle to facts other than itself.
+
+Each pin takes an oracle build `o` (oracle.Oracle) and raises AssertionError on
+a mismatch.  The sources of truth are the post ("BitDelta: Serving 14 Zen
+Models from One GPU Cluster", hanzo.blog 2026-02-28), closed forms,
+independent libraries (torch's bf16 conversion, numpy's bit unpacking and
+float64 matmul, Python's exact math.fsum and fractions) and hand-derived
+fixtures under tests/golden/.  They are chosen so that a plausible slip in the
+oracle (a dropped term, a wrong sign, bit order or index, a transposed
+operand, a wrong divisor) fails at least one of them; tests/test_oracle_mutants.py
+checks exactly that on deliberately broken builds.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _json(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f32_bits(h: str) -> np.float32:
+    return np.array([int(h, 16)], dtype=np.uint32).view(np.float32)[0]
+
+
+def _torch_bf16_bits(vals: np.ndarray) -> np.ndarray:
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _torch_widen(bits: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.float().numpy()
+
+
+def _ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    ia = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+# --------------------------------------------------------------------- bf16
+
+
+def pin_bf16_widen(o):
+    """Widening bf16 -> fp32 agrees with torch on every finite pattern class."""
+    bits = np.concatenate([np.arange(0, 0x7F80, 97, dtype=np.uint16),
+                           (np.arange(0, 0x7F80, 89) | 0x8000).astype(np.uint16),
+                           np.array([0x0001, 0x007F, 0x0080, 0x7F7F, 0x7F80, 0xFF80, 0x8000], dtype=np.uint16)])
+    got = o.f32_from_bf16(bits)
+    ref = _torch_widen(bits)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def pin_bf16_round(o):
+    """Nearest-even rounding to bf16 agrees with torch's conversion, including
+    exact ties, subnormals and overflow."""
+    rng_vals = synth.normal_f32(4000, 1.0, 7, 901) * np.float32(3e-2)
+    big = synth.normal_f32(1000, 1.0, 7, 902) * np.float32(1e30)
+    # construct exact ties: a bf16 value plus exactly half of its last place
+    base = synth.to_bf16_bits(synth.normal_f32(1000, 1.0, 7, 903))
+    ties = (base.astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    near = (base.astype(np.uint32) << 16 | 0x7FFF).view(np.float32)
+    sub = np.array([1e-40, -1e-40, 5e-39, 1.2e-38, 3.4e38, -3.4e38, 0.0, -0.0], dtype=np.float32)
+    vals = np.concatenate([rng_vals, big, ties, near, sub]).astype(np.float32)
+    got = o.bf16_from_f32(vals)
+    ref = _torch_bf16_bits(vals)
+    assert np.array_equal(got, ref), np.nonzero(got != ref)
+
+
+def pin_bf16_hand_ties(o):
+    """Hand-derived ties (tests/golden/reconstruct_cases.json, first cases)."""
+    assert o.bf16_from_f32(np.float32(1 + 2 ** -8)) == 0x3F80
+    assert o.bf16_from_f32(np.float32(1 + 3 * 2 ** -8)) == 0x3F82
+    assert o.bf16_from_f32(np.float32(1 - 2 ** -8)) == 0x3F7F
+    assert o.bf16_from_f32(np.float32(-1 - 2 ** -8)) == 0xBF80
+
+
+# ----------------------------------------------------------------- compress
+
+
+def _handbuilt_4x16():
+    """Inputs of tests/golden/compress_4x16.json, built from its stated rules."""
+    j = np.arange(16)
+    wb = np.zeros((4, 16), dtype=np.float64)
+    wb[0:3] = (j - 8) * 2.0 ** -6
+    wb[3] = (j - 15) * 2.0 ** -6
+    d = np.zeros((4, 16), dtype=np.float64)
+    d[0] = np.where(j % 2 == 0, 2.0 ** -10, -(2.0 ** -10))
+    d[1] = np.where(j < 8, 3 * 2.0 ** -9, 0.0)
+    d[2] = -(j + 1) * 2.0 ** -12
+    d[3] = -(2.0 ** -11)
+    d[3, 0] = 2.0 ** -8
+    d[3, 15] = 0.0
+    w_base = synth.to_bf16_bits(wb.astype(np.float32))
+    w_ft = (wb + d).astype(np.float32)
+    w_ft[3, 15] = np.float32(-0.0)  # W_base[3,15] = +0, so Delta = -0
+    assert synth.bf16_bits_to_f32(w_base)[3, 15] == 0.0
+    return w_base, w_ft
+
+
+def pin_compress_handbuilt(o):
+    g = _json("compress_4x16.json")
+    w_base, w_ft = _handbuilt_4x16()
+    signs, alpha = o.compress(w_base, w_ft)
+    assert signs.tolist() == g["expected_signs"], signs.tolist()
+    assert alpha.tolist() == g["expected_alpha_row"], alpha.tolist()
+    s2, a2 = o.compress(w_base, w_ft, per_matrix=True)
+    assert np.array_equal(s2, signs)
+    assert a2.tolist() == [g["expected_alpha_matrix"]]
+    # A bf16 W_ft is widened exactly first: same result as its fp32 value.
+    ft16 = synth.to_bf16_bits(w_ft)
+    s3, a3 = o.compress(w_base, ft16)
+    s4, a4 = o.compress(w_base, synth.bf16_bits_to_f32(ft16))
+    assert np.array_equal(s3, s4) and np.array_equal(a3, a4)
+
+
+def pin_compress_packing_vs_numpy(o):
+    """Packed bits equal numpy's little-endian unpacking of (Delta >= 0)."""
+    w_base, w_ft = synth.layer(37, 200, seed=3, index=5)
+    signs, _ = o.compress(w_base, w_ft)
+    assert signs.shape == (37, 25)
+    d = w_ft - synth.bf16_bits_to_f32(w_base)  # numpy fp32 subtract
+    bits = np.unpackbits(signs, axis=1, bitorder="little")
+    assert np.array_equal(bits.astype(bool), d >= 0)
+
+
+def pin_alpha_exact_mean(o):
+    """alpha_r is the mean |Delta| rounded to fp32: compare with an exact sum
+    (math.fsum) divided by C.  fp64 accumulation may straddle a rounding
+    boundary only rarely, so: all within 1 ulp, nearly all exact."""
+    for (R, C, seed) in ((64, 4096, 11), (256, 512, 0), (16, 28672, 12)):
+        w_base, w_ft = synth.layer(R, C, seed=seed)
+        _, alpha, sums = o.compress(w_base, w_ft, return_row_sums=True)
+        d = np.abs(w_ft - synth.bf16_bits_to_f32(w_base)).astype(np.float64)
+        exact = np.array([math.fsum(row) for row in d])
+        ref = (exact / C).astype(np.float32)
+        ud = _ulp_diff_f32(alpha, ref)
+        assert ud.max() <= 1, ud.max()
+        assert (ud == 0).mean() >= 0.98
+        # the fp64 row sums are within C * 2^-52 relative of the exact sums
+        assert np.all(np.abs(sums - exact) <= exact * C * 2.0 ** -52)
+        _, am = o.compress(w_base, w_ft, per_matrix=True)
+        tot = math.fsum(d.ravel()) / (R * C)
+        assert _ulp_diff_f32(am, np.float32(tot)).max() <= 1
+
+
+def pin_alpha_laplace(o):
+    """Delta ~ Laplace(0, b) has E|Delta| = b and sd |Delta| = b, so every
+    row's alpha_r / b - 1 is about N(0, 1/C): bound it by 6 / sqrt(C)."""
+    b = 1e-3
+    R, C = 64, 4096
+    w_base = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, 5, 1))
+    delta = synth.laplace_f32((R, C), b, 5, 2)
+    w_ft = synth.bf16_bits_to_f32(w_base) + delta
+    _, alpha = o.compress(w_base, w_ft)
+    dev = np.abs(alpha / b - 1.0)
+    assert dev.max() < 6.0 / math.sqrt(C), dev.max()
+    assert abs(alpha.mean() / b - 1.0) < 6.0 / math.sqrt(R * C)
+
+
+def pin_alpha_least_squares(o):
+    """For the stored signs s, alpha minimises ||Delta - a s||^2 over scalar a
+    (the derivative sum s (Delta - a s) vanishes at a = mean |Delta|)."""
+    w_base, w_ft = synth.layer(8, 1024, seed=21)
+    signs, alpha = o.compress(w_base, w_ft)
+    d = (w_ft - synth.bf16_bits_to_f32(w_base)).astype(np.float64)
+    s = np.unpackbits(signs, axis=1, bitorder="little").astype(np.float64) * 2 - 1
+    for r in range(8):
+        f = lambda a: float(np.sum((d[r] - a * s[r]) ** 2))  # noqa: E731
+        a = float(alpha[r])
+        assert f(a) <= f(a * (1 + 1e-4)) and f(a) <= f(a * (1 - 1e-4))
+        grad = float(np.sum(s[r] * (d[r] - a * s[r])))
+        assert abs(grad) <= 1e-6 * float(np.sum(np.abs(d[r])))
+
+
+# -------------------------------------------------------------- reconstruct
+
+
+def pin_reconstruct_hand_cases(o):
+    g = _json("reconstruct_cases.json")
+    for wb, ab, bit, exp, why in g["cases"]:
+        w_base = np.full((1, 8), int(wb, 16), dtype=np.uint16)
+        alpha = np.array([_f32_bits(ab)], dtype=np.float32)
+        signs = np.array([[0xFF if bit else 0x00]], dtype=np.uint8)
+        out = o.reconstruct(w_base, signs, alpha)
+        assert np.all(out == int(exp, 16)), (why, hex(int(out[0, 0])))
+
+
+def pin_reconstruct_vs_torch(o):
+    """Random layer: W_eff equals torch's fp32 add + bf16 conversion of
+    W_base + alpha_r * s (s from numpy's bit unpacking)."""
+    import torch
+
+    w_base, w_ft = synth.layer(96, 640, seed=4, index=3)
+    signs, alpha = o.compress(w_base, w_ft)
+    s = np.unpackbits(signs, axis=1, bitorder="little").astype(np.float32) * 2 - 1
+    for per_matrix in (False, True):
+        a = alpha if not per_matrix else o.compress(w_base, w_ft, per_matrix=True)[1]
+        wf = torch.from_numpy(synth.bf16_bits_to_f32(w_base))
+        av = torch.from_numpy(a.reshape(-1, 1) if not per_matrix else a.reshape(1, 1))
+        ref = (wf + av * torch.from_numpy(s)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        got = o.reconstruct(w_base, signs, a, per_matrix=per_matrix)
+        assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------- linear
+
+
+def pin_linear_exact_rational(o):
+    """Tiny case: y64 equals the exact rational product (fractions) to within
+    fp64 rounding of the sum, and the normaliser equals sum |x| |W_eff|."""
+    M, R, C = 3, 5, 24
+    w_base, w_ft = synth.layer(R, C, seed=8)
+    x = synth.activations(M, C, seed=8)
+    signs, alpha = o.compress(w_base, w_ft)
+    weff = _torch_widen(o.reconstruct(w_base, signs, alpha)).astype(np.float64)
+    xf = _torch_widen(x).astype(np.float64)
+    y, sc = o.linear(x, w_base, signs, alpha)
+    for m in range(M):
+        for r in range(R):
+            exact = sum(Fraction(float(xf[m, j])) * Fraction(float(weff[r, j])) for j in range(C))
+            absum = sum(abs(Fraction(float(xf[m, j])) * Fraction(float(weff[r, j]))) for j in range(C))
+            assert abs(Fraction(y[m, r]) - exact) <= absum * Fraction(C, 2 ** 52)
+            assert abs(Fraction(sc[m, r]) - absum) <= absum * Fraction(C, 2 ** 52)
+
+
+def pin_linear_vs_numpy(o):
+    """Tiny single layer (256 x 512, 4 tokens): y64 equals numpy's float64
+    matmul of x and torch-reconstructed W_eff, to fp64 rounding."""
+    import torch
+
+    w_base, w_ft = synth.layer(256, 512, seed=0)
+    x = synth.activations(4, 512, seed=0)
+    signs, alpha = o.compress(w_base, w_ft)
+    s = np.unpackbits(signs, axis=1, bitorder="little").astype(np.float32) * 2 - 1
+    weff = (torch.from_numpy(synth.bf16_bits_to_f32(w_base)) + torch.from_numpy(alpha).view(-1, 1)
+            * torch.from_numpy(s)).to(torch.bfloat16).float().numpy().astype(np.float64)
+    xf = _torch_widen(x).astype(np.float64)
+    ref = xf @ weff.T
+    y, sc = o.linear(x, w_base, signs, alpha)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * (np.abs(xf) @ np.abs(weff).T).max())
+    assert np.allclose(sc, np.abs(xf) @ np.abs(weff).T, rtol=1e-13)
+    # selected rows in any order give the same columns
+    rows = np.array([255, 3, 77, 3], dtype=np.int64)
+    y2, _ = o.linear(x, w_base, signs, alpha, rows=rows)
+    assert np.array_equal(y2, y[:, rows])
+
+
+def dyadic_case(M: int, R: int, C: int, seed: int, n_variants: int = 1):
+    """Exact-arithmetic inputs: W_base in {k 2^-8 : |k| <= 8}, alpha_r =
+    (1 + (r + v) mod 4) 2^-8 for variant v, x in {-1, 0, 1} with at most 8
+    non-zeros per row.  Every product and partial sum is exact in fp32 and
+    |y| 2^8 <= 8 * 12 = 96 < 256, so y is exact in bf16 whatever the order."""
+    u = synth.u64((R, C), seed, 7001)
+    k = (u % np.uint64(17)).astype(np.int64) - 8
+    w_base = synth.to_bf16_bits((k * 2.0 ** -8).astype(np.float32))
+    sign_bytes = synth.u64((n_variants, R, C // 8), seed, 7002).astype(np.uint8)
+    alpha = np.stack([((1 + (np.arange(R) + v) % 4) * 2.0 ** -8).astype(np.float32)
+                      for v in range(n_variants)])
+    x = np.zeros((M, C), dtype=np.float32)
+    cols = synth.u64((M, 8), seed, 7003) % np.uint64(C)
+    vals = (synth.u64((M, 8), seed, 7004) % np.uint64(3)).astype(np.float32) - 1
+    for m in range(M):
+        for t in range(8):
+            x[m, int(cols[m, t])] = vals[m, t]
+    return synth.to_bf16_bits(x), w_base, k, sign_bytes, alpha
+
+
+def pin_linear_dyadic(o):
+    """Exact inputs: y64 equals the integer-arithmetic product exactly."""
+    M, R, C = 6, 40, 64
+    x, w_base, k, sb, alpha = dyadic_case(M, R, C, seed=31)
+    signs, a = sb[0], alpha[0]
+    y, _ = o.linear(x, w_base, signs, a)
+    s = np.unpackbits(signs, axis=1, bitorder="little").astype(np.int64) * 2 - 1
+    wq = k + (1 + np.arange(R)[:, None] % 4) * s        # W_eff * 2^8, integers
+    xi = synth.bf16_bits_to_f32(x).astype(np.int64)
+    assert np.array_equal(y * 256.0, (xi @ wq.T).astype(np.float64))
+
+
+# ------------------------------------------------------------------ grouped
+
+
+def pin_grouped(o):
+    """Grouped = per-token linear with that token's variant; ids out of range
+    give zero rows; the result is equivariant under token permutation."""
+    V, M, R, C = 3, 9, 20, 32
+    w_base = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, 9, 1))
+    signs = np.zeros((V, R, C // 8), dtype=np.uint8)
+    alpha = np.zeros((V, R), dtype=np.float32)
+    for v in range(V):
+        w_ft = synth.variant_ft(w_base, v, b=1e-3 * (v + 1), seed=9)
+        signs[v], alpha[v] = o.compress(w_base, w_ft)
+    x = synth.activations(M, C, seed=9)
+    ids = np.array([0, 2, 1, 5, 0, -1, 2, 2, 1], dtype=np.int32)
+    y, sc = o.linear_grouped(x, ids, w_base, signs, alpha)
+    for m in range(M):
+        v = ids[m]
+        if 0 <= v < V:
+            ym, _ = o.linear(x[m:m + 1], w_base, signs[v], alpha[v])
+            assert np.array_equal(y[m], ym[0])
+            # the variant's own deltas matter: another variant gives another row
+            yo, _ = o.linear(x[m:m + 1], w_base, signs[(v + 1) % V], alpha[(v + 1) % V])
+            assert not np.array_equal(ym, yo)
+        else:
+            assert np.all(y[m] == 0) and np.all(sc[m] == 0)
+    perm = np.array([4, 2, 8, 0, 1, 7, 3, 6, 5])
+    yp, _ = o.linear_grouped(x[perm], ids[perm], w_base, signs, alpha)
+    assert np.array_equal(yp, y[perm])
+    # per-matrix alpha: alpha [V]
+    am = np.array([alpha[v].mean() for v in range(V)], dtype=np.float32)
+    y3, _ = o.linear_grouped(x, ids, w_base, signs, am, per_matrix=True)
+    for m in (0, 1, 2):
+        ym, _ = o.linear(x[m:m + 1], w_base, signs[ids[m]], am[ids[m]:ids[m] + 1], per_matrix=True)
+        assert np.array_equal(y3[m], ym[0])
+
+
+def pin_shape_4096(o):
+    """A 4096 x 4096 layer packs to a [4096, 512] byte tensor ('Infrastructure
+    Details' storage format)."""
+    R = C = 4096
+    w_base = np.zeros((R, C), dtype=np.uint16)
+    w_ft = np.zeros((R, C), dtype=np.float32)
+    signs, alpha = o.compress(w_base, w_ft)
+    assert signs.shape == (4096, 512) and signs.dtype == np.uint8
+    assert np.all(signs == 0xFF) and np.all(alpha == 0)
+
+
+ALL = [pin_bf16_widen, pin_bf16_round, pin_bf16_hand_ties, pin_compress_handbuilt,
+       pin_compress_packing_vs_numpy, pin_alpha_exact_mean, pin_alpha_laplace,
+       pin_alpha_least_squares, pin_reconstruct_hand_cases, pin_reconstruct_vs_torch,
+       pin_linear_exact_rational, pin_linear_vs_numpy, pin_linear_dyadic, pin_grouped,
+       pin_shape_4096]
