@@ -1,0 +1,145 @@
+/*
+ * bitdelta.h -- C ABI of the BitDelta hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method: "BitDelta: Serving 14 Zen Models from One GPU Cluster"
+ * (hanzo.blog, 2026-02-28), sections "Mathematical Foundation" (task delta
+ * Delta = W_ft - W_base, the 1-bit code W_ft ~ W_base + alpha * sign(Delta),
+ * alpha = mean |Delta_ij|), "Serving Architecture" (step 3 rebuilds
+ * W_eff = W_base + alpha * sign(Delta) inside a fused kernel that never
+ * writes W_eff to HBM; the conceptual fused_bitdelta_linear(x, w_base,
+ * delta_sign, alpha) sketch; one HBM-resident base read by every variant in
+ * the delta cache) and "Infrastructure Details" (signs packed 8 per byte,
+ * [4096,4096] -> [4096,512]; alpha stored as fp32, one per output row).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers on the current HIP device unless stated.
+ *    The caller owns every buffer; the library allocates nothing inside these
+ *    calls and keeps no pointer after a call returns.
+ *  - bf16 tensors travel as raw 16-bit patterns (bd_bf16).
+ *  - Layouts are row-major and dense: W [d_out, d_in], signs [d_out, d_in/8],
+ *    x [m, d_in] (a [batch, seq, d_in] activation flattened), y [m, d_out].
+ *  - Sign packing: column j of a row is bit (j & 7) of byte (j >> 3) of that
+ *    row (least significant bit first); bit 1 means +1, bit 0 means -1; a
+ *    delta >= 0 (including -0) is stored as +1.
+ *  - alpha: BD_ALPHA_ROW = fp32 [d_out], one per output row;
+ *    BD_ALPHA_MATRIX = fp32 [1], one per matrix.
+ *  - W_eff[r,j] = bf16_rne(fp32(W_base[r,j]) + (bit ? alpha_r : -alpha_r)),
+ *    the sum formed in fp32 and rounded once to bf16 (nearest, ties to even).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise the host.  Outputs are fully overwritten
+ *    and must not alias inputs.
+ *  - Errors are detected on the host before any launch and return a status;
+ *    nothing is launched then.  BD_EDEVICE reports a launch failure;
+ *    bitdelta_last_error() gives the detail (thread-local).
+ *  - Alignment: bf16 and fp32 matrices (x, y, W_base, W_ft, W_eff) must be
+ *    16-byte aligned, alpha and variant ids 4-byte aligned, workspaces as
+ *    stated per call; signs need no alignment.
+ *  - d_in must be a positive multiple of 8 (whole sign bytes); d_out > 0;
+ *    m >= 0 (m = 0 is a no-op returning BD_OK).
+ *  - Calls are thread-safe; concurrent calls on different streams may share
+ *    read-only inputs.
+ */
+#ifndef BITDELTA_H
+#define BITDELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t bd_bf16;
+
+typedef enum {
+    BD_OK = 0,
+    BD_EINVAL = 1,     /* null pointer with a non-zero extent, bad enum, n_variants <= 0 */
+    BD_ESHAPE = 2,     /* d_in % 8 != 0, d_in <= 0, d_out <= 0, m < 0, or a size the grid cannot cover */
+    BD_EALIGN = 3,     /* a pointer misses the alignment stated above */
+    BD_EWORKSPACE = 4, /* workspace smaller than the matching *_workspace() query */
+    BD_EDEVICE = 5     /* the HIP runtime rejected a launch */
+} bd_status;
+
+typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;
+
+typedef enum { BD_ALPHA_ROW = 0, BD_ALPHA_MATRIX = 1 } bd_alpha_mode;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int bitdelta_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char *bitdelta_status_string(int status);
+
+/* Detail of the last non-OK status on this thread (static per thread). */
+const char *bitdelta_last_error(void);
+
+/* ---------------------------------------------------------------- compress
+ * "Mathematical Foundation" (Delta, sign, alpha = mean |Delta|) and
+ * "Infrastructure Details" (packed sign storage, fp32 alpha per row).
+ *
+ * Delta[r,j] = fl32(W_ft[r,j] - W_base[r,j]); signs[r, j>>3] bit (j&7) =
+ * (Delta >= 0).  alpha: the |Delta| values of a row are summed in fp64 in a
+ * fixed order -- 8-column groups g = 0,1,... feed 256 partial sums
+ * (group g into partial g mod 256, columns in increasing order), which are
+ * then combined by a halving tree (p[k] += p[k+s], s = 128 ... 1).
+ *   BD_ALPHA_ROW:    alpha[r] = fp32(S_r / d_in).
+ *   BD_ALPHA_MATRIX: the row sums S_r are combined the same way (row r into
+ *                    partial r mod 256, then the halving tree) into T, and
+ *                    alpha[0] = fp32(T / (d_out * d_in)).
+ * w_base: bf16 [d_out, d_in]; w_ft: [d_out, d_in] of type ft_dtype (BD_BF16
+ * or BD_F32); signs out: uint8 [d_out, d_in/8]; alpha out: fp32 [d_out] or [1].
+ * workspace: device scratch of at least bitdelta_compress_workspace() bytes
+ * (0 for BD_ALPHA_ROW; 8 * d_out for BD_ALPHA_MATRIX), 8-byte aligned;
+ * may be NULL when the query returns 0. */
+size_t bitdelta_compress_workspace(int64_t d_out, int64_t d_in, int alpha_mode);
+bd_status bitdelta_compress(const bd_bf16 *w_base, const void *w_ft, int ft_dtype,
+                            int64_t d_out, int64_t d_in, int alpha_mode,
+                            uint8_t *signs, float *alpha,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------- reconstruct
+ * "Serving Architecture", step 3 of the request flow: materialise
+ * W_eff = W_base + alpha * sign(Delta) as bf16 [d_out, d_in].  (The fused
+ * linear below never does this; this call exists for callers that want the
+ * dense weight and as the exact reference of the fused path.) */
+bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+                               int alpha_mode, int64_t d_out, int64_t d_in,
+                               bd_bf16 *w_eff, void *stream);
+
+/* ------------------------------------------------------------------ linear
+ * "Serving Architecture", the fused reconstruct + matmul (the conceptual
+ * fused_bitdelta_linear sketch): y = x W_eff^T with W_eff formed in registers
+ * and LDS only.  fp32 accumulation, bf16 output (nearest-even).
+ * x: bf16 [m, d_in]; y: bf16 [m, d_out].  m <= 16 runs the bandwidth-bound
+ * decode kernel; larger m the bf16-MFMA prefill kernel.
+ * workspace: at least bitdelta_linear_workspace(m, d_out, d_in) bytes,
+ * 16-byte aligned (may be NULL when that is 0). */
+size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in);
+bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
+                          const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+                          int alpha_mode, int64_t d_out, int64_t d_in,
+                          bd_bf16 *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------- linear_grouped
+ * "Serving Architecture", the delta cache: many variants share one
+ * HBM-resident W_base; token i uses variant v = variant_ids[i]:
+ *   y[i] = x[i] (W_base + alpha_v * sign(Delta_v))^T.
+ * variant_ids: int32 [m] on the device; ids outside [0, n_variants) give a
+ * zero row.  signs: uint8 [n_variants, d_out, d_in/8]; alpha: fp32
+ * [n_variants, d_out] (BD_ALPHA_ROW) or [n_variants] (BD_ALPHA_MATRIX).
+ * Tokens are bucketed by variant on the device (no host synchronisation).
+ * n_variants must be in [1, 4096].
+ * workspace: at least bitdelta_linear_grouped_workspace() bytes, 16-byte
+ * aligned. */
+size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t d_out, int64_t d_in);
+bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids,
+                                  int32_t n_variants, const bd_bf16 *w_base,
+                                  const uint8_t *signs, const float *alpha, int alpha_mode,
+                                  int64_t d_out, int64_t d_in, bd_bf16 *y,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITDELTA_H */

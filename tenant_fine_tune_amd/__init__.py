@@ -1,0 +1,204 @@
+"""BitDelta on MI355X: thin Python binding of libbitdelta.so (include/bitdelta.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the library.  torch supplies device memory (outputs and workspaces are
+allocated with torch on the input's device) and the current stream, which is
+handed to the library as a hipStream_t.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+Method: "BitDelta: Serving 14 Zen Models from One GPU Cluster" (hanzo.blog,
+2026-02-28), "Mathematical Foundation", "Serving Architecture" and
+"Infrastructure Details"; `linear` mirrors the post's conceptual
+fused_bitdelta_linear(x, w_base, delta_sign, alpha) signature.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped",
+           "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE",
+           "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
+
+BD_OK, BD_EINVAL, BD_ESHAPE, BD_EALIGN, BD_EWORKSPACE, BD_EDEVICE = range(6)
+BD_BF16, BD_F32 = 0, 1
+BD_ALPHA_ROW, BD_ALPHA_MATRIX = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libbitdelta.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); every symbol declared in include/bitdelta.h
+EXPORTS = {
+    "bitdelta_version": (_INT, []),
+    "bitdelta_status_string": (ctypes.c_char_p, [_INT]),
+    "bitdelta_last_error": (ctypes.c_char_p, []),
+    "bitdelta_compress_workspace": (_SZ, [_I64, _I64, _INT]),
+    "bitdelta_compress": (_INT, [_P, _P, _INT, _I64, _I64, _INT, _P, _P, _P, _SZ, _P]),
+    "bitdelta_reconstruct": (_INT, [_P, _P, _P, _INT, _I64, _I64, _P, _P]),
+    "bitdelta_linear_workspace": (_SZ, [_I64, _I64, _I64]),
+    "bitdelta_linear": (_INT, [_P, _I64, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
+    "bitdelta_linear_grouped_workspace": (_SZ, [_I64, _I32, _I64, _I64]),
+    "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
+}
+
+
+class BitDeltaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{lib.bitdelta_status_string(status).decode()}: {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(f"libbitdelta.so is not built at {lib_path}; run __graft_entry__.build()")
+    handle = ctypes.CDLL(lib_path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def check(status: int) -> None:
+    if status != BD_OK:
+        raise BitDeltaError(status, lib.bitdelta_last_error().decode())
+
+
+# --------------------------------------------------------------- torch glue
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev_tensor(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _alpha_mode(alpha, d_out, per_matrix):
+    if per_matrix is None:
+        per_matrix = alpha.numel() == 1 and d_out != 1
+    want = 1 if per_matrix else d_out
+    if alpha.numel() != want:
+        raise ValueError(f"alpha has {alpha.numel()} values, expected {want}")
+    return BD_ALPHA_MATRIX if per_matrix else BD_ALPHA_ROW
+
+
+def compress(w_base, w_ft, per_matrix: bool = False):
+    """Delta = W_ft - W_base -> (packed signs uint8 [d_out, d_in/8], alpha fp32 [d_out] or [1])."""
+    torch = _torch()
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    if w_ft.dtype == torch.float32:
+        ft = BD_F32
+    elif w_ft.dtype == torch.bfloat16:
+        ft = BD_BF16
+    else:
+        raise TypeError("w_ft must be float32 or bfloat16")
+    _dev_tensor(w_ft, w_ft.dtype, "w_ft")
+    d_out, d_in = w_base.shape
+    if tuple(w_ft.shape) != (d_out, d_in):
+        raise ValueError("w_ft shape differs from w_base")
+    mode = BD_ALPHA_MATRIX if per_matrix else BD_ALPHA_ROW
+    dev = w_base.device
+    signs = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+    alpha = torch.empty((1 if per_matrix else d_out,), dtype=torch.float32, device=dev)
+    nws = lib.bitdelta_compress_workspace(d_out, d_in, mode)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev) if nws else None
+    check(lib.bitdelta_compress(_ptr(w_base), _ptr(w_ft), ft, d_out, d_in, mode, _ptr(signs), _ptr(alpha),
+                                _ptr(ws), nws, _stream(dev)))
+    return signs, alpha
+
+
+def reconstruct(w_base, signs, alpha, per_matrix: bool | None = None):
+    """Materialised W_eff = bf16(W_base + alpha * sign) [d_out, d_in]."""
+    torch = _torch()
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    _dev_tensor(signs, torch.uint8, "signs")
+    _dev_tensor(alpha, torch.float32, "alpha")
+    d_out, d_in = w_base.shape
+    mode = _alpha_mode(alpha, d_out, per_matrix)
+    w_eff = torch.empty_like(w_base)
+    check(lib.bitdelta_reconstruct(_ptr(w_base), _ptr(signs), _ptr(alpha), mode, d_out, d_in, _ptr(w_eff),
+                                   _stream(w_base.device)))
+    return w_eff
+
+
+def linear(x, w_base, delta_sign, alpha, per_matrix: bool | None = None):
+    """Fused y = x (W_base + alpha * sign(Delta))^T; x [..., d_in] -> y [..., d_out] bf16."""
+    torch = _torch()
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    _dev_tensor(delta_sign, torch.uint8, "delta_sign")
+    _dev_tensor(alpha, torch.float32, "alpha")
+    d_out, d_in = w_base.shape
+    if x.shape[-1] != d_in:
+        raise ValueError(f"x has width {x.shape[-1]}, w_base expects {d_in}")
+    mode = _alpha_mode(alpha, d_out, per_matrix)
+    lead = tuple(x.shape[:-1])
+    m = 1
+    for s in lead:
+        m *= s
+    y = torch.empty(lead + (d_out,), dtype=torch.bfloat16, device=x.device)
+    nws = lib.bitdelta_linear_workspace(m, d_out, d_in)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=x.device) if nws else None
+    check(lib.bitdelta_linear(_ptr(x), m, _ptr(w_base), _ptr(delta_sign), _ptr(alpha), mode, d_out, d_in,
+                              _ptr(y), _ptr(ws), nws, _stream(x.device)))
+    return y
+
+
+def linear_grouped(x, variant_ids, w_base, signs, alpha, per_matrix: bool | None = None):
+    """Multi-variant linear over one shared W_base: token i uses variant variant_ids[i].
+    signs [V, d_out, d_in/8]; alpha [V, d_out] or [V]."""
+    torch = _torch()
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(variant_ids, torch.int32, "variant_ids")
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    _dev_tensor(signs, torch.uint8, "signs")
+    _dev_tensor(alpha, torch.float32, "alpha")
+    d_out, d_in = w_base.shape
+    V = signs.shape[0]
+    if tuple(signs.shape) != (V, d_out, d_in // 8):
+        raise ValueError("signs must be [V, d_out, d_in/8]")
+    if per_matrix is None:
+        per_matrix = alpha.dim() == 1 and d_out != 1
+    if alpha.numel() != (V if per_matrix else V * d_out):
+        raise ValueError("alpha must be [V, d_out] (per row) or [V] (per matrix)")
+    mode = BD_ALPHA_MATRIX if per_matrix else BD_ALPHA_ROW
+    m = x.shape[0]
+    if x.dim() != 2 or variant_ids.numel() != m:
+        raise ValueError("x must be [m, d_in] with one variant id per row")
+    y = torch.empty((m, d_out), dtype=torch.bfloat16, device=x.device)
+    nws = lib.bitdelta_linear_grouped_workspace(m, V, d_out, d_in)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
+    check(lib.bitdelta_linear_grouped(_ptr(x), m, _ptr(variant_ids), V, _ptr(w_base), _ptr(signs), _ptr(alpha),
+                                      mode, d_out, d_in, _ptr(y), _ptr(ws), nws, _stream(x.device)))
+    return y

@@ -1,0 +1,252 @@
+// C ABI of the BitDelta library (declared in include/bitdelta.h).
+//
+// Every argument is checked on the host before anything is launched; a bad
+// argument returns a status and launches nothing, so the checks are testable
+// on a machine without a GPU.  No call allocates device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+
+#include "../../include/bitdelta.h"
+#include "bd_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bd_status fail(bd_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+bd_status fail(bd_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bd_status device(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return BD_OK;
+    return fail(BD_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
+
+bd_status check_matrix(int64_t d_out, int64_t d_in)
+{
+    if (d_out <= 0)
+        return fail(BD_ESHAPE, "d_out must be positive (got %lld)", (long long)d_out);
+    if (d_in <= 0 || d_in % 8 != 0)
+        return fail(BD_ESHAPE, "d_in must be a positive multiple of 8 (got %lld)", (long long)d_in);
+    if (d_out > kMaxGrid || d_in > (int64_t)1 << 40 || d_out > std::numeric_limits<int64_t>::max() / d_in)
+        return fail(BD_ESHAPE, "matrix [%lld, %lld] too large", (long long)d_out, (long long)d_in);
+    return BD_OK;
+}
+
+bd_status check_mode(int mode)
+{
+    if (mode != BD_ALPHA_ROW && mode != BD_ALPHA_MATRIX)
+        return fail(BD_EINVAL, "alpha_mode must be BD_ALPHA_ROW (0) or BD_ALPHA_MATRIX (1), got %d", mode);
+    return BD_OK;
+}
+
+#define BD_TRY(expr)                  \
+    do {                              \
+        bd_status s__ = (expr);       \
+        if (s__ != BD_OK)             \
+            return s__;               \
+    } while (0)
+
+#define BD_NONNULL(p)                                             \
+    do {                                                          \
+        if (!(p))                                                 \
+            return fail(BD_EINVAL, "%s must not be NULL", #p);    \
+    } while (0)
+
+#define BD_ALIGNED(p, a)                                                        \
+    do {                                                                        \
+        if (!aligned((p), (a)))                                                 \
+            return fail(BD_EALIGN, "%s must be %d-byte aligned", #p, (int)(a)); \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int bitdelta_version(void) { return 100; }
+
+const char *bitdelta_status_string(int s)
+{
+    switch (s) {
+    case BD_OK: return "BD_OK";
+    case BD_EINVAL: return "BD_EINVAL: invalid argument";
+    case BD_ESHAPE: return "BD_ESHAPE: unsupported or invalid shape";
+    case BD_EALIGN: return "BD_EALIGN: misaligned pointer";
+    case BD_EWORKSPACE: return "BD_EWORKSPACE: workspace too small";
+    case BD_EDEVICE: return "BD_EDEVICE: HIP launch failed";
+    default: return "unknown bitdelta status";
+    }
+}
+
+const char *bitdelta_last_error(void) { return g_err; }
+
+size_t bitdelta_compress_workspace(int64_t d_out, int64_t d_in, int alpha_mode)
+{
+    (void)d_in;
+    if (alpha_mode != BD_ALPHA_MATRIX || d_out <= 0)
+        return 0;
+    return sizeof(double) * (size_t)d_out;
+}
+
+bd_status bitdelta_compress(const bd_bf16 *w_base, const void *w_ft, int ft_dtype, int64_t d_out,
+                            int64_t d_in, int alpha_mode, uint8_t *signs, float *alpha,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    BD_TRY(check_mode(alpha_mode));
+    if (ft_dtype != BD_BF16 && ft_dtype != BD_F32)
+        return fail(BD_EINVAL, "ft_dtype must be BD_BF16 (0) or BD_F32 (1), got %d", ft_dtype);
+    BD_TRY(check_matrix(d_out, d_in));
+    BD_NONNULL(w_base);
+    BD_NONNULL(w_ft);
+    BD_NONNULL(signs);
+    BD_NONNULL(alpha);
+    BD_ALIGNED(w_base, 16);
+    BD_ALIGNED(w_ft, 16);
+    BD_ALIGNED(alpha, 4);
+    const bool per_matrix = alpha_mode == BD_ALPHA_MATRIX;
+    const size_t need = bitdelta_compress_workspace(d_out, d_in, alpha_mode);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "compress needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (need) {
+        BD_NONNULL(workspace);
+        BD_ALIGNED(workspace, 8);
+    }
+    return device(bd::launch_compress(w_base, w_ft, ft_dtype == BD_F32, d_out, d_in, per_matrix, signs,
+                                      alpha, static_cast<double *>(workspace), (hipStream_t)stream),
+                  "bitdelta_compress");
+}
+
+bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+                               int alpha_mode, int64_t d_out, int64_t d_in, bd_bf16 *w_eff,
+                               void *stream)
+{
+    BD_TRY(check_mode(alpha_mode));
+    BD_TRY(check_matrix(d_out, d_in));
+    BD_NONNULL(w_base);
+    BD_NONNULL(signs);
+    BD_NONNULL(alpha);
+    BD_NONNULL(w_eff);
+    BD_ALIGNED(w_base, 16);
+    BD_ALIGNED(w_eff, 16);
+    BD_ALIGNED(alpha, 4);
+    const int64_t bpr = (d_in / 8 + 255) / 256;
+    if (d_out * bpr > kMaxGrid)
+        return fail(BD_ESHAPE, "matrix [%lld, %lld] exceeds the reconstruct grid", (long long)d_out, (long long)d_in);
+    return device(bd::launch_reconstruct(w_base, signs, alpha, alpha_mode == BD_ALPHA_MATRIX, d_out, d_in, w_eff,
+                                         (hipStream_t)stream),
+                  "bitdelta_reconstruct");
+}
+
+size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in)
+{
+    (void)m;
+    (void)d_out;
+    (void)d_in;
+    return 0;
+}
+
+bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, const uint8_t *signs,
+                          const float *alpha, int alpha_mode, int64_t d_out, int64_t d_in, bd_bf16 *y,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    BD_TRY(check_mode(alpha_mode));
+    BD_TRY(check_matrix(d_out, d_in));
+    if (m < 0)
+        return fail(BD_ESHAPE, "m must be >= 0 (got %lld)", (long long)m);
+    const size_t need = bitdelta_linear_workspace(m, d_out, d_in);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "linear needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (m == 0)
+        return BD_OK;
+    BD_NONNULL(x);
+    BD_NONNULL(w_base);
+    BD_NONNULL(signs);
+    BD_NONNULL(alpha);
+    BD_NONNULL(y);
+    BD_ALIGNED(x, 16);
+    BD_ALIGNED(w_base, 16);
+    BD_ALIGNED(y, 16);
+    BD_ALIGNED(alpha, 4);
+    if (need) {
+        BD_NONNULL(workspace);
+        BD_ALIGNED(workspace, 16);
+    }
+    const bool per_matrix = alpha_mode == BD_ALPHA_MATRIX;
+    hipStream_t s = (hipStream_t)stream;
+    if (m <= bd::kGemvMaxM)
+        return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
+                      "bitdelta_linear (decode)");
+    const int64_t tiles = ((m + bd::kGemmBM - 1) / bd::kGemmBM) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
+    if (tiles > kMaxGrid)
+        return fail(BD_ESHAPE, "linear m=%lld d_out=%lld exceeds the prefill grid", (long long)m, (long long)d_out);
+    return device(bd::launch_gemm(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
+                  "bitdelta_linear (prefill)");
+}
+
+size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t d_out, int64_t d_in)
+{
+    (void)d_out;
+    (void)d_in;
+    if (m < 0 || n_variants <= 0)
+        return 0;
+    return bd::grouped_workspace_bytes(m, n_variants);
+}
+
+bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids, int32_t n_variants,
+                                  const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+                                  int alpha_mode, int64_t d_out, int64_t d_in, bd_bf16 *y,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    BD_TRY(check_mode(alpha_mode));
+    if (n_variants <= 0 || n_variants > 4096)
+        return fail(BD_EINVAL, "n_variants must be in [1, 4096] (got %d)", n_variants);
+    BD_TRY(check_matrix(d_out, d_in));
+    if (m < 0)
+        return fail(BD_ESHAPE, "m must be >= 0 (got %lld)", (long long)m);
+    if (m > std::numeric_limits<int32_t>::max() / 2)
+        return fail(BD_ESHAPE, "grouped m=%lld too large for int32 token indices", (long long)m);
+    const size_t need = bitdelta_linear_grouped_workspace(m, n_variants, d_out, d_in);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "linear_grouped needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (m == 0)
+        return BD_OK;
+    BD_NONNULL(x);
+    BD_NONNULL(variant_ids);
+    BD_NONNULL(w_base);
+    BD_NONNULL(signs);
+    BD_NONNULL(alpha);
+    BD_NONNULL(y);
+    BD_NONNULL(workspace);
+    BD_ALIGNED(x, 16);
+    BD_ALIGNED(w_base, 16);
+    BD_ALIGNED(y, 16);
+    BD_ALIGNED(alpha, 4);
+    BD_ALIGNED(variant_ids, 4);
+    BD_ALIGNED(workspace, 16);
+    const int64_t tiles = bd::grouped_max_tiles(m, n_variants) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
+    if (tiles > kMaxGrid)
+        return fail(BD_ESHAPE, "grouped m=%lld d_out=%lld exceeds the grid", (long long)m, (long long)d_out);
+    return device(bd::launch_grouped(x, m, variant_ids, n_variants, w_base, signs, alpha,
+                                     alpha_mode == BD_ALPHA_MATRIX, d_out, d_in, y,
+                                     static_cast<int32_t *>(workspace), (hipStream_t)stream),
+                  "bitdelta_linear_grouped");
+}
+
+}  // extern "C"

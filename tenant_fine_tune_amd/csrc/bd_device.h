@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+//
+// bf16 values are carried as raw 16-bit patterns packed two per 32-bit word
+// (element 2p in the low half, 2p+1 in the high half), which is how a
+// row-major bf16 row looks when loaded as dwords.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Exact widening of the low / high bf16 of a packed pair to fp32.
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two fp32 values to bf16, nearest-even, packed (lo, hi).  Lowers to one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu); }
+
+// +alpha where bit i of `bits` is 1, -alpha where it is 0 (alpha's own sign
+// bit is flipped by the complement of the delta bit).
+__device__ __forceinline__ float signed_alpha(uint32_t bits, int i, float a)
+{
+    return __uint_as_float(__float_as_uint(a) ^ (((~bits >> i) & 1u) << 31));
+}
+
+// W_eff for the two bf16 weights packed in `w`, whose delta bits are bits i
+// and i+1 of `bits`: fp32 add, then one rounding to bf16 each.
+__device__ __forceinline__ uint32_t weff_pair(uint32_t w, uint32_t bits, int i, float a)
+{
+    float e0 = lo_f32(w) + signed_alpha(bits, i, a);
+    float e1 = hi_f32(w) + signed_alpha(bits, i + 1, a);
+    return pack_bf16x2(e0, e1);
+}
+
+// W_eff for 8 consecutive weights (one 16-byte load) and their sign byte.
+__device__ __forceinline__ uint4 weff_group(uint4 w, uint32_t byte, float a)
+{
+    uint4 r;
+    r.x = weff_pair(w.x, byte, 0, a);
+    r.y = weff_pair(w.y, byte, 2, a);
+    r.z = weff_pair(w.z, byte, 4, a);
+    r.w = weff_pair(w.w, byte, 6, a);
+    return r;
+}
+
+// sum_k lo/hi products of two packed bf16 pairs, accumulated in fp32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+}  // namespace bd

@@ -1,0 +1,43 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI in api.cpp
+// after all argument checks).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+// compress.hip
+hipError_t launch_compress(const uint16_t *w_base, const void *w_ft, bool ft_f32, int64_t d_out,
+                           int64_t d_in, bool per_matrix, uint8_t *signs, float *alpha,
+                           double *row_sums, hipStream_t s);
+
+// reconstruct.hip
+hipError_t launch_reconstruct(const uint16_t *w_base, const uint8_t *signs, const float *alpha,
+                              bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *w_eff,
+                              hipStream_t s);
+
+// gemv.hip: m in [1, 16]
+constexpr int kGemvMaxM = 16;
+hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
+                       const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
+                       uint16_t *y, hipStream_t s);
+
+// gemm.hip: dense prefill GEMM and the grouped variant
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
+                       const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
+                       uint16_t *y, hipStream_t s);
+
+// Grouped: bucketing writes this table into the workspace, then the grouped
+// GEMM walks it.  Layout (int32 words): [0] total tiles, [1..3] pad,
+// then perm[m], tile_v[max_tiles], tile_row0[max_tiles], tile_rows[max_tiles].
+int64_t grouped_max_tiles(int64_t m, int32_t n_variants);
+size_t grouped_workspace_bytes(int64_t m, int32_t n_variants);
+hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int32_t n_variants,
+                          const uint16_t *w_base, const uint8_t *signs, const float *alpha,
+                          bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
+                          int32_t *workspace, hipStream_t s);
+
+}  // namespace bd

@@ -1,0 +1,44 @@
+"""One small pass of the hot path on cuda:0, checked against the oracle:
+compress -> reconstruct -> linear (decode and prefill) -> grouped, on a
+256 x 512 layer (the tiny single-layer workload) with 4 and 40 tokens."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import bf16_dev, check_linear, f32_dev, host, host_bits, i32_dev, u8_dev
+
+
+def run() -> None:
+    import tenant_fine_tune_amd as bd
+
+    assert torch.cuda.is_available(), "smoke needs a GPU"
+    R, C = 256, 512
+    w_base, w_ft = synth.layer(R, C, seed=0)
+    so, ao = oracle.compress(w_base, w_ft)
+    wd = bf16_dev(w_base)
+    sg, ag = bd.compress(wd, f32_dev(w_ft))
+    assert np.array_equal(host(sg), so), "compress signs differ from the oracle"
+    assert np.array_equal(host(ag).view(np.uint32), ao.view(np.uint32)), "alpha differs from the oracle"
+    weff = host_bits(bd.reconstruct(wd, sg, ag))
+    assert np.array_equal(weff, oracle.reconstruct(w_base, so, ao)), "reconstruct differs from the oracle"
+    for M in (4, 40):
+        x = synth.activations(M, C, seed=0, index=M)
+        y = host_bits(bd.linear(bf16_dev(x), wd, sg, ag))
+        y64, sc = oracle.linear(x, w_base, so, ao)
+        err = check_linear(y, y64, sc, f"smoke linear m={M}")
+        print(f"smoke: linear m={M} max normalised error {err:.3e}", flush=True)
+    V = 3
+    signs = np.stack([so] + [oracle.compress(w_base, synth.variant_ft(w_base, v, 1e-3, seed=0))[0] for v in (1, 2)])
+    alpha = np.stack([ao] + [oracle.compress(w_base, synth.variant_ft(w_base, v, 1e-3, seed=0))[1] for v in (1, 2)])
+    ids = np.array([0, 2, 1, 1, 0, 2, 2, 0] * 5, dtype=np.int32)
+    x = synth.activations(ids.size, C, seed=0, index=7)
+    y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), wd, u8_dev(signs), f32_dev(alpha)))
+    y64, sc = oracle.linear_grouped(x, ids, w_base, signs, alpha)
+    check_linear(y, y64, sc, "smoke grouped")
+    torch.cuda.synchronize()
+    print("smoke: OK (compress, reconstruct, linear decode/prefill, grouped match the oracle)", flush=True)
+
+
+if __name__ == "__main__":
+    run()

@@ -1,0 +1,137 @@
+"""CPU tier: the C-ABI library loads, exports every declared symbol, and
+rejects bad arguments on the host before any launch (no GPU needed).
+
+Only invalid argument sets are passed here: every call below must return
+before reaching the HIP runtime.  The one exception (BD_EDEVICE) is run only
+where no GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "bitdelta.h")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    import tenant_fine_tune_amd as bd
+
+    return bd
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(bitdelta_\w+)\s*\(", src))
+
+
+def test_exports_match_header(bd):
+    decl = declared_functions()
+    assert decl == set(bd.EXPORTS), decl ^ set(bd.EXPORTS)
+    handle = ctypes.CDLL(bd.lib_path)
+    for name in decl:
+        assert hasattr(handle, name), name
+
+
+def test_version_and_strings(bd):
+    assert bd.lib.bitdelta_version() >= 100
+    for s in range(6):
+        assert bd.lib.bitdelta_status_string(s).decode().startswith("BD_")
+    assert b"unknown" in bd.lib.bitdelta_status_string(99)
+
+
+def test_no_torch_in_header():
+    src = open(HDR).read()
+    assert "torch" not in src.lower().replace("//", "") or "torch" not in re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    assert "extern \"C\"" in src
+
+
+FAKE = ctypes.c_void_p(4096)       # aligned, never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(4098)   # misaligned
+
+
+def err(bd):
+    return bd.lib.bitdelta_last_error().decode()
+
+
+def test_compress_validation(bd):
+    L = bd.lib
+    c = lambda *a: L.bitdelta_compress(*a)  # noqa: E731
+    assert c(FAKE, FAKE, 1, 4, 12, 0, FAKE, FAKE, None, 0, None) == bd.BD_ESHAPE  # d_in % 8
+    assert "multiple of 8" in err(bd)
+    assert c(FAKE, FAKE, 1, 0, 16, 0, FAKE, FAKE, None, 0, None) == bd.BD_ESHAPE   # d_out = 0
+    assert c(FAKE, FAKE, 1, 4, -8, 0, FAKE, FAKE, None, 0, None) == bd.BD_ESHAPE   # d_in < 0
+    assert c(FAKE, FAKE, 1, 4, 16, 2, FAKE, FAKE, None, 0, None) == bd.BD_EINVAL   # bad mode
+    assert c(FAKE, FAKE, 7, 4, 16, 0, FAKE, FAKE, None, 0, None) == bd.BD_EINVAL   # bad dtype
+    assert c(None, FAKE, 1, 4, 16, 0, FAKE, FAKE, None, 0, None) == bd.BD_EINVAL   # null
+    assert c(FAKE, FAKE, 1, 4, 16, 0, None, FAKE, None, 0, None) == bd.BD_EINVAL
+    assert c(FAKE_ODD, FAKE, 1, 4, 16, 0, FAKE, FAKE, None, 0, None) == bd.BD_EALIGN
+    assert c(FAKE, FAKE_ODD, 1, 4, 16, 0, FAKE, FAKE, None, 0, None) == bd.BD_EALIGN
+    assert c(FAKE, FAKE, 1, 4, 16, 0, FAKE, ctypes.c_void_p(4097), None, 0, None) == bd.BD_EALIGN
+    # per-matrix alpha needs 8 * d_out bytes of workspace
+    assert L.bitdelta_compress_workspace(4, 16, 1) == 32
+    assert L.bitdelta_compress_workspace(4, 16, 0) == 0
+    assert c(FAKE, FAKE, 1, 4, 16, 1, FAKE, FAKE, FAKE, 31, None) == bd.BD_EWORKSPACE
+    assert c(FAKE, FAKE, 1, 4, 16, 1, FAKE, FAKE, None, 32, None) == bd.BD_EINVAL
+
+
+def test_reconstruct_validation(bd):
+    r = bd.lib.bitdelta_reconstruct
+    assert r(FAKE, FAKE, FAKE, 0, 4, 20, FAKE, None) == bd.BD_ESHAPE
+    assert r(FAKE, FAKE, FAKE, 5, 4, 16, FAKE, None) == bd.BD_EINVAL
+    assert r(FAKE, None, FAKE, 0, 4, 16, FAKE, None) == bd.BD_EINVAL
+    assert r(FAKE, FAKE, FAKE, 0, 4, 16, FAKE_ODD, None) == bd.BD_EALIGN
+
+
+def test_linear_validation(bd):
+    f = bd.lib.bitdelta_linear
+    assert f(FAKE, 4, FAKE, FAKE, FAKE, 0, 8, 12, FAKE, None, 0, None) == bd.BD_ESHAPE
+    assert f(FAKE, -1, FAKE, FAKE, FAKE, 0, 8, 16, FAKE, None, 0, None) == bd.BD_ESHAPE
+    assert f(FAKE, 4, FAKE, FAKE, FAKE, 3, 8, 16, FAKE, None, 0, None) == bd.BD_EINVAL
+    assert f(None, 4, FAKE, FAKE, FAKE, 0, 8, 16, FAKE, None, 0, None) == bd.BD_EINVAL
+    assert f(FAKE, 4, FAKE, FAKE, FAKE, 0, 8, 16, None, None, 0, None) == bd.BD_EINVAL
+    assert f(FAKE_ODD, 4, FAKE, FAKE, FAKE, 0, 8, 16, FAKE, None, 0, None) == bd.BD_EALIGN
+    assert f(FAKE, 40, FAKE, FAKE, FAKE, 0, 8, 16, FAKE_ODD, None, 0, None) == bd.BD_EALIGN
+    # m = 0 is a no-op, whatever the (unused) pointers are
+    assert f(None, 0, None, None, None, 0, 8, 16, None, None, 0, None) == bd.BD_OK
+    assert bd.lib.bitdelta_linear_workspace(4096, 4096, 4096) == 0
+
+
+def test_grouped_validation(bd):
+    g = bd.lib.bitdelta_linear_grouped
+    W = bd.lib.bitdelta_linear_grouped_workspace
+    need = W(100, 3, 64, 64)
+    assert need >= 4 * (100 + 4)
+    assert g(FAKE, 100, FAKE, 0, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, need, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, FAKE, 5000, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, 1 << 30, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, FAKE, 3, FAKE, FAKE, FAKE, 0, 64, 60, FAKE, FAKE, need, None) == bd.BD_ESHAPE
+    assert g(FAKE, 100, FAKE, 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, need - 1, None) == bd.BD_EWORKSPACE
+    assert g(FAKE, 100, None, 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, need, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, ctypes.c_void_p(4098), 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, need, None) == bd.BD_EALIGN
+    assert g(None, 0, None, 3, None, None, None, 0, 64, 64, None, None, W(0, 3, 64, 64), None) == bd.BD_OK
+
+
+def test_python_binding_rejects_host_tensors(bd):
+    import torch
+
+    w = torch.zeros(8, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bd.compress(w, w.float())
+    with pytest.raises(ValueError):
+        bd.linear(torch.zeros(2, 16, dtype=torch.bfloat16), w, torch.zeros(8, 2, dtype=torch.uint8),
+                  torch.zeros(8))
+
+
+def test_launch_without_device_reports_edevice(bd):
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: this case is only for hosts without one")
+    # Valid arguments: validation passes and the launch itself fails (no device),
+    # so no memory is ever touched.
+    st = bd.lib.bitdelta_reconstruct(FAKE, FAKE, FAKE, 0, 4, 16, FAKE, None)
+    assert st == bd.BD_EDEVICE, st
+    assert "bitdelta_reconstruct" in err(bd)

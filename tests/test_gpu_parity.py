@@ -1,0 +1,333 @@
+"""GPU tier: the HIP path against the oracle, through the C ABI.
+
+compress / pack / reconstruct must match bit for bit; linear outputs must meet
+the official normalised tolerance (1e-2) and the tight bound of gpu_util,
+and the exact-arithmetic cases (identity / one-hot x, dyadic inputs) must
+match bit for bit, because the official tolerance alone cannot see the deltas.
+Inputs are seeded synthetic tensors with the laws of the post's 70B-class
+workloads (see synth).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import pins
+from tests.gpu_util import (bf16_dev, check_linear, f32_dev, host, host_bits, i32_dev, same_bits_pm0,
+                            u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import tenant_fine_tune_amd as bd
+
+    return bd
+
+
+def _bits32(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------ compress
+
+COMPRESS_SHAPES = [(256, 512), (5, 24), (1, 8), (3, 2056), (64, 28672), (300, 4096), (4096, 4096)]
+
+
+@pytest.mark.parametrize("ft_bf16", [False, True], ids=["ft_f32", "ft_bf16"])
+@pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
+@pytest.mark.parametrize("shape", COMPRESS_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_compress_bit_exact(bd, shape, per_matrix, ft_bf16):
+    R, C = shape
+    w_base, w_ft = synth.layer(R, C, seed=0, index=R % 61 + C % 53, ft_bf16=ft_bf16)
+    so, ao = oracle.compress(w_base, w_ft, per_matrix=per_matrix)
+    ft_dev = bf16_dev(w_ft) if ft_bf16 else f32_dev(w_ft)
+    sg, ag = bd.compress(bf16_dev(w_base), ft_dev, per_matrix=per_matrix)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sg), so)
+    assert np.array_equal(_bits32(host(ag)), _bits32(ao))
+
+
+def test_compress_handbuilt(bd):
+    g = json.load(open(os.path.join(GOLDEN, "compress_4x16.json")))
+    w_base, w_ft = pins._handbuilt_4x16()
+    sg, ag = bd.compress(bf16_dev(w_base), f32_dev(w_ft))
+    assert host(sg).tolist() == g["expected_signs"]
+    assert host(ag).tolist() == g["expected_alpha_row"]
+    _, am = bd.compress(bf16_dev(w_base), f32_dev(w_ft), per_matrix=True)
+    assert host(am).tolist() == [g["expected_alpha_matrix"]]
+
+
+def test_compress_deterministic(bd):
+    w_base, w_ft = synth.layer(512, 4096, seed=1)
+    a = bd.compress(bf16_dev(w_base), f32_dev(w_ft), per_matrix=True)
+    b = bd.compress(bf16_dev(w_base), f32_dev(w_ft), per_matrix=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# --------------------------------------------------------------- reconstruct
+
+RECON_SHAPES = [(256, 512), (5, 24), (3, 2056), (300, 4096), (2048, 8192)]
+
+
+@pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
+@pytest.mark.parametrize("shape", RECON_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_reconstruct_bit_exact(bd, shape, per_matrix):
+    R, C = shape
+    w_base, w_ft = synth.layer(R, C, seed=2, index=R % 61)
+    so, ao = oracle.compress(w_base, w_ft, per_matrix=per_matrix)
+    wo = oracle.reconstruct(w_base, so, ao, per_matrix=per_matrix)
+    wg = bd.reconstruct(bf16_dev(w_base), u8_dev(so), f32_dev(ao), per_matrix=per_matrix)
+    assert np.array_equal(host_bits(wg), wo)
+
+
+def test_reconstruct_hand_cases(bd):
+    g = json.load(open(os.path.join(GOLDEN, "reconstruct_cases.json")))
+    cases = g["cases"]
+    n = len(cases)
+    w_base = np.array([[int(c[0], 16)] * 8 for c in cases], dtype=np.uint16)
+    alpha = np.array([int(c[1], 16) for c in cases], dtype=np.uint32).view(np.float32)
+    signs = np.array([[0xFF if c[2] else 0x00] for c in cases], dtype=np.uint8)
+    wg = host_bits(bd.reconstruct(bf16_dev(w_base), u8_dev(signs), f32_dev(alpha), per_matrix=False))
+    for i in range(n):
+        assert np.all(wg[i] == int(cases[i][3], 16)), (cases[i][4], hex(int(wg[i, 0])))
+
+
+# -------------------------------------------------------------------- linear
+
+
+def _layer_dev(R, C, seed, index=0, b=1e-3, per_matrix=False):
+    w_base, w_ft = synth.layer(R, C, seed=seed, index=index, b=b)
+    so, ao = oracle.compress(w_base, w_ft, per_matrix=per_matrix)
+    return w_base, so, ao, (bf16_dev(w_base), u8_dev(so), f32_dev(ao))
+
+
+DECODE_CASES = [((256, 512), m) for m in (1, 2, 3, 4, 5, 8, 9, 16)] + \
+               [((4096, 4096), m) for m in (1, 4, 16)] + \
+               [((300, 200), 3), ((7, 8), 16), ((1000, 1032), 7), ((33, 24), 1)]
+
+
+@pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
+def test_linear_decode(bd, case, per_matrix):
+    (R, C), M = case
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=3, index=M, per_matrix=per_matrix)
+    x = synth.activations(M, C, seed=3, index=M)
+    y = bd.linear(bf16_dev(x), wd, sd, ad, per_matrix=per_matrix)
+    y64, sc = oracle.linear(x, w_base, so, ao, per_matrix=per_matrix)
+    check_linear(host_bits(y), y64, sc, f"decode {R}x{C} m={M}")
+
+
+PREFILL_CASES = [((256, 512), 17), ((256, 512), 64), ((256, 512), 256), ((256, 512), 300),
+                 ((300, 200), 257), ((1000, 1032), 513), ((520, 64), 40), ((64, 4096), 600)]
+
+
+@pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
+def test_linear_prefill(bd, case, per_matrix):
+    (R, C), M = case
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=4, index=M % 61, per_matrix=per_matrix)
+    x = synth.activations(M, C, seed=4, index=M % 61)
+    y = bd.linear(bf16_dev(x), wd, sd, ad, per_matrix=per_matrix)
+    y64, sc = oracle.linear(x, w_base, so, ao, per_matrix=per_matrix)
+    check_linear(host_bits(y), y64, sc, f"prefill {R}x{C} m={M}")
+
+
+def test_linear_3d_input_and_determinism(bd):
+    R, C = 256, 512
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=5)
+    x = synth.activations(2 * 150, C, seed=5)
+    xd = bf16_dev(x).view(2, 150, C)
+    y1 = bd.linear(xd, wd, sd, ad)
+    y2 = bd.linear(xd, wd, sd, ad)
+    assert y1.shape == (2, 150, R)
+    assert torch.equal(y1, y2)
+    y64, sc = oracle.linear(x, w_base, so, ao)
+    check_linear(host_bits(y1.view(300, R)), y64, sc, "3d input")
+
+
+@pytest.mark.parametrize("M", [1, 16], ids=["m1", "m16"])
+def test_identity_decode(bd, M):
+    """One-hot x: y[t, r] must equal W_eff[r, j_t] bit for bit."""
+    R, C = 1000, 1032
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=6)
+    weff = oracle.reconstruct(w_base, so, ao)
+    cols = np.linspace(0, C - 1, M).astype(int)
+    x = np.zeros((M, C), dtype=np.float32)
+    x[np.arange(M), cols] = 1.0
+    y = host_bits(bd.linear(bf16_dev(synth.to_bf16_bits(x)), wd, sd, ad))
+    assert same_bits_pm0(y, weff[:, cols].T)
+
+
+@pytest.mark.parametrize("shape", [(384, 512), (300, 264)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_identity_prefill(bd, shape):
+    """x = I (m = d_in tokens): y = W_eff^T bit for bit."""
+    R, C = shape
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=7)
+    weff = oracle.reconstruct(w_base, so, ao)
+    eye = synth.to_bf16_bits(np.eye(C, dtype=np.float32))
+    y = host_bits(bd.linear(bf16_dev(eye), wd, sd, ad))
+    assert same_bits_pm0(y, weff.T)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 40, 300], ids=lambda m: f"m{m}")
+def test_dyadic_exact(bd, M):
+    """Exact-arithmetic inputs: every sign bit and alpha shows in y, bit for bit."""
+    R, C = 200, 256
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=40 + M)
+    y = host_bits(bd.linear(bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])))
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0])
+    assert np.array_equal(synth.bf16_bits_to_f32(y).astype(np.float64), y64)
+
+
+def test_zero_tokens_and_misaligned(bd):
+    R, C = 64, 128
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=8)
+    y = bd.linear(torch.empty((0, C), dtype=torch.bfloat16, device="cuda"), wd, sd, ad)
+    assert y.shape == (0, R)
+    big = bf16_dev(synth.activations(5, C + 1, seed=8))
+    x_bad = big.view(-1)[1:1 + 4 * C].view(4, C)   # 2-byte offset: not 16-byte aligned
+    with pytest.raises(bd.BitDeltaError) as e:
+        bd.linear(x_bad, wd, sd, ad)
+    assert e.value.status == bd.BD_EALIGN
+
+
+# -------------------------------------------- prefill on the 70B layer shapes
+
+
+SHAPES_70B = [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)]
+
+
+@pytest.mark.parametrize("shape", SHAPES_70B, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_prefill_70b_shapes(bd, shape):
+    """M = 2048 tokens: full bit-exact compress, linear checked on sampled
+    output features (first, last, tile edges, random) for every token."""
+    R, C = shape
+    M = 2048
+    w_base, w_ft = synth.layer(R, C, seed=0, index=100 + R % 57)
+    so, ao = oracle.compress(w_base, w_ft)
+    wd = bf16_dev(w_base)
+    sg, ag = bd.compress(wd, f32_dev(w_ft))
+    assert np.array_equal(host(sg), so)
+    assert np.array_equal(_bits32(host(ag)), _bits32(ao))
+    del w_ft
+    x = synth.activations(M, C, seed=0, index=100 + R % 57)
+    y = host_bits(bd.linear(bf16_dev(x), wd, sg, ag))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, R - 1], np.arange(0, R, R // 8),
+                                     synth.u64(24, 0, 9000 + R) % np.uint64(R)]).astype(np.int64))
+    y64, sc = oracle.linear(x, w_base, so, ao, rows=rows)
+    check_linear(y[:, rows], y64, sc, f"prefill {R}x{C}")
+
+
+def test_identity_prefill_8192(bd):
+    """x = I on an 8192 x 8192 layer: y = W_eff^T over the whole matrix."""
+    R = C = 8192
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=9)
+    weff = oracle.reconstruct(w_base, so, ao)
+    eye = torch.eye(C, dtype=torch.bfloat16, device="cuda")
+    y = host_bits(bd.linear(eye, wd, sd, ad))
+    assert same_bits_pm0(y, weff.T)
+
+
+# ------------------------------------------------------------------- grouped
+
+
+def _variants(R, C, V, seed, per_matrix=False):
+    w_base = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, seed, synth.tag(synth.TAG_WBASE)))
+    bv = synth.variant_scales(V, seed=seed)
+    signs = np.zeros((V, R, C // 8), dtype=np.uint8)
+    alpha = np.zeros((V, 1 if per_matrix else R), dtype=np.float32)
+    for v in range(V):
+        signs[v], alpha[v] = oracle.compress(w_base, synth.variant_ft(w_base, v, float(bv[v]), seed=seed),
+                                             per_matrix=per_matrix)
+    if per_matrix:
+        alpha = alpha[:, 0].copy()
+    return w_base, signs, alpha
+
+
+@pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
+def test_grouped_small(bd, per_matrix):
+    R, C, V, M = 300, 200, 3, 600
+    w_base, signs, alpha = _variants(R, C, V, seed=11, per_matrix=per_matrix)
+    x = synth.activations(M, C, seed=11)
+    ids = (synth.u64(M, 11, 500) % np.uint64(V)).astype(np.int32)
+    ids[[5, 77, 300]] = [-1, V, 1000]   # out of range: zero rows
+    y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), bf16_dev(w_base), u8_dev(signs), f32_dev(alpha),
+                                    per_matrix=per_matrix))
+    y64, sc = oracle.linear_grouped(x, ids, w_base, signs, alpha, per_matrix=per_matrix)
+    check_linear(y, y64, sc, "grouped small")
+    assert np.all(y[[5, 77, 300]] == 0)
+
+
+def test_grouped_equals_linear_per_variant(bd):
+    R, C, V, M = 256, 512, 4, 300
+    w_base, signs, alpha = _variants(R, C, V, seed=12)
+    x = bf16_dev(synth.activations(M, C, seed=12))
+    wd, sd, ad = bf16_dev(w_base), u8_dev(signs), f32_dev(alpha)
+    for v in range(V):
+        ids = torch.full((M,), v, dtype=torch.int32, device="cuda")
+        yg = bd.linear_grouped(x, ids, wd, sd, ad)
+        yl = bd.linear(x, wd, sd[v].contiguous(), ad[v].contiguous())
+        assert torch.equal(yg, yl), v
+
+
+def test_grouped_dyadic_exact(bd):
+    R, C, V, M = 96, 128, 14, 400
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=13, n_variants=V)
+    ids = (synth.u64(M, 13, 501) % np.uint64(V)).astype(np.int32)
+    y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), bf16_dev(w_base), u8_dev(sb), f32_dev(alpha)))
+    y64, _ = oracle.linear_grouped(x, ids, w_base, sb, alpha)
+    assert np.array_equal(synth.bf16_bits_to_f32(y).astype(np.float64), y64)
+
+
+def test_grouped_edge_sizes(bd):
+    R, C, V = 64, 64, 2
+    w_base, signs, alpha = _variants(R, C, V, seed=14)
+    wd, sd, ad = bf16_dev(w_base), u8_dev(signs), f32_dev(alpha)
+    y0 = bd.linear_grouped(torch.empty((0, C), dtype=torch.bfloat16, device="cuda"),
+                           torch.empty((0,), dtype=torch.int32, device="cuda"), wd, sd, ad)
+    assert y0.shape == (0, R)
+    x = synth.activations(1, C, seed=14)
+    ids = np.array([1], dtype=np.int32)
+    y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), wd, sd, ad))
+    y64, sc = oracle.linear_grouped(x, ids, w_base, signs, alpha)
+    check_linear(y, y64, sc, "grouped m=1")
+
+
+def test_grouped_zipf_14_variants(bd):
+    """One 8192 x 8192 base, 14 variants, 4096 tokens in a Zipf(1.1) split:
+    per-variant compress bit-exact, sampled output features for every token."""
+    R = C = 8192
+    V, M = 14, 4096
+    w_base = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, 0, synth.tag(synth.TAG_WBASE, 200)))
+    wd = bf16_dev(w_base)
+    bv = synth.variant_scales(V, seed=0)
+    rows = np.unique(np.concatenate([[0, 255, 256, R - 1], synth.u64(12, 0, 9100) % np.uint64(R)]).astype(np.int64))
+    signs = torch.empty((V, R, C // 8), dtype=torch.uint8, device="cuda")
+    alpha = torch.empty((V, R), dtype=torch.float32, device="cuda")
+    # The oracle sees only its own compress output, on the sampled rows (the
+    # rows it is asked about); the other rows stay zero and are never read.
+    so_rows = np.zeros((V, R, C // 8), dtype=np.uint8)
+    ao_all = np.zeros((V, R), dtype=np.float32)
+    for v in range(V):
+        w_ft = synth.variant_ft(w_base, v, float(bv[v]), seed=0, index=200)
+        sg, ag = bd.compress(wd, f32_dev(w_ft))
+        signs[v], alpha[v] = sg, ag
+        so, ao = oracle.compress(w_base[rows], w_ft[rows])
+        assert np.array_equal(host(sg)[rows], so) and np.array_equal(_bits32(host(ag)[rows]), _bits32(ao))
+        so_rows[v][rows], ao_all[v][rows] = so, ao
+    counts = synth.zipf_counts(M, V, 1.1)
+    ids = synth.variant_ids(counts, seed=0)
+    x = synth.activations(M, C, seed=0, index=200)
+    y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), wd, signs, alpha))
+    y64, sc = oracle.linear_grouped(x, ids, w_base, so_rows, ao_all, rows=rows)
+    check_linear(y[:, rows], y64, sc, "grouped zipf")
