@@ -1,0 +1,414 @@
+#!/usr/bin/env python
+"""Benchmark of the BitDelta hot path on one MI355X; prints ONE JSON line.
+
+Workload of the headline number: the decode layer of the post's 70B-class
+model, one 4096 x 4096 bf16 weight with packed 1-bit deltas.  One step is a
+full pass of the single-layer hot path over one batch:
+  compress (per-row alpha) -> compress (per-matrix alpha) -> reconstruct ->
+  fused linear at m = 1, 4, 16 tokens with per-row alpha -> the same three
+  with the per-matrix alpha,
+each call reading its own weight set out of 16 rotating sets (571 MB of
+weights, more than the 256 MB MALL, so every step streams from HBM).
+`value` is the step's algorithmic HBM bytes (inputs read + outputs written,
+per kernel) divided by its time: GB/s.  The steps are captured in HIP graphs
+(one per weight set) so the microsecond-scale decode launches are not bound
+by host launch overhead; the timed region replays exactly --steps steps.
+
+The same line carries:
+  kernels     per-kernel average launch time (HIP events around graph
+              replays of that kernel alone, on its own stream) and GB/s;
+  roofline    for the dominant kernel of the step (largest share of step
+              time), against 8 TB/s;
+  prefill     the fused MFMA GEMM at m = 2048 tokens on the q/o, k/v,
+              gate/up and down shapes (TFLOP/s and fraction of the 2.5
+              PFLOP/s bf16 dense peak);
+  grouped     14 variants over one shared 8192 x 8192 base, 4096 tokens in a
+              Zipf(1.1) split (TFLOP/s);
+  cpu_baseline  the oracle timed on the host cores on the same step, at the
+              same shape, on host-generated inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused BitDelta linear: prefill TFLOP/s + decode HBM GB/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+R = C = 4096          # decode layer
+DECODE_M = (1, 4, 16)
+SETS = 16
+PREFILL_SHAPES = [("q/o", 8192, 8192), ("k/v", 1024, 8192), ("gate/up", 28672, 8192), ("down", 8192, 28672)]
+PREFILL_M = 2048
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-grouped", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- decode step
+
+
+class DecodeStep:
+    """Buffers and the ordered list of C-ABI launches of one step per weight set."""
+
+    def __init__(self, torch, bd, synth):
+        self.torch, self.bd = torch, bd
+        dev = torch.device("cuda")
+        self.sets = []
+        for i in range(SETS):
+            w_base, w_ft = synth.device_layer(R, C, seed=0, index=i)
+            s = dict(w_base=w_base, w_ft=w_ft,
+                     signs=torch.empty((R, C // 8), dtype=torch.uint8, device=dev),
+                     alpha=torch.empty((R,), dtype=torch.float32, device=dev),
+                     alpha_m=torch.empty((1,), dtype=torch.float32, device=dev),
+                     ws=torch.empty((bd.lib.bitdelta_compress_workspace(R, C, 1),), dtype=torch.uint8, device=dev))
+            self.sets.append(s)
+        self.weff = [torch.empty((R, C), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        self.x = {m: synth.device_activations(m, C, seed=0, index=m) for m in DECODE_M}
+        self.y = {m: [torch.empty((m, R), dtype=torch.bfloat16, device=dev) for _ in range(2)] for m in DECODE_M}
+        torch.cuda.synchronize()
+        # kernels of the step: name -> (algorithmic bytes per launch, launches per step)
+        w = R * C
+        self.bytes = {
+            "compress_row": w * 2 + w * 4 + w // 8 + 4 * R,
+            "compress_matrix": w * 2 + w * 4 + w // 8 + 4,
+            "reconstruct": w * 2 + w // 8 + 4 * R + w * 2,
+        }
+        for m in DECODE_M:
+            self.bytes[f"linear_m{m}_row"] = w * 2 + w // 8 + 4 * R + 2 * m * C + 2 * m * R
+            self.bytes[f"linear_m{m}_matrix"] = w * 2 + w // 8 + 4 + 2 * m * C + 2 * m * R
+
+    def launch(self, name, i, stream):
+        """Enqueue one kernel of the step for weight set i on `stream` (raw C ABI)."""
+        bd, s = self.bd, self.sets[i]
+        P = ctypes.c_void_p
+        st = P(stream.cuda_stream)
+        if name == "compress_row":
+            rc = bd.lib.bitdelta_compress(P(s["w_base"].data_ptr()), P(s["w_ft"].data_ptr()), bd.BD_F32, R, C,
+                                          bd.BD_ALPHA_ROW, P(s["signs"].data_ptr()), P(s["alpha"].data_ptr()),
+                                          None, 0, st)
+        elif name == "compress_matrix":
+            rc = bd.lib.bitdelta_compress(P(s["w_base"].data_ptr()), P(s["w_ft"].data_ptr()), bd.BD_F32, R, C,
+                                          bd.BD_ALPHA_MATRIX, P(s["signs"].data_ptr()), P(s["alpha_m"].data_ptr()),
+                                          P(s["ws"].data_ptr()), s["ws"].numel(), st)
+        elif name == "reconstruct":
+            rc = bd.lib.bitdelta_reconstruct(P(s["w_base"].data_ptr()), P(s["signs"].data_ptr()),
+                                             P(s["alpha"].data_ptr()), bd.BD_ALPHA_ROW, R, C,
+                                             P(self.weff[i % 2].data_ptr()), st)
+        else:
+            _, mm, mode = name.split("_")
+            m = int(mm[1:])
+            a = s["alpha"] if mode == "row" else s["alpha_m"]
+            rc = bd.lib.bitdelta_linear(P(self.x[m].data_ptr()), m, P(s["w_base"].data_ptr()),
+                                        P(s["signs"].data_ptr()), P(a.data_ptr()),
+                                        bd.BD_ALPHA_ROW if mode == "row" else bd.BD_ALPHA_MATRIX, R, C,
+                                        P(self.y[m][i % 2].data_ptr()), None, 0, st)
+        bd.check(rc)
+
+    def step(self, i, stream):
+        for name in self.bytes:
+            self.launch(name, i, stream)
+
+    @property
+    def step_bytes(self):
+        return sum(self.bytes.values())
+
+
+def capture(torch, fn):
+    """Capture fn(stream) into a HIP graph (torch's capture stream is current)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(s)  # eager warm-up call outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, n, warm):
+    """Replay graphs round-robin; time exactly n replays with HIP events on the replay stream."""
+    stream = torch.cuda.current_stream()
+    for k in range(warm):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(n):
+        graphs[k % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall  # seconds (device events), seconds (host wall)
+
+
+def run_decode(torch, bd, synth, steps, warmup):
+    ds = DecodeStep(torch, bd, synth)
+    step_graphs = [capture(torch, lambda s, i=i: ds.step(i, s)) for i in range(SETS)]
+    dev_s, wall_s = time_graphs(torch, step_graphs, steps, warmup)
+    # per-kernel: a graph of SETS launches (one per weight set) of that kernel alone
+    kernels = {}
+    for name, nbytes in ds.bytes.items():
+        g = capture(torch, lambda s, name=name: [ds.launch(name, i, s) for i in range(SETS)])
+        reps = max(8, 2000 // SETS)
+        t, _ = time_graphs(torch, [g], reps, 4)
+        us = t / (reps * SETS) * 1e6
+        kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+                         "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del g
+    del step_graphs
+    return ds, dev_s, wall_s, kernels
+
+
+# -------------------------------------------------------------------- prefill
+
+
+def run_prefill(torch, bd, synth, reps=10):
+    out = {}
+    dev = torch.device("cuda")
+    for label, N, K in PREFILL_SHAPES:
+        sets = []
+        for i in range(2):
+            w_base, w_ft = synth.device_layer(N, K, seed=1, index=10 * i + len(out))
+            signs, alpha = bd.compress(w_base, w_ft)
+            del w_ft
+            sets.append((w_base, signs, alpha))
+        x = synth.device_activations(PREFILL_M, K, seed=1, index=len(out))
+        y = torch.empty((PREFILL_M, N), dtype=torch.bfloat16, device=dev)
+        P = ctypes.c_void_p
+
+        def call(i, s):
+            w, sg, a = sets[i % 2]
+            bd.check(bd.lib.bitdelta_linear(P(x.data_ptr()), PREFILL_M, P(w.data_ptr()), P(sg.data_ptr()),
+                                            P(a.data_ptr()), bd.BD_ALPHA_ROW, N, K, P(y.data_ptr()), None, 0,
+                                            P(s.cuda_stream)))
+
+        stream = torch.cuda.current_stream()
+        for i in range(3):
+            call(i, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        flop = 2.0 * PREFILL_M * N * K
+        tf = flop / us / 1e6
+        out[label] = {"d_out": N, "d_in": K, "m": PREFILL_M, "us": round(us, 1), "TFLOP/s": round(tf, 1),
+                      "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+        log(f"prefill {label} [{N},{K}] m={PREFILL_M}: {us:.1f} us, {tf:.1f} TFLOP/s")
+        del sets, x, y
+        torch.cuda.empty_cache()
+    tot_flop = sum(2.0 * PREFILL_M * v["d_out"] * v["d_in"] for v in out.values())
+    tot_us = sum(v["us"] for v in out.values())
+    agg = tot_flop / tot_us / 1e6
+    return {"shapes": out, "layer_TFLOP/s": round(agg, 1), "layer_frac_mfma": round(agg / BF16_PEAK_TFLOPS, 4),
+            "peak_TFLOP/s": BF16_PEAK_TFLOPS}
+
+
+# -------------------------------------------------------------------- grouped
+
+
+def run_grouped(torch, bd, synth, reps=10):
+    dev = torch.device("cuda")
+    N = K = 8192
+    V, M = 14, 4096
+    w_base = synth.device_normal((N, K), 0.02, 2, synth.tag(synth.TAG_WBASE), dev, torch.bfloat16)
+    bv = synth.variant_scales(V, seed=0)
+    signs = torch.empty((V, N, K // 8), dtype=torch.uint8, device=dev)
+    alpha = torch.empty((V, N), dtype=torch.float32, device=dev)
+    for v in range(V):
+        w_ft = w_base.float().add_(synth.device_laplace((N, K), float(bv[v]), 2, synth.tag(synth.TAG_VARIANT + v), dev))
+        sg, a = bd.compress(w_base, w_ft)
+        signs[v].copy_(sg)
+        alpha[v].copy_(a)
+        del w_ft, sg, a
+    counts = synth.zipf_counts(M, V, 1.1)
+    ids = torch.from_numpy(synth.variant_ids(counts, seed=0)).to(dev)
+    x = synth.device_activations(M, K, seed=2)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    nws = bd.lib.bitdelta_linear_grouped_workspace(M, V, N, K)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bd.check(bd.lib.bitdelta_linear_grouped(P(x.data_ptr()), M, P(ids.data_ptr()), V, P(w_base.data_ptr()),
+                                                P(signs.data_ptr()), P(alpha.data_ptr()), bd.BD_ALPHA_ROW, N, K,
+                                                P(y.data_ptr()), P(ws.data_ptr()), nws, P(stream.cuda_stream)))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flop = 2.0 * M * N * K
+    tf = flop / us / 1e6
+    log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s")
+    return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
+            "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+# ----------------------------------------------------------------- cpu oracle
+
+
+def run_cpu_baseline(target_s):
+    """The oracle, untuned, on the same decode step on host-generated inputs of
+    the same shape; repeated until about target_s seconds have elapsed."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    w_base, w_ft = synth.layer(R, C, seed=0)
+    xs = {m: synth.activations(m, C, seed=0, index=m) for m in DECODE_M}
+    bytes_step = 0
+    w = R * C
+    bytes_step += 2 * (w * 6 + w // 8) + 4 * R + 4          # two compresses
+    bytes_step += w * 4 + w // 8 + 4 * R                    # reconstruct
+    for m in DECODE_M:
+        bytes_step += 2 * (w * 2 + w // 8 + 2 * m * C + 2 * m * R) + 4 * R + 4
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        signs, alpha = oracle.compress(w_base, w_ft)
+        _, alpha_m = oracle.compress(w_base, w_ft, per_matrix=True)
+        oracle.reconstruct(w_base, signs, alpha)
+        for m in DECODE_M:
+            oracle.linear(xs[m], w_base, signs, alpha)
+            oracle.linear(xs[m], w_base, signs, alpha_m, per_matrix=True)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    gbs = bytes_step * n / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(oracle.num_threads()), "kind": "oracle",
+            "sample": f"the full decode step (2 compresses, reconstruct, linear m=1,4,16 x 2 alpha modes) on one "
+                      f"4096x4096 layer, host-generated inputs, repeated {n} times in {el:.1f} s",
+            "seconds_per_step": round(el / n, 4), "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------- main
+
+
+def traffic_for(kernel_name):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the current kernel sources (profiles/traffic.json); else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    entry = rec.get("kernels", {}).get(kernel_name)
+    if not entry or entry.get("source_sha") != source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tenant_fine_tune_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              f"Sharding is described in the design notes; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import synth
+    import tenant_fine_tune_amd as bd
+
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup)
+    ms_per_step = dev_s / args.steps * 1e3
+    value = ds.step_bytes * args.steps / dev_s / 1e9
+    log(f"decode step: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s (wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
+    for k, v in kernels.items():
+        log(f"  {k:22s} {v['us']:8.2f} us  {v['GB/s']:8.1f} GB/s  {100 * v['frac_hbm']:.1f}% of HBM")
+    # dominant kernel: largest share of the step's time
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom),
+                "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_us": kd["us"]}
+    step_bytes = ds.step_bytes
+    del ds
+    torch.cuda.empty_cache()
+
+    prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
+    grouped = None if args.no_grouped else run_grouped(torch, bd, synth)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode layer 4096x4096 bf16 + packed 1-bit deltas: compress (row and matrix alpha), "
+                               "reconstruct, fused linear m=1,4,16 (row and matrix alpha); 16 rotating weight sets",
+                   "d_out": R, "d_in": C, "m": list(DECODE_M), "weight_sets": SETS, "parallelism": "single GPU",
+                   "step_bytes": step_bytes},
+        "roofline": roofline,
+        "kernels": kernels,
+        "prefill": prefill,
+        "grouped": grouped,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

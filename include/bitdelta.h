@@ -111,7 +111,8 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
  * fused_bitdelta_linear sketch): y = x W_eff^T with W_eff formed in registers
  * and LDS only.  fp32 accumulation, bf16 output (nearest-even).
  * x: bf16 [m, d_in]; y: bf16 [m, d_out].  m <= 16 runs the bandwidth-bound
- * decode kernel; larger m the bf16-MFMA prefill kernel.
+ * decode kernel; larger m the bf16-MFMA prefill kernel, which needs x, W_base
+ * and y each below 2 GiB (BD_ESHAPE otherwise).
  * workspace: at least bitdelta_linear_workspace(m, d_out, d_in) bytes,
  * 16-byte aligned (may be NULL when that is 0). */
 size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in);
@@ -128,7 +129,8 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
  * zero row.  signs: uint8 [n_variants, d_out, d_in/8]; alpha: fp32
  * [n_variants, d_out] (BD_ALPHA_ROW) or [n_variants] (BD_ALPHA_MATRIX).
  * Tokens are bucketed by variant on the device (no host synchronisation).
- * n_variants must be in [1, 4096].
+ * n_variants must be in [1, 4096]; x, W_base, y and each variant's signs
+ * must be below 2 GiB (BD_ESHAPE otherwise).
  * workspace: at least bitdelta_linear_grouped_workspace() bytes, 16-byte
  * aligned. */
 size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t d_out, int64_t d_in);

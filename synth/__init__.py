@@ -150,3 +150,48 @@ def variant_ids(counts, seed: int = 0, shuffle: bool = True) -> np.ndarray:
             j = int(u[i] * (i + 1))
             ids[i], ids[j] = ids[j], ids[i]
     return ids
+
+
+# ------------------------------------------------------------ device side
+# Large benchmark inputs are drawn on the GPU with torch's seeded Philox
+# generator (same laws as above; values differ from the host streams, which
+# is fine: these feed timing runs, parity tests use the host streams).
+
+
+def _gen(seed: int, tg: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1000003 + int(tg)) & ((1 << 63) - 1))
+    return g
+
+
+def device_normal(shape, std: float, seed: int, tg: int, device="cuda", dtype=None):
+    import torch
+
+    t = torch.randn(shape, generator=_gen(seed, tg, device), device=device, dtype=torch.float32).mul_(std)
+    return t if dtype is None else t.to(dtype)
+
+
+def device_laplace(shape, b: float, seed: int, tg: int, device="cuda"):
+    """Inverse-CDF Laplace(0, b) draws, fp32."""
+    import torch
+
+    t = torch.rand(shape, generator=_gen(seed, tg, device), device=device, dtype=torch.float64) - 0.5
+    return (-b * torch.sign(t) * torch.log1p(-2.0 * t.abs())).to(torch.float32)
+
+
+def device_layer(d_out: int, d_in: int, seed: int = 0, index: int = 0, b: float = 1e-3,
+                 std: float = 0.02, device="cuda"):
+    """(W_base bf16, W_ft fp32 = fl32(W_base + Delta)) on the device."""
+    import torch
+
+    w_base = device_normal((d_out, d_in), std, seed, tag(TAG_WBASE, index), device, torch.bfloat16)
+    w_ft = w_base.float().add_(device_laplace((d_out, d_in), b, seed, tag(TAG_DELTA, index), device))
+    return w_base, w_ft
+
+
+def device_activations(m: int, d_in: int, seed: int = 0, index: int = 0, device="cuda"):
+    import torch
+
+    return device_normal((m, d_in), 1.0, seed, tag(TAG_X, index), device, torch.bfloat16)

@@ -50,6 +50,14 @@ bd_status check_matrix(int64_t d_out, int64_t d_in)
     return BD_OK;
 }
 
+// The prefill kernels address x, W_base, signs and y through 32-bit buffer
+// offsets: each operand (per variant for signs) must stay below 2 GiB.
+bool operands_fit(int64_t m, int64_t d_out, int64_t d_in)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return m * d_in * 2 < lim && d_out * d_in * 2 < lim && m * d_out * 2 < lim;
+}
+
 bd_status check_mode(int mode)
 {
     if (mode != BD_ALPHA_ROW && mode != BD_ALPHA_MATRIX)
@@ -194,6 +202,9 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, co
         return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
                       "bitdelta_linear (decode)");
     const int64_t tiles = ((m + bd::kGemmBM - 1) / bd::kGemmBM) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
+    if (!operands_fit(m, d_out, d_in))
+        return fail(BD_ESHAPE, "prefill operands must each be below 2 GiB (m=%lld, d_out=%lld, d_in=%lld)",
+                    (long long)m, (long long)d_out, (long long)d_in);
     if (tiles > kMaxGrid)
         return fail(BD_ESHAPE, "linear m=%lld d_out=%lld exceeds the prefill grid", (long long)m, (long long)d_out);
     return device(bd::launch_gemm(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
@@ -240,6 +251,9 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
     BD_ALIGNED(alpha, 4);
     BD_ALIGNED(variant_ids, 4);
     BD_ALIGNED(workspace, 16);
+    if (!operands_fit(m, d_out, d_in))
+        return fail(BD_ESHAPE, "grouped operands must each be below 2 GiB (m=%lld, d_out=%lld, d_in=%lld)",
+                    (long long)m, (long long)d_out, (long long)d_in);
     const int64_t tiles = bd::grouped_max_tiles(m, n_variants) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
     if (tiles > kMaxGrid)
         return fail(BD_ESHAPE, "grouped m=%lld d_out=%lld exceeds the grid", (long long)m, (long long)d_out);

@@ -11,18 +11,25 @@
 // Tile: 256 tokens x 256 output features per workgroup, K stepped by 64.
 // Four waves; wave w owns output features [64w, 64w+64) of the tile for all
 // 256 tokens (8 x 2 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
-// accumulators per lane).  Per K step:
-//  - the 256 x 64 activation tile is staged in LDS (rows padded by 16 bytes
-//    so the 16-byte fragment reads of 32 consecutive rows hit distinct banks);
-//  - each wave loads its own 64 x 64 slice of W_base directly in the MFMA
-//    B-operand layout (lane l: feature l%32, 8 consecutive k) plus the sign
-//    bytes, forms W_eff = bf16(W_base + +-alpha) in VGPRs and feeds it to the
-//    MFMA without any LDS round trip: each weight is rebuilt exactly once per
-//    workgroup;
-//  - the next step's global loads are issued before the MFMAs of this one.
+// accumulators per lane).  Pipeline, per K step t:
+//  - activations: the tile of step t+1 is copied HBM -> LDS by direct-to-LDS
+//    loads (no VGPRs, no LDS write instructions) into the other of two LDS
+//    buffers; rows are stored unpadded with the 16-byte chunks of row r
+//    permuted by c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 32
+//    consecutive rows spread over all banks;
+//  - weights: each wave loads its own 64 x 64 slice of W_base straight in the
+//    MFMA B-operand layout (lane l: feature l%32, 8 consecutive k) with the
+//    sign bytes, two steps ahead; while the MFMAs of step t run, the VALU
+//    forms step t+1's W_eff = bf16(W_base + +-alpha) fragments in VGPRs, so
+//    each weight is rebuilt exactly once per workgroup and never touches LDS;
+//  - one barrier per step.  Every load address is clamped into its tensor
+//    (tail rows/columns read valid data whose results are discarded or
+//    multiplied by zero), so no load sits under a branch.
 // Workgroups are remapped so that the ones sharing an output-feature tile run
 // on the same XCD (blocks are dealt round-robin over the 8 XCDs), so each
 // W_base tile is fetched into one L2 once.
+#include <type_traits>
+
 #include "bd_device.h"
 #include "bd_launch.h"
 
@@ -30,7 +37,6 @@ namespace bd {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64;
-constexpr int LDS_LD = BK + 8;  // bf16 per LDS row
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
@@ -42,56 +48,44 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
     return (b % kXcds) * per + b / kXcds;
 }
 
-struct Stage {
-    uint4 xr[8];
-    uint4 wr[2][4];
-    uint32_t sr[2][4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// GATHER = false: tile rows are tokens m0 .. m0+255 of x.
-// GATHER = true : tile rows are the tokens listed in rows_s (grouped path).
-template <bool PER_MATRIX, bool GATHER>
-__device__ __forceinline__ void load_stage(Stage &st, const uint16_t *__restrict__ x, int64_t M,
-                                           const int32_t *rows_s, int64_t m0,
-                                           const uint16_t *__restrict__ w_base,
-                                           const uint8_t *__restrict__ signs, int64_t N, int64_t K,
-                                           int64_t n_lane0, int64_t k0, int lane)
+// Buffer offset of a row that does not exist: beyond every tensor (all
+// tensors are below 2 GiB, checked on the host) without wrapping when a K
+// offset is added, so loads return zero and stores are dropped.
+constexpr uint32_t kInvalidOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
-    const int64_t G = K >> 3;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = threadIdx.x + kThreads * i;
-        const int row = q >> 3, c = q & 7;
-        const int64_t kc = k0 + c * 8;
-        int64_t tok;
-        if constexpr (GATHER)
-            tok = rows_s[row];
-        else
-            tok = m0 + row < M ? m0 + row : -1;
-        st.xr[i] = (tok >= 0 && kc < K) ? *reinterpret_cast<const uint4 *>(x + tok * K + kc)
-                                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t n = n_lane0 + nb * 32;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int64_t kc = k0 + kb * 16 + 8 * (lane >> 5);
-            const bool ok = n < N && kc < K;
-            st.wr[nb][kb] = ok ? *reinterpret_cast<const uint4 *>(w_base + n * K + kc) : make_uint4(0, 0, 0, 0);
-            st.sr[nb][kb] = ok ? (uint32_t)signs[n * G + (kc >> 3)] : 0u;
-        }
-    }
+    // raw buffer: stride 0, num_records in bytes, default data format word
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // s_waitcnt encoding on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool PER_MATRIX, bool GATHER>
+struct WRaw {
+    uint4 w[2][4];     // [nb][kb]: 8 consecutive bf16 of one feature row
+    uint32_t s[2][2];  // [nb]: sign bytes of the 64 columns of the step (8 bytes)
+};
+
+// K64: d_in is a multiple of 64, so a step's 8 sign bytes are one aligned
+// 8-byte load; otherwise they are fetched byte by byte.
+template <bool PER_MATRIX, bool GATHER, bool K64>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
                 const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
                 int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
                 const int32_t *__restrict__ table, int32_t n_variants)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[BM * LDS_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * BM * BK];
     __shared__ int32_t rows_s[BM];
 
     const int lane = threadIdx.x & 63;
@@ -131,13 +125,102 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
         m0 = 0;
     }
 
-    const int64_t n_lane0 = n0 + wave * 64 + (lane & 31);
+    const int64_t G = K >> 3;
+    const int T = (int)((K + BK - 1) / BK);
+    const int hi = lane >> 5;  // which 8-column half of a 16-column k block
+
+    // Buffer resources: 32-bit byte offsets, hardware bounds checks (loads
+    // past the end return zero, stores past it are dropped).
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, N * K * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, N * G);
+
+    // ---- activation DMA: wave w copies slots [512w, 512w + 512) of a tile,
+    // slot s = 8 * row + p holding logical chunk p ^ ((row >> 1) & 7) of
+    // tile row `row`; instruction j covers rows 64w + 8j .. 64w + 8j + 7.
+    // Rows past M read zeros; columns past K read the next row (finite, and
+    // multiplied by the zero W_eff of those columns).
+    uint32_t xoff[GATHER ? 8 : 2];
+    int64_t xrow_stride = 0;  // bytes between instruction j and j+1 (dense)
+    {
+        const int p = lane & 7;
+#pragma unroll
+        for (int j = 0; j < (GATHER ? 8 : 2); ++j) {
+            const int row = wave * 64 + j * 8 + (lane >> 3);
+            const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
+            int64_t tok;
+            if constexpr (GATHER)
+                tok = rows_s[row];
+            else
+                tok = m0 + row;
+            xoff[j] = (tok < 0 || tok >= M) ? kInvalidOffset : (uint32_t)((tok * K + c * 8) * 2);
+        }
+        xrow_stride = 8 * K * 2;
+    }
+    auto dma_x = [&](int t, int buf) {
+        const uint32_t kbytes = (uint32_t)((int64_t)t * BK * 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t vo;
+            if constexpr (GATHER)
+                vo = xoff[j] + kbytes;
+            else
+                vo = xoff[j & 1] + (uint32_t)((j >> 1) * 2 * xrow_stride) + kbytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xs + buf * BM * BK + (wave * 8 + j) * 512), 16,
+                                                     vo, 0, 0, 0);
+        }
+    };
+
+    // ---- weights: lane's feature rows and per-row alpha
+    uint32_t woff[2], soff[2];
     float a[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-        const int64_t n = n_lane0 + nb * 32;
-        a[nb] = PER_MATRIX ? alpha[0] : (n < N ? alpha[n] : 0.0f);
+        const int64_t n = n0 + wave * 64 + nb * 32 + (lane & 31);
+        const bool ok = n < N;
+        woff[nb] = ok ? (uint32_t)((n * K + 8 * hi) * 2) : kInvalidOffset;
+        soff[nb] = ok ? (uint32_t)(n * G) : kInvalidOffset;
+        a[nb] = PER_MATRIX ? alpha[0] : (ok ? alpha[n] : 0.0f);
     }
+    auto load_w = [&](WRaw &r, int t) {
+        const uint32_t k0b = (uint32_t)((int64_t)t * BK * 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                r.w[nb][kb] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + k0b + kb * 32, 0, 0));
+            if constexpr (K64) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, soff[nb] + (uint32_t)(t * 8), 0, 0);
+                r.s[nb][0] = v[0];
+                r.s[nb][1] = v[1];
+            } else {
+                uint32_t v[2] = {0, 0};
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    v[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff[nb] + (uint32_t)(t * 8) + i, 0, 0)
+                                 << (8 * (i & 3));
+                r.s[nb][0] = v[0];
+                r.s[nb][1] = v[1];
+            }
+        }
+    };
+    auto build_b = [&](bf16x8 (&B)[2][4], const WRaw &r, int t) {
+        const int64_t k0 = (int64_t)t * BK;
+        const bool tail = k0 + BK > K;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int byte_i = kb * 2 + hi;  // sign byte of this lane's 8 columns
+                const uint32_t byte = (r.s[nb][byte_i >> 2] >> (8 * (byte_i & 3))) & 0xFFu;
+                uint4 e = weff_group(r.w[nb][kb], byte, a[nb]);
+                if (tail && k0 + kb * 16 + 8 * hi >= K)
+                    e = make_uint4(0, 0, 0, 0);
+                B[nb][kb] = __builtin_bit_cast(bf16x8, e);
+            }
+        }
+    };
 
     f32x16 acc[8][2];
 #pragma unroll
@@ -148,55 +231,81 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
             for (int v = 0; v < 16; ++v)
                 acc[mb][nb][v] = 0.0f;
 
-    Stage st;
-    load_stage<PER_MATRIX, GATHER>(st, x, M, rows_s, m0, w_base, signs, N, K, n_lane0, 0, lane);
-
-    for (int64_t k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = threadIdx.x + kThreads * i;
-            *reinterpret_cast<uint4 *>(&xs[(q >> 3) * LDS_LD + (q & 7) * 8]) = st.xr[i];
-        }
-        bf16x8 B[2][4];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                B[nb][kb] = __builtin_bit_cast(bf16x8, weff_group(st.wr[nb][kb], st.sr[nb][kb] >> (0), a[nb]));
-        if (k0 + BK < K)
-            load_stage<PER_MATRIX, GATHER>(st, x, M, rows_s, m0, w_base, signs, N, K, n_lane0, k0 + BK, lane);
-        __syncthreads();
+    // A fragment address within a buffer: row mb*32 + (lane&31), logical
+    // chunk kb*2 + hi, stored at chunk position (kb*2 + hi) ^ ((row >> 1) & 7).
+    const int arow = lane & 31;
+    const int asw = (arow >> 1) & 7;
+    auto mfma_step = [&](const bf16x8 (&B)[2][4], int buf) {
+        const uint16_t *base = xs + buf * BM * BK + arow * BK;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            const int chunk = (kb * 2 + hi) ^ asw;
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
-                    &xs[(mb * 32 + (lane & 31)) * LDS_LD + kb * 16 + 8 * (lane >> 5)]);
+                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(base + mb * 32 * BK + chunk * 8);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[nb][kb], acc[mb][nb], 0, 0, 0);
             }
         }
+    };
+
+    // ---- prologue: x(0) -> LDS[0], W(0), W(1); build B(0)
+    WRaw wr[2];
+    bf16x8 B[2][2][4];
+    dma_x(0, 0);
+    load_w(wr[0], 0);
+    load_w(wr[1], T > 1 ? 1 : 0);
+    build_b(B[0], wr[0], 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- main loop, unrolled by two so buffers and register stages are static
+    auto step = [&](int t, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        constexpr int nxt = 1 - cur;
+        const int t1 = t + 1 < T ? t + 1 : T - 1;
+        const int t2 = t + 2 < T ? t + 2 : T - 1;
+        dma_x(t1, nxt);              // 8 vector-memory ops
+        load_w(wr[cur], t2);         // W(t+2) into the stage W(t) used to occupy
+        // keep the loads ahead of the work that follows (the scheduler would
+        // otherwise hoist the W_eff build above them and stall on W(t+1))
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(B[cur], cur);
+        build_b(B[nxt], wr[nxt], t1);
+        __builtin_amdgcn_sched_barrier(0);
+        // x(t+1) must have landed; W(t+2) (4 x 16-byte loads per feature
+        // block plus its sign loads) may stay in flight
+        wait_vmcnt<K64 ? 10 : 24>();
+        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < T)
+        step(t, std::integral_constant<int, 0>{});
 
     // Output: lane l holds feature column l%32 of each 32x32 block; register
-    // v holds token row 8*(v/4) + 4*(l/32) + v%4 of the block.
+    // v holds token row 8*(v/4) + 4*(l/32) + v%4 of the block.  Rows and
+    // features that do not exist get an out-of-range offset (store dropped).
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t j = n0 + wave * 64 + nb * 32 + (lane & 31);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int64_t j = n_lane0 + nb * 32;
+        for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int i = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int i = mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
                 int64_t tok;
                 if constexpr (GATHER)
                     tok = rows_s[i];
                 else
                     tok = m0 + i < M ? m0 + i : -1;
-                if (tok >= 0 && j < N)
-                    y[tok * N + j] = to_bf16(acc[mb][nb][v]);
+                const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
+                __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
             }
         }
     }
@@ -255,7 +364,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tokens(const int32_t *_
     int32_t *tile_rows = tile_row0 + max_tiles;
     const int32_t total = tstart[nb];
     for (int ti = threadIdx.x; ti < total; ti += kBucketThreads) {
-        int lo = 0, hi = nb - 1;  // last bucket with tstart <= ti
+        int lo = 0, hi = nb - 1;  // last bucket with tstart <= ti (a non-empty one)
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (tstart[mid] <= ti)
@@ -263,9 +372,6 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tokens(const int32_t *_
             else
                 hi = mid - 1;
         }
-        // skip empty buckets that share the same start
-        while (lo + 1 < nb && tstart[lo + 1] <= ti)
-            ++lo;
         const int32_t r0 = seg[lo] + (ti - tstart[lo]) * BM;
         tile_v[ti] = lo;
         tile_row0[ti] = r0;
@@ -273,20 +379,32 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tokens(const int32_t *_
     }
 }
 
+template <bool GATHER, bool K64>
+hipError_t launch_tiles2(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
+                         const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
+                         int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s)
+{
+    const int64_t n_tiles = (d_out + BN - 1) / BN;
+    const dim3 grid((unsigned)(m_tiles * n_tiles)), block(kThreads);
+    if (per_matrix)
+        hipLaunchKernelGGL((gemm_tiles<true, GATHER, K64>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
+                           d_in, y, m_tiles, table, n_variants);
+    else
+        hipLaunchKernelGGL((gemm_tiles<false, GATHER, K64>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
+                           d_in, y, m_tiles, table, n_variants);
+    return hipGetLastError();
+}
+
 template <bool GATHER>
 hipError_t launch_tiles(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                         const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                         int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s)
 {
-    const int64_t n_tiles = (d_out + BN - 1) / BN;
-    const dim3 grid((unsigned)(m_tiles * n_tiles)), block(kThreads);
-    if (per_matrix)
-        hipLaunchKernelGGL((gemm_tiles<true, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, d_in, y,
-                           m_tiles, table, n_variants);
-    else
-        hipLaunchKernelGGL((gemm_tiles<false, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, d_in, y,
-                           m_tiles, table, n_variants);
-    return hipGetLastError();
+    if (d_in % 64 == 0)
+        return launch_tiles2<GATHER, true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
+                                           n_variants, s);
+    return launch_tiles2<GATHER, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
+                                        n_variants, s);
 }
 
 }  // namespace
