@@ -71,6 +71,14 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// vmcnt(N) and lgkmcnt(0) in one wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 struct WRaw {
     uint4 w[2][4];     // [nb][kb]: 8 consecutive bf16 of one feature row
     uint32_t s[2][2];  // [nb]: sign bytes of the 64 columns of the step (8 bytes)
@@ -311,6 +319,267 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (d_in a multiple of 64): the W_base slices and sign bytes of the
+// next steps are also copied HBM -> LDS by direct-to-LDS loads, two steps
+// ahead, instead of being staged in VGPRs.  Each wave copies and reads only
+// its own 64 feature rows, so the copies need no barrier, only the wave's
+// own wait.  The registers this frees hold a second set of A fragments, so
+// the LDS reads of k block kb+1 are in flight while the MFMAs of kb run.
+// LDS (static, 133 KB): x tiles 2 x 32 KB, W tiles 2 x 32 KB, sign tiles
+// 2 x 2 KB, gathered rows 1 KB.
+constexpr int kXsBytes = BM * BK * 2;                    // 32768
+constexpr int kWsBytes = BN * BK * 2;                    // 32768
+constexpr int kSsBytes = BN * BK / 8;                    // 2048
+
+template <bool PER_MATRIX, bool GATHER>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
+                     const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
+                     int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
+                     const int32_t *__restrict__ table, int32_t n_variants)
+{
+    // separate objects, so the compiler can tell a read of one buffer from
+    // a copy in flight into another and does not wait for every copy
+    __shared__ __attribute__((aligned(16))) uint8_t XS0[kXsBytes], XS1[kXsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t WS0[kWsBytes], WS1[kWsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t SS0[kSsBytes], SS1[kSsBytes];
+    __shared__ int32_t rows_s[BM];
+    uint8_t *const XSb[2] = {XS0, XS1};
+    uint8_t *const WSb[2] = {WS0, WS1};
+    uint8_t *const SSb[2] = {SS0, SS1};
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hi = lane >> 5;
+    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t mt = b % m_tiles, nt = b / m_tiles;
+    const int64_t n0 = nt * BN;
+
+    int64_t m0 = mt * BM;
+    const uint8_t *signs = signs_all;
+    const float *alpha = alpha_all;
+    if constexpr (GATHER) {
+        const int32_t total = table[0];
+        if (mt >= total)
+            return;
+        const int32_t *perm = table + 4;
+        const int32_t *tile_v = perm + M;
+        const int32_t *tile_row0 = tile_v + m_tiles;
+        const int32_t *tile_rows = tile_row0 + m_tiles;
+        const int v = tile_v[mt];
+        const int row0 = tile_row0[mt], nrows = tile_rows[mt];
+        for (int i = threadIdx.x; i < BM; i += kThreads)
+            rows_s[i] = i < nrows ? perm[row0 + i] : -1;
+        __syncthreads();
+        if (v >= n_variants) {
+            for (int i = 0; i < nrows; ++i) {
+                const int64_t tok = rows_s[i];
+                for (int64_t j = n0 + threadIdx.x; j < min(N, n0 + BN); j += kThreads)
+                    y[tok * N + j] = 0;
+            }
+            return;
+        }
+        signs = signs_all + (int64_t)v * N * (K >> 3);
+        alpha = PER_MATRIX ? alpha_all + v : alpha_all + (int64_t)v * N;
+        m0 = 0;
+    }
+
+    const int64_t G = K >> 3;
+    const int T = (int)(K / BK);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, N * K * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, N * G);
+
+    // DMA instruction j of a wave covers 8 rows (8j .. 8j+7 of its 64); lane
+    // l writes chunk position l&7 of row 8j + l/8, i.e. logical chunk
+    // (l&7) ^ ((row >> 1) & 7), which only depends on the parity of j.
+    const int p = lane & 7;
+    uint32_t xoff[GATHER ? 8 : 2], woff[2];
+#pragma unroll
+    for (int j = 0; j < (GATHER ? 8 : 2); ++j) {
+        const int row = wave * 64 + j * 8 + (lane >> 3);
+        const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
+        int64_t tok;
+        if constexpr (GATHER)
+            tok = rows_s[row];
+        else
+            tok = m0 + row;
+        xoff[j] = (tok < 0 || tok >= M) ? kInvalidOffset : (uint32_t)((tok * K + c * 8) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
+        const int64_t n = n0 + wave * 64 + j * 8 + (lane >> 3);
+        woff[j] = n < N ? (uint32_t)((n * K + c * 8) * 2) : kInvalidOffset;
+    }
+    // sign tile: instruction j covers rows 32j .. 32j+31, lane l -> row
+    // 32j + l/2, dword l&1 of the row's 8 bytes
+    uint32_t soff;
+    {
+        const int64_t n = n0 + wave * 64 + (lane >> 1);
+        soff = n < N ? (uint32_t)(n * G + (lane & 1) * 4) : kInvalidOffset;
+    }
+    const uint32_t xstride = (uint32_t)(8 * K * 2);   // 8 rows further (dense)
+    const uint32_t sstride = (uint32_t)(32 * G);      // 32 rows further
+
+    auto dma_x = [&](int t, int buf) {
+        const uint32_t kb = (uint32_t)(t * BK * 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t vo;
+            if constexpr (GATHER)
+                vo = xoff[j] + kb;
+            else
+                vo = xoff[j & 1] + (uint32_t)(j >> 1) * 2 * xstride + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 8 + j) * 1024), 16,
+                                                     vo, 0, 0, 0);
+        }
+    };
+    auto dma_w = [&](int t, int buf) {
+        const uint32_t kb = (uint32_t)(t * BK * 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t vo = woff[j & 1] + (uint32_t)(j >> 1) * 2 * (uint32_t)(8 * K * 2) + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(WSb[buf] + wave * 8192 + j * 1024), 16,
+                                                     vo, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(SSb[buf] + wave * 512 + j * 256), 4,
+                                                     soff + (uint32_t)j * sstride + (uint32_t)(t * 8), 0, 0, 0);
+    };
+
+    float a[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t n = n0 + wave * 64 + nb * 32 + (lane & 31);
+        a[nb] = PER_MATRIX ? alpha[0] : (n < N ? alpha[n] : 0.0f);
+    }
+    // this lane's B rows inside the wave's W tile, and their swizzle
+    const int brow = lane & 31;
+    const int bsw = (brow >> 1) & 7;  // same for brow and brow + 32
+    struct Raw {
+        uint4 w[2][4];
+        uint2 s[2];
+    };
+    auto read_w = [&](Raw &r, int buf) {
+        const uint8_t *wt = WSb[buf] + wave * 8192;
+        const uint8_t *st = SSb[buf] + wave * 512;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int row = nb * 32 + brow;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                r.w[nb][kb] = *reinterpret_cast<const uint4 *>(wt + row * 128 + (((kb * 2 + hi) ^ bsw) * 16));
+            r.s[nb] = *reinterpret_cast<const uint2 *>(st + row * 8);
+        }
+    };
+    auto build = [&](bf16x8 (&B)[2][4], const Raw &r, int nb, int kb) {
+        const int byte_i = kb * 2 + hi;
+        const uint32_t word = byte_i < 4 ? r.s[nb].x : r.s[nb].y;
+        const uint32_t byte = (word >> (8 * (byte_i & 3))) & 0xFFu;
+        B[nb][kb] = __builtin_bit_cast(bf16x8, weff_group(r.w[nb][kb], byte, a[nb]));
+    };
+
+    f32x16 acc[8][2];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[mb][nb][v] = 0.0f;
+
+    const int arow = lane & 31;
+    const int asw = (arow >> 1) & 7;
+    auto read_a = [&](bf16x8 (&A)[8], int buf, int kb) {
+        const uint8_t *base = XSb[buf] + arow * 128 + (((kb * 2 + hi) ^ asw) * 16);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+            A[mb] = *reinterpret_cast<const bf16x8 *>(base + mb * 32 * 128);
+    };
+
+    // ---- prologue
+    bf16x8 B[2][2][4];
+    {
+        dma_x(0, 0);
+        dma_w(0, 0);
+        dma_w(T > 1 ? 1 : 0, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        Raw r;
+        read_w(r, 0);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                build(B[0], r, nb, kb);
+    }
+
+    auto step = [&](int t, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        constexpr int nxt = 1 - cur;
+        const int t1 = t + 1 < T ? t + 1 : T - 1;
+        const int t2 = t + 2 < T ? t + 2 : T - 1;
+        dma_x(t1, nxt);   // 8 ops
+        dma_w(t2, cur);   // 10 ops; W tile buffer `cur` held W(t), already built into B[cur]
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<18>();  // this wave's W(t+1) tile has landed
+        Raw r;
+        read_w(r, nxt);
+        bf16x8 A[2][8];
+        read_a(A[0], cur, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb < 3)
+                read_a(A[(kb + 1) & 1], cur, kb + 1);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[cur][nb][kb], acc[mb][nb],
+                                                                          0, 0, 0);
+            }
+            build(B[nxt], r, 0, kb);
+            build(B[nxt], r, 1, kb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // x(t+1) has landed (W(t+2) may stay in flight) and this wave's LDS
+        // reads are done; then a bare barrier: __syncthreads()' fence would
+        // also wait for the W(t+2) copies, which nobody else reads.
+        wait_vmcnt_lgkm0<10>();
+        __builtin_amdgcn_s_barrier();
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < T)
+        step(t, std::integral_constant<int, 0>{});
+
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t j = n0 + wave * 64 + nb * 32 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                int64_t tok;
+                if constexpr (GATHER)
+                    tok = rows_s[i];
+                else
+                    tok = m0 + i < M ? m0 + i : -1;
+                const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
+                __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
+            }
+        }
+    }
+}
+
 // Bucket tokens by variant id in one workgroup: counts, exclusive scan, a
 // scatter into per-variant segments, and the tile table of the grouped GEMM.
 // Out-of-range ids form one extra bucket (index n_variants) whose tiles
@@ -400,11 +669,18 @@ hipError_t launch_tiles(const uint16_t *x, int64_t m, const uint16_t *w_base, co
                         const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                         int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s)
 {
-    if (d_in % 64 == 0)
-        return launch_tiles2<GATHER, true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
-                                           n_variants, s);
-    return launch_tiles2<GATHER, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
-                                        n_variants, s);
+    if (d_in % 64 != 0)
+        return launch_tiles2<GATHER, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
+                                            n_variants, s);
+    const int64_t n_tiles = (d_out + BN - 1) / BN;
+    const dim3 grid((unsigned)(m_tiles * n_tiles)), block(kThreads);
+    if (per_matrix)
+        hipLaunchKernelGGL((gemm_tiles_fast<true, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha,
+                           d_out, d_in, y, m_tiles, table, n_variants);
+    else
+        hipLaunchKernelGGL((gemm_tiles_fast<false, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha,
+                           d_out, d_in, y, m_tiles, table, n_variants);
+    return hipGetLastError();
 }
 
 }  // namespace
