@@ -60,6 +60,11 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    p.add_argument("--kernel-reps", type=int, default=125,
+                   help="graph replays per kernel for the per-kernel timings (lower it under a profiler)")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="after the run, copy a buffer of this many MiB once (torch copy_), so counter runs can "
+                        "calibrate FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
     return p.parse_args()
 
 
@@ -168,7 +173,7 @@ def time_graphs(torch, graphs, n, warm):
     return e0.elapsed_time(e1) / 1e3, wall  # seconds (device events), seconds (host wall)
 
 
-def run_decode(torch, bd, synth, steps, warmup):
+def run_decode(torch, bd, synth, steps, warmup, kernel_reps):
     ds = DecodeStep(torch, bd, synth)
     step_graphs = [capture(torch, lambda s, i=i: ds.step(i, s)) for i in range(SETS)]
     dev_s, wall_s = time_graphs(torch, step_graphs, steps, warmup)
@@ -176,7 +181,7 @@ def run_decode(torch, bd, synth, steps, warmup):
     kernels = {}
     for name, nbytes in ds.bytes.items():
         g = capture(torch, lambda s, name=name: [ds.launch(name, i, s) for i in range(SETS)])
-        reps = max(8, 2000 // SETS)
+        reps = max(1, kernel_reps)
         t, _ = time_graphs(torch, [g], reps, 4)
         us = t / (reps * SETS) * 1e6
         kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
@@ -364,7 +369,7 @@ def main():
     import tenant_fine_tune_amd as bd
 
     log(f"device: {torch.cuda.get_device_name(0)}")
-    ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup)
+    ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup, args.kernel_reps)
     ms_per_step = dev_s / args.steps * 1e3
     value = ds.step_bytes * args.steps / dev_s / 1e9
     log(f"decode step: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s (wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
@@ -408,6 +413,14 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read + {n} bytes written")
 
 
 if __name__ == "__main__":

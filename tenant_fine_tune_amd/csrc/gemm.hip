@@ -350,7 +350,7 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
     uint8_t *const SSb[2] = {SS0, SS1};
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
     const int hi = lane >> 5;
     const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t mt = b % m_tiles, nt = b / m_tiles;
@@ -421,33 +421,38 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
         soff = n < N ? (uint32_t)(n * G + (lane & 1) * 4) : kInvalidOffset;
     }
     const uint32_t xstride = (uint32_t)(8 * K * 2);   // 8 rows further (dense)
+    const uint32_t xstride_w = xstride;               // same for W rows
     const uint32_t sstride = (uint32_t)(32 * G);      // 32 rows further
 
+    // Per-step offsets (and the uniform part of the row offset) go in the
+    // scalar offset: with d_in a multiple of 64 a valid row never steps past
+    // its tensor, and an invalid row (offset >= 2^31) stays out of range.
     auto dma_x = [&](int t, int buf) {
         const uint32_t kb = (uint32_t)(t * BK * 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint32_t vo;
-            if constexpr (GATHER)
-                vo = xoff[j] + kb;
-            else
-                vo = xoff[j & 1] + (uint32_t)(j >> 1) * 2 * xstride + kb;
+            uint32_t vo, so;
+            if constexpr (GATHER) {
+                vo = xoff[j];
+                so = kb;
+            } else {
+                vo = xoff[j & 1];
+                so = (uint32_t)(j >> 1) * 2 * xstride + kb;
+            }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 8 + j) * 1024), 16,
-                                                     vo, 0, 0, 0);
+                                                     vo, so, 0, 0);
         }
     };
     auto dma_w = [&](int t, int buf) {
         const uint32_t kb = (uint32_t)(t * BK * 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t vo = woff[j & 1] + (uint32_t)(j >> 1) * 2 * (uint32_t)(8 * K * 2) + kb;
+        for (int j = 0; j < 8; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(WSb[buf] + wave * 8192 + j * 1024), 16,
-                                                     vo, 0, 0, 0);
-        }
+                                                     woff[j & 1], (uint32_t)(j >> 1) * 2 * xstride_w + kb, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(SSb[buf] + wave * 512 + j * 256), 4,
-                                                     soff + (uint32_t)j * sstride + (uint32_t)(t * 8), 0, 0, 0);
+                                                     soff, (uint32_t)j * sstride + (uint32_t)(t * 8), 0, 0);
     };
 
     float a[2];
@@ -522,14 +527,23 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
         constexpr int nxt = 1 - cur;
         const int t1 = t + 1 < T ? t + 1 : T - 1;
         const int t2 = t + 2 < T ? t + 2 : T - 1;
+        // Issue order matters: the explicit vmcnt waits below count the ops
+        // issued after a given copy, so the groups are kept in order.
         dma_x(t1, nxt);   // 8 ops
+        __builtin_amdgcn_sched_barrier(0);
         dma_w(t2, cur);   // 10 ops; W tile buffer `cur` held W(t), already built into B[cur]
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<18>();  // this wave's W(t+1) tile has landed
+        wait_vmcnt<18>();  // this wave's W(t+1) tile has landed (8 + 10 ops issued since)
         Raw r;
         read_w(r, nxt);
         bf16x8 A[2][8];
         read_a(A[0], cur, 0);
+        // 64 slots, each one MFMA of step t; every second slot also forms one
+        // packed W_eff pair of step t+1 (32 pairs: 2 feature blocks x 4 k
+        // blocks x 4 pairs).  sched_barrier between slots keeps this order,
+        // so the VALU work issues while the matrix core is busy.
+        uint32_t Bn[2][4][4];
+        uint32_t sbyte = 0;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (kb < 3)
@@ -537,13 +551,35 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int slot = kb * 16 + mb * 2 + nb;
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[cur][nb][kb], acc[mb][nb],
                                                                           0, 0, 0);
+                    if (slot & 1) {
+                        const int q = slot >> 1;  // pair 0..31
+                        const int bnb = q >> 4, bkb = (q >> 2) & 3, pr = q & 3;
+                        if (pr == 0) {
+                            const int byte_i = bkb * 2 + hi;
+                            const uint32_t word = byte_i < 4 ? r.s[bnb].x : r.s[bnb].y;
+                            sbyte = (word >> (8 * (byte_i & 3))) & 0xFFu;
+                        }
+                        const uint4 &w = r.w[bnb][bkb];
+                        const uint32_t wv = pr == 0 ? w.x : pr == 1 ? w.y : pr == 2 ? w.z : w.w;
+                        Bn[bnb][bkb][pr] = weff_pair(wv, sbyte, 2 * pr, a[bnb]);
+                        // pin the pair here: without this, IR code sinking moves
+                        // every build down to its use after the last MFMA
+                        asm volatile("" : "+v"(Bn[bnb][bkb][pr]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            build(B[nxt], r, 0, kb);
-            build(B[nxt], r, 1, kb);
         }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                B[nxt][nb][kb] = __builtin_bit_cast(bf16x8, make_uint4(Bn[nb][kb][0], Bn[nb][kb][1], Bn[nb][kb][2],
+                                                                       Bn[nb][kb][3]));
         __builtin_amdgcn_sched_barrier(0);
         // x(t+1) has landed (W(t+2) may stay in flight) and this wave's LDS
         // reads are done; then a bare barrier: __syncthreads()' fence would
