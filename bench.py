@@ -62,6 +62,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     p.add_argument("--kernel-reps", type=int, default=125,
                    help="graph replays per kernel for the per-kernel timings (lower it under a profiler)")
+    p.add_argument("--stack", action="store_true",
+                   help="instead of the decode-layer line, build the full 70B-shaped stack (80 layers x 7 linears, "
+                        "14 delta sets, 257 GB resident) and time a compress pass over one variant's full weight set, "
+                        "a 512-token prefill pass and a 1-token decode pass through every linear")
+    p.add_argument("--stack-layers", type=int, default=80)
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (torch copy_), so counter runs can "
                         "calibrate FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
@@ -206,13 +211,15 @@ def run_prefill(torch, bd, synth, reps=10):
             sets.append((w_base, signs, alpha))
         x = synth.device_activations(PREFILL_M, K, seed=1, index=len(out))
         y = torch.empty((PREFILL_M, N), dtype=torch.bfloat16, device=dev)
+        nws = bd.lib.bitdelta_linear_workspace(PREFILL_M, N, K)
+        ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
         P = ctypes.c_void_p
 
         def call(i, s):
             w, sg, a = sets[i % 2]
             bd.check(bd.lib.bitdelta_linear(P(x.data_ptr()), PREFILL_M, P(w.data_ptr()), P(sg.data_ptr()),
-                                            P(a.data_ptr()), bd.BD_ALPHA_ROW, N, K, P(y.data_ptr()), None, 0,
-                                            P(s.cuda_stream)))
+                                            P(a.data_ptr()), bd.BD_ALPHA_ROW, N, K, P(y.data_ptr()),
+                                            P(ws.data_ptr()), nws, P(s.cuda_stream)))
 
         stream = torch.cuda.current_stream()
         for i in range(3):
@@ -285,6 +292,84 @@ def run_grouped(torch, bd, synth, reps=10):
     log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s")
     return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
             "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+# ---------------------------------------------------------------- 70B stack
+
+
+def run_stack(torch, bd, synth, n_layers):
+    from tenant_fine_tune_amd.stack import LinearStack
+
+    dev = torch.device("cuda")
+    free0, total = torch.cuda.mem_get_info()
+    t0 = time.perf_counter()
+    st = LinearStack(n_layers=n_layers, n_variants=14)
+    st.reserve(512)
+    log(f"stack: {n_layers} layers x {len(st.shapes)} linears, 14 delta sets, "
+        f"{st.resident_bytes() / 1e9:.2f} GB resident (device had {free0 / 1e9:.1f} of {total / 1e9:.1f} GB free)")
+    names = [s[0] for s in st.shapes]
+    bv = synth.variant_scales(14, seed=4)
+    for l, name, d_out, d_in in st.matrices():
+        idx = 5000 + 10 * l + names.index(name)
+        st.base[l, name].copy_(synth.device_normal((d_out, d_in), 0.02, 4, synth.tag(synth.TAG_WBASE, idx), dev,
+                                                   torch.bfloat16))
+        g = torch.Generator(device=dev)
+        g.manual_seed(idx)
+        for v in range(1, 14):  # the other variants: random packed signs, alpha near b_v
+            st.signs[v, l, name].copy_(torch.randint(0, 256, st.signs[v, l, name].shape, generator=g, device=dev,
+                                                     dtype=torch.int32).to(torch.uint8))
+            st.alpha[v, l, name].copy_(torch.rand(st.alpha[v, l, name].shape, generator=g, device=dev)
+                                       .mul_(float(bv[v])).add_(float(bv[v]) * 0.5))
+        if name == names[-1] and l % 10 == 9:
+            torch.cuda.synchronize()
+            log(f"stack: layer {l + 1}/{n_layers} filled ({time.perf_counter() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    log(f"stack: filled in {time.perf_counter() - t0:.1f} s")
+
+    # compress pass over variant 0's full weight set, W_ft streamed one matrix at a time
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def make_w_ft(l, name, base):
+        idx = 5000 + 10 * l + names.index(name)
+        w_ft = base.float().add_(synth.device_laplace(base.shape, float(bv[0]), 4, synth.tag(synth.TAG_DELTA, idx), dev))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ev.append([e0, None])
+        return w_ft
+
+    def after(l, name):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        ev[-1][1] = e1
+
+    st.compress_variant(0, make_w_ft, on_matrix=after)
+    torch.cuda.synchronize()
+    comp_ms = sum(a.elapsed_time(b) for a, b in ev)
+    comp_bytes = sum(d_out * d_in * (2 + 4) + d_out * d_in // 8 + 4 * d_out for _, _, d_out, d_in in st.matrices())
+    log(f"stack compress (variant 0, fp32 W_ft): {comp_ms:.1f} ms, {comp_bytes / comp_ms / 1e6:.1f} GB/s")
+
+    out = {"resident_GB": round(st.resident_bytes() / 1e9, 2), "layers": n_layers, "variants": 14,
+           "params": st.params(),
+           "compress": {"ms": round(comp_ms, 2), "bytes": comp_bytes, "GB/s": round(comp_bytes / comp_ms / 1e6, 1),
+                        "frac_hbm": round(comp_bytes / comp_ms / 1e6 / HBM_PEAK_GBS, 4)}}
+    widths = {name: d_in for name, _, d_in in st.shapes}
+    outs = {name: d_out for name, d_out, _ in st.shapes}
+    for label, m, reps in (("prefill", 512, 3), ("decode", 1, 10)):
+        xs = {name: synth.device_activations(m, widths[name], seed=4, index=m + i) for i, name in enumerate(widths)}
+        ys = {name: torch.empty((m, outs[name]), dtype=torch.bfloat16, device=dev) for name in outs}
+        g = capture(torch, lambda s: st.forward(0, xs, ys, s))
+        dev_s, _ = time_graphs(torch, [g], reps, 1)
+        ms = dev_s / reps * 1e3
+        flop, nbytes = st.flops(m), st.linear_bytes(m)
+        out[label] = {"m": m, "ms": round(ms, 3), "TFLOP/s": round(flop / ms / 1e9, 1),
+                      "frac_mfma": round(flop / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                      "GB/s": round(nbytes / ms / 1e6, 1), "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                      "bytes": nbytes, "linears": n_layers * len(st.shapes)}
+        log(f"stack {label} m={m} through {n_layers * len(st.shapes)} linears: {ms:.2f} ms, "
+            f"{flop / ms / 1e9:.1f} TFLOP/s, {nbytes / ms / 1e6:.1f} GB/s")
+        del g, xs, ys
+    return out
 
 
 # ----------------------------------------------------------------- cpu oracle
@@ -369,6 +454,17 @@ def main():
     import tenant_fine_tune_amd as bd
 
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.stack:
+        res = run_stack(torch, bd, synth, args.stack_layers)
+        line = {"metric": METRIC, "value": res["decode"]["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": 10,
+                "warmup": 1, "ms_per_step": res["decode"]["ms"], "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "config": {"workload": f"70B-shaped linear stack, {args.stack_layers} layers x 7 linears, 14 packed "
+                                       f"delta sets resident; value = 1-token decode pass through every linear",
+                           "parallelism": "single GPU"},
+                "stack": res}
+        print(json.dumps(line), flush=True)
+        return
     ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup, args.kernel_reps)
     ms_per_step = dev_s / args.steps * 1e3
     value = ds.step_bytes * args.steps / dev_s / 1e9

@@ -164,10 +164,9 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
 
 size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in)
 {
-    (void)m;
-    (void)d_out;
-    (void)d_in;
-    return 0;
+    if (m <= bd::kGemvMaxM || d_out <= 0 || d_in <= 0 || d_in % 8 != 0)
+        return 0;
+    return bd::gemm_workspace_bytes(m, d_out, d_in);
 }
 
 bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, const uint8_t *signs,
@@ -207,7 +206,10 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, co
                     (long long)m, (long long)d_out, (long long)d_in);
     if (tiles > kMaxGrid)
         return fail(BD_ESHAPE, "linear m=%lld d_out=%lld exceeds the prefill grid", (long long)m, (long long)d_out);
-    return device(bd::launch_gemm(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
+    if (need >= ((size_t)1 << 31))
+        return fail(BD_ESHAPE, "linear m=%lld d_out=%lld d_in=%lld needs a split-K workspace above 2 GiB",
+                    (long long)m, (long long)d_out, (long long)d_in);
+    return device(bd::launch_gemm(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, workspace, s),
                   "bitdelta_linear (prefill)");
 }
 

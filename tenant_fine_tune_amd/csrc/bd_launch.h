@@ -26,9 +26,14 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
 // gemm.hip: dense prefill GEMM and the grouped variant
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 256;
+// `workspace` must hold gemm_workspace_bytes(m, d_out, d_in) bytes (split-K
+// partials; 0 when the shape runs unsplit).
+int gemm_splits(int64_t m, int64_t d_out, int64_t d_in);
+int64_t gemm_k_split(int64_t d_in, int splits);
+size_t gemm_workspace_bytes(int64_t m, int64_t d_out, int64_t d_in);
 hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
-                       uint16_t *y, hipStream_t s);
+                       uint16_t *y, void *workspace, hipStream_t s);
 
 // Grouped: bucketing writes this table into the workspace, then the grouped
 // GEMM walks it.  Layout (int32 words): [0] total tiles, [1..3] pad,

@@ -9,6 +9,8 @@
 // serves in one launch.
 //
 // Tile: 256 tokens x 256 output features per workgroup, K stepped by 64.
+// Two kernels share the tiling: gemm_tiles_fast (d_in a multiple of 64) and
+// gemm_tiles (any d_in that is a multiple of 8, with a masked K tail).
 // Four waves; wave w owns output features [64w, 64w+64) of the tile for all
 // 256 tokens (8 x 2 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
 // accumulators per lane).  Pipeline, per K step t:
@@ -17,11 +19,13 @@
 //    buffers; rows are stored unpadded with the 16-byte chunks of row r
 //    permuted by c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 32
 //    consecutive rows spread over all banks;
-//  - weights: each wave loads its own 64 x 64 slice of W_base straight in the
-//    MFMA B-operand layout (lane l: feature l%32, 8 consecutive k) with the
-//    sign bytes, two steps ahead; while the MFMAs of step t run, the VALU
-//    forms step t+1's W_eff = bf16(W_base + +-alpha) fragments in VGPRs, so
-//    each weight is rebuilt exactly once per workgroup and never touches LDS;
+//  - weights: each wave loads its own 64 x 64 slice of W_base and the sign
+//    bytes two steps ahead (general kernel: into VGPRs, in the MFMA B-operand
+//    layout, lane l: feature l%32, 8 consecutive k; fast kernel: into LDS by
+//    direct-to-LDS loads, read back in that layout); while the MFMAs of step t
+//    run, the VALU forms step t+1's W_eff = bf16(W_base + +-alpha) fragments
+//    in VGPRs, so each weight is rebuilt exactly once per workgroup and W_eff
+//    itself is never written anywhere;
 //  - one barrier per step.  Every load address is clamped into its tensor
 //    (tail rows/columns read valid data whose results are discarded or
 //    multiplied by zero), so no load sits under a branch.
@@ -332,12 +336,13 @@ constexpr int kXsBytes = BM * BK * 2;                    // 32768
 constexpr int kWsBytes = BN * BK * 2;                    // 32768
 constexpr int kSsBytes = BN * BK / 8;                    // 2048
 
-template <bool PER_MATRIX, bool GATHER>
+template <bool PER_MATRIX, bool GATHER, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
                      const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
                      int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
-                     const int32_t *__restrict__ table, int32_t n_variants)
+                     const int32_t *__restrict__ table, int32_t n_variants,
+                     int64_t k_split, float *__restrict__ partial)
 {
     // separate objects, so the compiler can tell a read of one buffer from
     // a copy in flight into another and does not wait for every copy
@@ -386,7 +391,11 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
     }
 
     const int64_t G = K >> 3;
-    const int T = (int)(K / BK);
+    // split-K: blockIdx.y takes columns [k_begin, k_begin + k_split) of K
+    const int64_t k_begin = (int64_t)blockIdx.y * k_split;
+    const int T = (int)((min(K, k_begin + k_split) - k_begin) / BK);
+    const uint32_t kx0 = (uint32_t)(k_begin * 2);   // byte offset of k_begin in a bf16 row
+    const uint32_t ks0 = (uint32_t)(k_begin / 8);   // byte offset of k_begin in a sign row
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, N * K * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, N * G);
@@ -428,7 +437,7 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
     // scalar offset: with d_in a multiple of 64 a valid row never steps past
     // its tensor, and an invalid row (offset >= 2^31) stays out of range.
     auto dma_x = [&](int t, int buf) {
-        const uint32_t kb = (uint32_t)(t * BK * 2);
+        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint32_t vo, so;
@@ -444,7 +453,7 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
         }
     };
     auto dma_w = [&](int t, int buf) {
-        const uint32_t kb = (uint32_t)(t * BK * 2);
+        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(WSb[buf] + wave * 8192 + j * 1024), 16,
@@ -452,7 +461,7 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(SSb[buf] + wave * 512 + j * 256), 4,
-                                                     soff, (uint32_t)j * sstride + (uint32_t)(t * 8), 0, 0);
+                                                     soff, (uint32_t)j * sstride + ks0 + (uint32_t)(t * 8), 0, 0);
     };
 
     float a[2];
@@ -595,25 +604,78 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
     if (t < T)
         step(t, std::integral_constant<int, 0>{});
 
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
+    if constexpr (SPLIT) {
+        // split-K: fp32 partial sums in accumulator order, 1 KB per (wave, mb,
+        // nb, quarter) chunk, reduced in split order by splitk_reduce
+        const int64_t tile = nt * m_tiles + mt;
+        const int64_t tiles = (int64_t)gridDim.x;
+        float *base = partial + (((int64_t)blockIdx.y * tiles + tile) * 4 + wave) * (8 * 2 * 4 * 256);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t j = n0 + wave * 64 + nb * 32 + (lane & 31);
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-                int64_t tok;
-                if constexpr (GATHER)
-                    tok = rows_s[i];
-                else
-                    tok = m0 + i < M ? m0 + i : -1;
-                const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
-                __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(base + ((mb * 2 + nb) * 4 + q) * 256 + lane * 4) =
+                        make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                    acc[mb][nb][4 * q + 3]);
+    } else {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int64_t j = n0 + wave * 64 + nb * 32 + (lane & 31);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int i = mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                    int64_t tok;
+                    if constexpr (GATHER)
+                        tok = rows_s[i];
+                    else
+                        tok = m0 + i < M ? m0 + i : -1;
+                    const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
+                    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
+                }
             }
         }
     }
+}
+
+// Sum the split-K partials of gemm_tiles_fast in split order (fixed, so the
+// result is deterministic) and write bf16 y.  One thread per 4 accumulators.
+__global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ partial, int splits, int64_t tiles,
+                                                     int64_t m_tiles, int64_t M, int64_t N,
+                                                     uint16_t *__restrict__ y)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * 4 waves * 64 chunks * 64 lanes
+    const int lane = (int)(gid & 63);
+    const int64_t chunk = gid >> 6;
+    const int q = (int)(chunk & 3), nb = (int)((chunk >> 2) & 1), mb = (int)((chunk >> 3) & 7);
+    const int wave = (int)((chunk >> 6) & 3);
+    const int64_t tile = chunk >> 8;
+    if (tile >= tiles)
+        return;
+    const int64_t stride = tiles * 4 * (8 * 2 * 4 * 256);  // floats per split
+    const float *src = partial + chunk * 256 + lane * 4;
+    float4 s = *reinterpret_cast<const float4 *>(src);
+    for (int sp = 1; sp < splits; ++sp) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + sp * stride);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    const int64_t mt = tile % m_tiles, nt = tile / m_tiles;
+    const int64_t j = nt * BN + wave * 64 + nb * 32 + (lane & 31);
+    const int64_t i0 = mt * BM + mb * 32 + 8 * q + 4 * (lane >> 5);
+    if (j >= N)
+        return;
+    const float v4[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (i0 + r < M)
+            y[(i0 + r) * N + j] = to_bf16(v4[r]);
 }
 
 // Bucket tokens by variant id in one workgroup: counts, exclusive scan, a
@@ -703,30 +765,82 @@ hipError_t launch_tiles2(const uint16_t *x, int64_t m, const uint16_t *w_base, c
 template <bool GATHER>
 hipError_t launch_tiles(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                         const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
-                        int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s)
+                        int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s,
+                        float *partial = nullptr, int splits = 1)
 {
     if (d_in % 64 != 0)
         return launch_tiles2<GATHER, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
                                             n_variants, s);
     const int64_t n_tiles = (d_out + BN - 1) / BN;
-    const dim3 grid((unsigned)(m_tiles * n_tiles)), block(kThreads);
-    if (per_matrix)
-        hipLaunchKernelGGL((gemm_tiles_fast<true, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha,
-                           d_out, d_in, y, m_tiles, table, n_variants);
-    else
-        hipLaunchKernelGGL((gemm_tiles_fast<false, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha,
-                           d_out, d_in, y, m_tiles, table, n_variants);
+    const int64_t k_split = splits > 1 ? gemm_k_split(d_in, splits) : d_in;
+    const int used = (int)((d_in + k_split - 1) / k_split);
+    float *part = used > 1 ? partial : nullptr;
+    const dim3 grid((unsigned)(m_tiles * n_tiles), (unsigned)used), block(kThreads);
+#define BD_FAST(PM, SP)                                                                                    \
+    hipLaunchKernelGGL((gemm_tiles_fast<PM, GATHER, SP>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, \
+                       d_in, y, m_tiles, table, n_variants, k_split, part)
+    if (per_matrix) {
+        if (part)
+            BD_FAST(true, true);
+        else
+            BD_FAST(true, false);
+    } else {
+        if (part)
+            BD_FAST(false, true);
+        else
+            BD_FAST(false, false);
+    }
+#undef BD_FAST
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || part == nullptr)
+        return e;
+    const int64_t tiles = m_tiles * n_tiles;
+    const int64_t threads = tiles * 4 * 64 * 64;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used, tiles,
+                       m_tiles, m, d_out, y);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Split-K: with few output tiles (small d_out or few tokens) the K loop is
+// cut into equal 64-aligned ranges so the grid covers the 256 CUs; each range
+// keeps at least 512 columns (8 steps) to amortise the pipeline fill.
+int gemm_splits(int64_t m, int64_t d_out, int64_t d_in)
+{
+    if (d_in % 64 != 0)
+        return 1;
+    const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
+    if (tiles >= 192)
+        return 1;
+    int sp = 1;
+    while (sp < 16 && tiles * sp < 256 && d_in / (2 * sp) >= 512)
+        sp *= 2;
+    const int64_t ks = gemm_k_split(d_in, sp);
+    return (int)((d_in + ks - 1) / ks);
+}
+
+int64_t gemm_k_split(int64_t d_in, int splits)
+{
+    return ((d_in + splits - 1) / splits + BK - 1) / BK * BK;
+}
+
+size_t gemm_workspace_bytes(int64_t m, int64_t d_out, int64_t d_in)
+{
+    const int sp = gemm_splits(m, d_out, d_in);
+    if (sp <= 1)
+        return 0;
+    const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
+    return (size_t)sp * (size_t)tiles * BM * BN * sizeof(float);
+}
+
 hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
-                       uint16_t *y, hipStream_t s)
+                       uint16_t *y, void *workspace, hipStream_t s)
 {
     const int64_t m_tiles = (m + BM - 1) / BM;
-    return launch_tiles<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, s);
+    return launch_tiles<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, s,
+                               static_cast<float *>(workspace), gemm_splits(m, d_out, d_in));
 }
 
 int64_t grouped_max_tiles(int64_t m, int32_t n_variants)

@@ -100,6 +100,27 @@ def test_linear_validation(bd):
     assert bd.lib.bitdelta_linear_workspace(4096, 4096, 4096) == 0
 
 
+def test_linear_split_k_workspace(bd):
+    """Prefill with few 256 x 256 output tiles splits K; the workspace holds
+    one fp32 256 x 256 partial per tile and split."""
+    W = bd.lib.bitdelta_linear_workspace
+    tile = 256 * 256 * 4
+    assert W(16, 64, 4096) == 0                    # decode path
+    assert W(2048, 8192, 8192) == 0                # 256 tiles fill the chip
+    assert W(2048, 28672, 8192) == 0
+    assert W(600, 64, 4096) == 8 * 3 * tile        # 3 tiles, K/8 = 512 per split
+    assert W(2048, 1024, 8192) == 8 * 32 * tile    # 32 tiles x 8 splits = 256
+    assert W(40, 1024, 8192) == 16 * 4 * tile      # capped at 16 splits
+    assert W(512, 8192, 28672) == 4 * 64 * tile
+    assert W(600, 64, 1032) == 0                   # d_in not a multiple of 64: general kernel
+    assert W(600, 64, 960) == 0                    # K too short to split
+    f = bd.lib.bitdelta_linear
+    need = W(600, 64, 4096)
+    assert f(FAKE, 600, FAKE, FAKE, FAKE, 0, 64, 4096, FAKE, FAKE, need - 1, None) == bd.BD_EWORKSPACE
+    assert f(FAKE, 600, FAKE, FAKE, FAKE, 0, 64, 4096, FAKE, None, need, None) == bd.BD_EINVAL
+    assert f(FAKE, 600, FAKE, FAKE, FAKE, 0, 64, 4096, FAKE, FAKE_ODD, need, None) == bd.BD_EALIGN
+
+
 def test_grouped_validation(bd):
     g = bd.lib.bitdelta_linear_grouped
     W = bd.lib.bitdelta_linear_grouped_workspace

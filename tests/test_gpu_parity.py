@@ -128,7 +128,9 @@ def test_linear_decode(bd, case, per_matrix):
 
 
 PREFILL_CASES = [((256, 512), 17), ((256, 512), 64), ((256, 512), 256), ((256, 512), 300),
-                 ((300, 200), 257), ((1000, 1032), 513), ((520, 64), 40), ((64, 4096), 600)]
+                 ((300, 200), 257), ((1000, 1032), 513), ((520, 64), 40), ((64, 4096), 600),
+                 # split-K: few output tiles, K cut into 2..16 ranges
+                 ((200, 4096), 64), ((520, 1024), 300), ((1024, 8192), 40), ((300, 2112), 17 + 256)]
 
 
 @pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
@@ -187,6 +189,35 @@ def test_dyadic_exact(bd, M):
     y = host_bits(bd.linear(bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])))
     y64, _ = oracle.linear(x, w_base, sb[0], alpha[0])
     assert np.array_equal(synth.bf16_bits_to_f32(y).astype(np.float64), y64)
+
+
+@pytest.mark.parametrize("case", [((200, 4096), 64), ((1024, 8192), 40), ((256, 2048), 300)],
+                         ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
+def test_split_k_dyadic_exact(bd, case):
+    """Split-K shapes on exact-arithmetic inputs: y bit for bit, and the
+    fixed-order reduce gives the same bits on every call."""
+    (R, C), M = case
+    assert bd.lib.bitdelta_linear_workspace(M, R, C) > 0
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=50 + M)
+    xd, wd, sd, ad = bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])
+    y = bd.linear(xd, wd, sd, ad)
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0])
+    assert np.array_equal(synth.bf16_bits_to_f32(host_bits(y)).astype(np.float64), y64)
+    x2 = bf16_dev(synth.activations(M, C, seed=50, index=M))
+    assert torch.equal(bd.linear(x2, wd, sd, ad), bd.linear(x2, wd, sd, ad))
+
+
+@pytest.mark.parametrize("shape", [(256, 2048), (520, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_identity_prefill_split_k(bd, shape):
+    """x = I on split-K shapes: each y element comes from one split, the
+    others add zeros, so y = W_eff^T bit for bit."""
+    R, C = shape
+    assert bd.lib.bitdelta_linear_workspace(C, R, C) > 0
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=12)
+    weff = oracle.reconstruct(w_base, so, ao)
+    eye = torch.eye(C, dtype=torch.bfloat16, device="cuda")
+    y = host_bits(bd.linear(eye, wd, sd, ad))
+    assert same_bits_pm0(y, weff.T)
 
 
 def test_zero_tokens_and_misaligned(bd):
@@ -331,3 +362,66 @@ def test_grouped_zipf_14_variants(bd):
     y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), wd, signs, alpha))
     y64, sc = oracle.linear_grouped(x, ids, w_base, so_rows, ao_all, rows=rows)
     check_linear(y[:, rows], y64, sc, "grouped zipf")
+
+
+# ----------------------------------------------------------- 70B-shaped stack
+
+
+def test_stack_two_layers(bd):
+    """The stack driver with two layers of every 70B shape and 14 delta sets:
+    variant 0 compressed from streamed fine-tuned weights (bit-exact on
+    sampled rows), the others random packed signs; prefill (m = 512) and decode
+    (m = 1) passes checked on sampled output features of every matrix."""
+    from tenant_fine_tune_amd.stack import LinearStack
+
+    st = LinearStack(n_layers=2, n_variants=14)
+    st.reserve(512)
+    dev = st.device
+    bv = synth.variant_scales(14, seed=3)
+    rows_of = {}
+    orc_rows = {}  # (l, name) -> (w_base rows, so rows, ao rows) from the oracle's own compress
+    for l, name, d_out, d_in in st.matrices():
+        idx = 1000 + 10 * l + [s[0] for s in st.shapes].index(name)
+        wb = synth.device_normal((d_out, d_in), 0.02, 3, synth.tag(synth.TAG_WBASE, idx), dev, torch.bfloat16)
+        st.base[l, name].copy_(wb)
+        w_ft = wb.float().add_(synth.device_laplace((d_out, d_in), float(bv[0]), 3, synth.tag(synth.TAG_DELTA, idx), dev))
+        st.compress_into(0, l, name, w_ft)
+        rows = np.unique(np.concatenate([[0, 255, d_out - 1], synth.u64(5, 3, 9300 + idx) % np.uint64(d_out)]))
+        rows_of[l, name] = rows.astype(np.int64)
+        r_t = torch.from_numpy(rows.astype(np.int64)).to(dev)
+        wb_rows = host_bits(wb.index_select(0, r_t))
+        ft_rows = host(w_ft.index_select(0, r_t))
+        so, ao = oracle.compress(wb_rows, ft_rows)
+        assert np.array_equal(host(st.signs[0, l, name].index_select(0, r_t)), so)
+        assert np.array_equal(_bits32(host(st.alpha[0, l, name].index_select(0, r_t))), _bits32(ao))
+        orc_rows[l, name] = (wb_rows, so, ao)
+        for v in range(1, 14):
+            g = torch.Generator(device=dev)
+            g.manual_seed(77 + 1000 * v + idx)
+            st.signs[v, l, name].copy_(torch.randint(0, 256, st.signs[v, l, name].shape, generator=g, device=dev,
+                                                     dtype=torch.int32).to(torch.uint8))
+            st.alpha[v, l, name].copy_(torch.rand(st.alpha[v, l, name].shape, generator=g, device=dev) * 2e-3)
+        del w_ft, wb
+    widths = {name: d_in for name, _, d_in in st.shapes}
+    outs = {name: d_out for name, d_out, _ in st.shapes}
+    for m in (512, 1):
+        xs_h = {name: synth.activations(m, widths[name], seed=3, index=m + i) for i, name in enumerate(widths)}
+        xs = {name: bf16_dev(a) for name, a in xs_h.items()}
+        ys = {name: torch.empty((m, outs[name]), dtype=torch.bfloat16, device=dev) for name in outs}
+        st.forward(0, xs, ys)  # ys now hold layer 1
+        for name in outs:
+            wb_rows, so, ao = orc_rows[1, name]
+            y64, sc = oracle.linear(xs_h[name], wb_rows, so, ao)
+            check_linear(host_bits(ys[name])[:, rows_of[1, name]], y64, sc, f"stack layer 1 {name} m={m}")
+        for name in outs:  # layer 0, and a random variant on layer 0
+            st.linear(0, 0, name, xs[name], ys[name])
+            wb_rows, so, ao = orc_rows[0, name]
+            y64, sc = oracle.linear(xs_h[name], wb_rows, so, ao)
+            check_linear(host_bits(ys[name])[:, rows_of[0, name]], y64, sc, f"stack layer 0 {name} m={m}")
+            r_t = torch.from_numpy(rows_of[0, name]).to(dev)
+            st.linear(9, 0, name, xs[name], ys[name])
+            s9 = host(st.signs[9, 0, name].index_select(0, r_t))
+            a9 = host(st.alpha[9, 0, name].index_select(0, r_t))
+            y64, sc = oracle.linear(xs_h[name], wb_rows, s9, a9)
+            check_linear(host_bits(ys[name])[:, rows_of[0, name]], y64, sc, f"stack variant 9 {name} m={m}")
+    assert st.resident_bytes() == st.params() * 2 + 14 * (st.params() // 8 + 4 * 2 * sum(o for _, o, _ in st.shapes))
