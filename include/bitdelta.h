@@ -114,7 +114,13 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
  * decode kernel; larger m the bf16-MFMA prefill kernel, which needs x, W_base
  * and y each below 2 GiB (BD_ESHAPE otherwise).
  * workspace: at least bitdelta_linear_workspace(m, d_out, d_in) bytes,
- * 16-byte aligned (may be NULL when that is 0). */
+ * 16-byte aligned (may be NULL when that is 0).  It is non-zero only for
+ * prefill shapes with few 256 x 256 output tiles, whose K loop is split:
+ * fp32 partial sums (256 KB per tile and split) are kept there and summed in
+ * split order, so the result does not depend on timing.  The caller owns it;
+ * its contents are scratch on entry and undefined after the call, and two
+ * calls in flight at once must not share one.  Too small: BD_EWORKSPACE; a
+ * requirement of 2 GiB or more: BD_ESHAPE. */
 size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in);
 bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
                           const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
