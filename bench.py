@@ -50,6 +50,20 @@ SETS = 16
 PREFILL_SHAPES = [("q/o", 8192, 8192), ("k/v", 1024, 8192), ("gate/up", 28672, 8192), ("down", 8192, 28672)]
 PREFILL_M = 2048
 
+# GPU kernels behind each entry of the decode step: source file under csrc/
+# and the kernel names (regular expressions on rocprofv3's demangled names)
+STEP_KERNELS = {
+    "compress_row": ("compress.hip", [r"compress_rows<true, false>"]),
+    "compress_matrix": ("compress.hip", [r"compress_rows<true, true>", r"alpha_matrix_finish"]),
+    "reconstruct": ("reconstruct.hip", [r"reconstruct_rows<false>"]),
+    "linear_m1_row": ("gemv.hip", [r"gemv_direct<1, 2, \d+, false>"]),
+    "linear_m1_matrix": ("gemv.hip", [r"gemv_direct<1, 2, \d+, true>"]),
+    "linear_m4_row": ("gemv.hip", [r"gemv_direct<4, 2, \d+, false>"]),
+    "linear_m4_matrix": ("gemv.hip", [r"gemv_direct<4, 2, \d+, true>"]),
+    "linear_m16_row": ("gemv.hip", [r"gemv_lds<16, 4, \d+, false>"]),
+    "linear_m16_matrix": ("gemv.hip", [r"gemv_lds<16, 4, \d+, true>"]),
+}
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -70,6 +84,14 @@ def parse():
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (torch copy_), so counter runs can "
                         "calibrate FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn the counter_collection CSVs of a FETCH_SIZE run and a WRITE_SIZE run (each "
+                        "made with --copy-probe-mb) into HBM bytes per launch of each decode-step kernel; writes "
+                        "profiles/traffic.json and prints a table")
+    p.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                   help="no GPU: per (kernel, grid) dispatch count and durations from a kernel_trace CSV")
+    p.add_argument("--copy-mb", type=int, default=256, help="--copy-probe-mb of the counter runs")
+    p.add_argument("--command", default="", help="command line recorded in profiles/traffic.json")
     return p.parse_args()
 
 
@@ -99,16 +121,22 @@ class DecodeStep:
         self.x = {m: synth.device_activations(m, C, seed=0, index=m) for m in DECODE_M}
         self.y = {m: [torch.empty((m, R), dtype=torch.bfloat16, device=dev) for _ in range(2)] for m in DECODE_M}
         torch.cuda.synchronize()
-        # kernels of the step: name -> (algorithmic bytes per launch, launches per step)
+        self.bytes = self.algorithmic_bytes()
+
+    @staticmethod
+    def algorithmic_bytes():
+        """Entries of the step in order -> algorithmic bytes per launch (inputs
+        read once + outputs written once)."""
         w = R * C
-        self.bytes = {
+        b = {
             "compress_row": w * 2 + w * 4 + w // 8 + 4 * R,
             "compress_matrix": w * 2 + w * 4 + w // 8 + 4,
             "reconstruct": w * 2 + w // 8 + 4 * R + w * 2,
         }
         for m in DECODE_M:
-            self.bytes[f"linear_m{m}_row"] = w * 2 + w // 8 + 4 * R + 2 * m * C + 2 * m * R
-            self.bytes[f"linear_m{m}_matrix"] = w * 2 + w // 8 + 4 + 2 * m * C + 2 * m * R
+            b[f"linear_m{m}_row"] = w * 2 + w // 8 + 4 * R + 2 * m * C + 2 * m * R
+            b[f"linear_m{m}_matrix"] = w * 2 + w // 8 + 4 + 2 * m * C + 2 * m * R
+        return b
 
     def launch(self, name, i, stream):
         """Enqueue one kernel of the step for weight set i on `stream` (raw C ABI)."""
@@ -414,9 +442,10 @@ def run_cpu_baseline(target_s):
 # ----------------------------------------------------------------------- main
 
 
-def traffic_for(kernel_name):
-    """HBM bytes per launch from the committed counter runs, if they were taken
-    on the current kernel sources (profiles/traffic.json); else None."""
+def traffic_for(entry):
+    """HBM bytes per launch of a decode-step entry from the committed counter
+    runs (profiles/traffic.json), if they were taken on the current source of
+    its kernels; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -424,22 +453,115 @@ def traffic_for(kernel_name):
         rec = json.load(open(path))
     except ValueError:
         return None
-    entry = rec.get("kernels", {}).get(kernel_name)
-    if not entry or entry.get("source_sha") != source_sha():
+    e = rec.get("kernels", {}).get(entry)
+    if not e or e.get("source_sha") != source_sha(STEP_KERNELS[entry][0]):
         return None
-    return entry.get("bytes_per_launch")
+    return e.get("bytes_per_launch")
 
 
-def source_sha():
+def source_sha(src):
+    """Hash of a kernel source file and the device headers it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tenant_fine_tune_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in (src, "bd_device.h", "bd_launch.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
+def _short(name):
+    import re
+
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mb, command):
+    """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each decode-step
+    kernel by what the same counters read for a copy of copy_mb MiB, and
+    record HBM bytes per launch next to the algorithmic bytes."""
+    import csv
+    import re
+    import statistics
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        return [(_short(r["Kernel_Name"]), int(r["Grid_Size"]), float(r["Counter_Value"]) * 1024.0) for r in rows]
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mb << 20
+    cf = max(v for n, _, v in fetch if "copyBuffer" in n)
+    cw = max(v for n, _, v in write if "copyBuffer" in n)
+    f_fetch, f_write = copy_bytes / cf, copy_bytes / cw
+    algo = DecodeStep.algorithmic_bytes()
+    out = {"command": command, "calibration": {"copy_bytes": copy_bytes, "fetch_factor": round(f_fetch, 4),
+                                               "write_factor": round(f_write, 4)}, "kernels": {}}
+    lines = [f"calibration: a {copy_mb} MiB copy reads FETCH_SIZE x {f_fetch:.4f} and WRITE_SIZE x {f_write:.4f}",
+             f"{'entry':18s} {'kernel':46s} {'n':>4s} {'fetch B':>12s} {'write B':>12s} {'HBM B':>12s} "
+             f"{'algorithmic B':>13s} {'ratio':>6s}"]
+    for entry, (src, pats) in STEP_KERNELS.items():
+        tf = tw = 0.0
+        names, n = [], 0
+        for pat in pats:
+            rx = re.compile(pat)
+            fv = [v for nm, _, v in fetch if rx.search(nm)]
+            wv = [v for nm, _, v in write if rx.search(nm)]
+            if not fv or not wv:
+                raise SystemExit(f"no dispatches of {pat} in the counter CSVs")
+            tf += statistics.median(fv) * f_fetch
+            tw += statistics.median(wv) * f_write
+            names.append(next(nm for nm, _, _ in fetch if rx.search(nm)))
+            n = len(fv)
+        total = tf + tw
+        out["kernels"][entry] = {"kernels": names, "source": src, "source_sha": source_sha(src),
+                                 "fetch_bytes": round(tf), "write_bytes": round(tw), "bytes_per_launch": round(total),
+                                 "algorithmic_bytes": algo[entry], "ratio": round(total / algo[entry], 4)}
+        lines.append(f"{entry:18s} {' + '.join(names)[:46]:46s} {n:4d} {tf:12.0f} {tw:12.0f} {total:12.0f} "
+                     f"{algo[entry]:13d} {total / algo[entry]:6.3f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_csv, gap=12):
+    """Durations (us) of the library kernels from a kernel_trace CSV, per run
+    of one (kernel, grid): a run ends when more than `gap` other dispatches
+    pass before the next one (so two shapes with one grid stay apart)."""
+    import csv
+    import statistics
+
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    runs, open_run = [], {}  # runs: [key, first dispatch, durations]; open_run: key -> (last dispatch, run)
+    for r in rows:
+        if "bd::" not in r["Kernel_Name"]:
+            continue
+        k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1),
+             int(r["Workgroup_Size_X"]))
+        i = int(r["Dispatch_Id"])
+        if k in open_run and i - open_run[k][0] <= gap:
+            j = open_run[k][1]
+        else:
+            runs.append([k, i, []])
+            j = len(runs) - 1
+        runs[j][2].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        open_run[k] = (i, j)
+    print(f"{'kernel':52s} {'threads':>9s} {'wg':>5s} {'first':>7s} {'n':>6s} {'avg us':>9s} {'median':>9s} {'min':>9s}")
+    for k, i, v in runs:
+        if len(v) < 2:
+            continue
+        print(f"{k[0][:52]:52s} {k[1]:9d} {k[2]:5d} {i:7d} {len(v):6d} {statistics.mean(v):9.2f} "
+              f"{statistics.median(v):9.2f} {min(v):9.2f}")
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.copy_mb, args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               f"Sharding is described in the design notes; run with --gpus 1.", file=sys.stderr)
@@ -471,10 +593,10 @@ def main():
     log(f"decode step: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s (wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
     for k, v in kernels.items():
         log(f"  {k:22s} {v['us']:8.2f} us  {v['GB/s']:8.1f} GB/s  {100 * v['frac_hbm']:.1f}% of HBM")
-    # dominant kernel: largest share of the step's time
-    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    # dominant kernel: the single-kernel entry with the largest share of the step's time
+    dom = max((k for k in kernels if len(STEP_KERNELS[k][1]) == 1), key=lambda k: kernels[k]["us"])
     kd = kernels[dom]
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    roofline = {"kernel": dom, "gpu_kernel": STEP_KERNELS[dom][1][0], "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom),
                 "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_us": kd["us"]}
     step_bytes = ds.step_bytes

@@ -52,36 +52,7 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
     return (b % kXcds) * per + b / kXcds;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Buffer offset of a row that does not exist: beyond every tensor (all
-// tensors are below 2 GiB, checked on the host) without wrapping when a K
-// offset is added, so loads return zero and stores are dropped.
-constexpr uint32_t kInvalidOffset = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    // raw buffer: stride 0, num_records in bytes, default data format word
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
 typedef const __attribute__((address_space(1))) void gbl_void;
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // s_waitcnt encoding on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// vmcnt(N) and lgkmcnt(0) in one wait.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
 
 struct WRaw {
     uint4 w[2][4];     // [nb][kb]: 8 consecutive bf16 of one feature row

@@ -1,4 +1,4 @@
-// Decode kernel: fused BitDelta linear for m <= 16 tokens, no MFMA.
+// Decode kernels: fused BitDelta linear for m <= 16 tokens.
 //
 // "BitDelta: Serving 14 Zen Models from One GPU Cluster", section "Serving
 // Architecture": the fused kernel reads the base weights and the packed
@@ -7,34 +7,45 @@
 // semantics y = x (W_base + alpha * unpack(signs))^T).
 //
 // At m <= 16 the layer is bound by HBM bandwidth (1 to 15 flop per byte of
-// W_base + signs), so this is a streaming GEMV on the vector ALUs whose job
-// is to keep enough bytes in flight:
-//  - a wave owns RW output rows and walks them 512 columns per step: lane l
-//    loads the 16 bytes of columns 8l..8l+7 of each row (every load
-//    instruction covers 1 KB of contiguous W_base) plus their sign byte;
-//  - a ring of D register stages keeps the next D steps' loads outstanding;
-//    the loop is split into a steady part (consume a stage, refill it D steps
-//    ahead) and a drain, with every load address clamped into the tensor, so
-//    no load sits under a branch and the compiler's wait counters stay exact
-//    (a branch around a load makes it wait for all loads at the join);
-//  - W_eff is formed in VGPRs (fp32 add of +-alpha, v_cvt_pk_bf16_f32 per
-//    pair) and each packed pair is multiplied into every token with
-//    v_dot2_f32_bf16 (fp32 accumulate);
-//  - m <= 4: the activations ride in the same ring (16-byte loads that hit
-//    L1/L2: x is at most 32 KB per row and shared by every wave);
-//    m in 5..16: they are staged per slab in LDS and read as 16-byte vectors,
-//    and each wave owns 4 rows to amortise those reads;
-//  - the RW * MT per-lane partial sums are reduced across the wave by a
-//    reduce-scatter (each halving step exchanges half of the values).
+// W_base + signs); the kernels exist to keep enough bytes in flight with as
+// few memory instructions as possible, and to keep the arithmetic per weight
+// small enough to hide under the loads.  Both build W_eff = bf16(W_base +
+// s alpha) the same way: the sign nibbles index a 16-entry LDS table of four
+// +-1.0f, one fma per weight (s alpha is exact, so the fma rounds once, as
+// the add would) and one v_cvt_pk_bf16_f32 per pair.
+//
+//  gemv_stream (m <= 4, vector ALU): a wave owns RW rows and walks them 512
+//    columns per step; lane l loads the 16 bytes of columns 8l..8l+7 of each
+//    row (every load instruction is 1 KB of one row, streamed past the
+//    caches), its sign byte, and the same columns of each token of x (L2
+//    hits).  A ring of D register stages keeps D steps of loads in flight;
+//    the loop is a steady part (consume a stage, refill it D steps ahead) and
+//    a drain, every address valid or deliberately out of range, so no load
+//    sits under a branch, and scheduling barriers keep the loads in issue
+//    order so the compiler's waits leave the later stages in flight.  Each
+//    packed W_eff pair meets every token in one v_dot2_f32_bf16; the RW * m
+//    per-lane sums are reduced across the wave by a reduce-scatter.
+//
+//  gemv_mfma (m in 5..16, matrix cores): one workgroup of 8 waves per block of
+//    16 rows; the columns are cut into super-blocks of 256 and wave w takes
+//    super-blocks w, w + 8, ...  Lane l (j = l % 16, q = l / 16) loads, for
+//    MFMA jj, the 16 bytes of chunk 4jj + q of row n0 + j (so the 4 lanes of a
+//    row read 64 contiguous bytes per instruction) and the same columns of
+//    token j, and runs v_mfma_f32_16x16x32_bf16 with A = x (tokens x 32
+//    columns) and B = W_eff (32 columns x rows).  A and B lanes of one q hold
+//    the same columns, whatever order the MFMA takes its k slots in.  Two
+//    register stages are in flight; the 8 partial 16 x 16 tiles are summed
+//    through LDS in wave order.
+//
+// All sums are in a fixed order: results do not depend on timing.
 #include <algorithm>
+#include <type_traits>
 
 #include "bd_device.h"
 #include "bd_launch.h"
 
 namespace bd {
 namespace {
-
-constexpr int kMaxLdsBytes = 128 * 1024;
 
 // One halving step of a reduce-scatter: lanes whose `MASK` bit is clear keep
 // values [0, HALF), the others keep [HALF, 2*HALF), each adding its partner's
@@ -72,85 +83,90 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[N])
     return s;
 }
 
-template <int RW, int MT>
-__device__ __forceinline__ void store_rows(float (&acc)[RW * MT], int64_t row0, int64_t R, int m,
-                                           uint16_t *__restrict__ y)
+// Sign table: entry e holds (bit b of e) ? +1 : -1 for b = 0..3.
+__device__ __forceinline__ void fill_sign_table(float *sgn)
 {
-    constexpr int N = RW * MT;
-    constexpr int kbits = log2i<N>();
-    const int lane = threadIdx.x & 63;
-    const float v = wave_reduce_scatter<N>(acc);
-    const int idx = lane >> (6 - kbits);
-    if ((lane & ((1 << (6 - kbits)) - 1)) == 0) {
-        const int r = idx / MT, t = idx - r * MT;
-        if (row0 + r < R && t < m)
-            y[(int64_t)t * R + row0 + r] = to_bf16(v);
-    }
+    if (threadIdx.x < 64)
+        sgn[threadIdx.x] = ((threadIdx.x >> 2) >> (threadIdx.x & 3)) & 1 ? 1.0f : -1.0f;
 }
 
-template <int RW, bool PER_MATRIX>
-struct Rows {
-    const uint4 *w[RW];
-    const uint8_t *s[RW];
-    float a[RW];
-    __device__ __forceinline__ Rows(const uint16_t *w_base, const uint8_t *signs, const float *alpha,
-                                    int64_t row0, int64_t R, int64_t C)
-    {
-        const int64_t G = C >> 3;
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int64_t row = row0 + r < R ? row0 + r : R - 1;  // clamped rows are never stored
-            w[r] = reinterpret_cast<const uint4 *>(w_base + row * C);
-            s[r] = signs + row * G;
-            a[r] = PER_MATRIX ? alpha[0] : alpha[row];
-        }
-    }
-};
+// W_eff for the 8 weights of `w` with sign byte `b` (bit i = weight i).
+__device__ __forceinline__ uint4 weff8(const float *sgn, uint32_t b, uint4 w, float a)
+{
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(&sgn[(b & 15u) * 4]);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(&sgn[((b >> 4) & 15u) * 4]);
+    uint4 e;
+    e.x = pack_bf16x2(fmaf(lo[0], a, lo_f32(w.x)), fmaf(lo[1], a, hi_f32(w.x)));
+    e.y = pack_bf16x2(fmaf(lo[2], a, lo_f32(w.y)), fmaf(lo[3], a, hi_f32(w.y)));
+    e.z = pack_bf16x2(fmaf(hi[0], a, lo_f32(w.z)), fmaf(hi[1], a, hi_f32(w.z)));
+    e.w = pack_bf16x2(fmaf(hi[2], a, lo_f32(w.w)), fmaf(hi[3], a, hi_f32(w.w)));
+    return e;
+}
 
-// ---------------------------------------------------------------- m <= 4
-template <int MT, int RW, int D, bool PER_MATRIX>
-__global__ __launch_bounds__(512) void gemv_direct(const uint16_t *__restrict__ x, int m,
+// ------------------------------------------------------------------ m <= 4
+// EVEN: d_in / 8 is a multiple of 64 (no ragged last step).  S = the number of
+// 512-column steps is a multiple of D (the host picks D).
+template <int MT, int RW, int D, bool PER_MATRIX, bool EVEN>
+__global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ x, int m,
                                                    const uint16_t *__restrict__ w_base,
                                                    const uint8_t *__restrict__ signs,
-                                                   const float *__restrict__ alpha, int64_t R, int64_t C,
-                                                   uint16_t *__restrict__ y)
+                                                   const float *__restrict__ alpha, int64_t R, int64_t K,
+                                                   uint16_t *__restrict__ y, int64_t ldy)
 {
     constexpr int kWaves = 8;
+    __shared__ __attribute__((aligned(16))) float sgn[64];
+    fill_sign_table(sgn);
+    __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RW;
-    const int64_t G = C >> 3;
-    const int S = (int)((G + 63) >> 6);  // a multiple of D (host checks)
-    const Rows<RW, PER_MATRIX> rows(w_base, signs, alpha, row0, R, C);
-    const uint4 *xrow[MT];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * RW;
+    const int64_t G = K >> 3;
+    const int S = (int)((G + 63) >> 6);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);
+    // Rows past R use an out-of-range offset (zeros, never stored).  In a
+    // ragged last step the lanes past the row read the next row's W_base and
+    // sign byte (finite) and x = 0, so they add nothing.
+    uint32_t wrow[RW], srow[RW];
+    float a[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const bool ok = row0 + r < R;
+        wrow[r] = ok ? (uint32_t)((row0 + r) * K * 2 + 16 * lane) : kInvalidOffset;
+        srow[r] = ok ? (uint32_t)((row0 + r) * G + lane) : kInvalidOffset;
+        a[r] = PER_MATRIX ? alpha[0] : alpha[ok ? row0 + r : R - 1];
+    }
+    uint32_t xrow[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
-        xrow[t] = reinterpret_cast<const uint4 *>(x) + (int64_t)(t < m ? t : m - 1) * G;
+        xrow[t] = t < m ? (uint32_t)(t * K * 2 + 16 * lane) : kInvalidOffset;
 
     uint4 wq[D][RW], xq[D][MT];
     uint32_t sq[D][RW];
     auto load = [&](int d, int s) {
-        const int64_t g0 = (int64_t)s * 64 + lane;
-        const int64_t g = g0 < G ? g0 : G - 1;
+        bool live = true;
+        if constexpr (!EVEN)
+            live = (int64_t)s * 64 + lane < G;
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            wq[d][r] = rows.w[r][g];
-            sq[d][r] = rows.s[r][g];
+            wq[d][r] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wrow[r], (uint32_t)s * 1024u, kStream));
+            sq[d][r] = __builtin_amdgcn_raw_buffer_load_b8(rs, srow[r], (uint32_t)s * 64u, kStream);
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-            xq[d][t] = xrow[t][g];
+            xq[d][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rx, live ? xrow[t] : kInvalidOffset, (uint32_t)s * 1024u, 0));
     };
     float acc[RW * MT];
 #pragma unroll
     for (int i = 0; i < RW * MT; ++i)
         acc[i] = 0.0f;
-    auto compute = [&](int d, int s) {
-        const bool live = (int64_t)s * 64 + lane < G;  // false only in a ragged last step
+    auto compute = [&](int d) {
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            uint4 e = weff_group(wq[d][r], sq[d][r], rows.a[r]);
-            if (!live)
-                e = make_uint4(0, 0, 0, 0);
+            const uint4 e = weff8(sgn, sq[d][r], wq[d][r], a[r]);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 float c = acc[r * MT + t];
@@ -163,116 +179,156 @@ __global__ __launch_bounds__(512) void gemv_direct(const uint16_t *__restrict__ 
         }
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+    for (int d = 0; d < D; ++d) {
         load(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s0 = 0; s0 < S - D; s0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            compute(d, s0 + d);
+            compute(d);
+            __builtin_amdgcn_sched_barrier(0);
             load(d, s0 + d + D);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-        compute(d, S - D + d);
-    store_rows<RW, MT>(acc, row0, R, m, y);
-}
+        compute(d);
 
-// ------------------------------------------------------------ m in 5..16
-// Activations staged in LDS, SLAB_STEPS steps (of 512 columns) at a time.
-template <int MT, int RW, int D, bool PER_MATRIX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemv_lds(const uint16_t *__restrict__ x, int m,
-                                                const uint16_t *__restrict__ w_base,
-                                                const uint8_t *__restrict__ signs,
-                                                const float *__restrict__ alpha, int64_t R, int64_t C,
-                                                uint16_t *__restrict__ y)
-{
-    constexpr int kWaves = 4;
-    constexpr int kThreads = 64 * kWaves;
-    constexpr int SLAB_STEPS = kMaxLdsBytes / (16 * 64 * MT);  // 8 for MT = 16
-    extern __shared__ uint4 xs[];                               // [MT][SLAB_STEPS * 64]
-    const int lane = threadIdx.x & 63;
-    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RW;
-    const int64_t G = C >> 3;
-    const int S = (int)((G + 63) >> 6);
-    const Rows<RW, PER_MATRIX> rows(w_base, signs, alpha, row0, R, C);
-    const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
-
-    uint4 wq[D][RW];
-    uint32_t sq[D][RW];
-    auto load = [&](int d, int s) {
-        const int64_t g0 = (int64_t)s * 64 + lane;
-        const int64_t g = g0 < G ? g0 : G - 1;
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            wq[d][r] = rows.w[r][g];
-            sq[d][r] = rows.s[r][g];
-        }
-    };
-    float acc[RW * MT];
-#pragma unroll
-    for (int i = 0; i < RW * MT; ++i)
-        acc[i] = 0.0f;
-    auto compute = [&](int d, int s, int s_base) {
-        const bool live = (int64_t)s * 64 + lane < G;
-        uint4 e[RW];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            e[r] = weff_group(wq[d][r], sq[d][r], rows.a[r]);
-            if (!live)
-                e[r] = make_uint4(0, 0, 0, 0);
-        }
-        const int lg = (s - s_base) * 64 + lane;
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const uint4 xv = xs[t * (SLAB_STEPS * 64) + lg];
-#pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                float c = acc[r * MT + t];
-                c = dot2(e[r].x, xv.x, c);
-                c = dot2(e[r].y, xv.y, c);
-                c = dot2(e[r].z, xv.z, c);
-                c = dot2(e[r].w, xv.w, c);
-                acc[r * MT + t] = c;
-            }
-        }
-    };
-
-    for (int base = 0; base < S; base += SLAB_STEPS) {
-        const int n = min(SLAB_STEPS, S - base);  // steps in this slab, a multiple of D
-        __syncthreads();
-        // Direct-to-LDS loads, 1 KB per wave instruction, all in flight at
-        // once.  Sources are clamped into x: tokens >= m read token m-1 and
-        // columns past the row read its last group, so every staged value is
-        // finite (their products are discarded or multiplied by zero).
-        for (int q = threadIdx.x >> 6; q < MT * SLAB_STEPS; q += kWaves) {
-            const int t = q / SLAB_STEPS, c = q - t * SLAB_STEPS;
-            const int64_t g0 = (int64_t)(base + c) * 64 + lane;
-            const int64_t g = g0 < G ? g0 : G - 1;
-            const uint4 *src = x4 + (int64_t)(t < m ? t : m - 1) * G + g;
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)src,
-                (void __attribute__((address_space(3))) *)(xs + t * (SLAB_STEPS * 64) + c * 64), 16, 0, 0);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): the staged slab has landed
-        __syncthreads();
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            load(d, base + d);
-        for (int s0 = base; s0 < base + n - D; s0 += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                compute(d, s0 + d, base);
-                load(d, s0 + d + D);
-            }
-        }
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            compute(d, base + n - D + d, base);
+    constexpr int N = RW * MT;
+    constexpr int kbits = log2i<N>();
+    const float v = wave_reduce_scatter<N>(acc);
+    const int idx = lane >> (6 - kbits);
+    if ((lane & ((1 << (6 - kbits)) - 1)) == 0) {
+        const int r = idx / MT, t = idx - r * MT;
+        if (row0 + r < R && t < m)
+            y[(int64_t)t * ldy + row0 + r] = to_bf16(v);
     }
-    store_rows<RW, MT>(acc, row0, R, m, y);
 }
 
+// ------------------------------------------------------------- m in 5..16
+constexpr int kMfmaWaves = 8;
+constexpr int kSuperK = 256;  // columns per super-block (32 chunks of 8)
+
+// EVEN: d_in is a multiple of 256 (whole super-blocks; sign rows 16-byte
+// aligned, so each lane fetches its super-block's 32 sign bytes in two
+// 16-byte loads).  Otherwise the lane loads its 8 sign bytes one by one and
+// x is zero past the row.
+template <bool PER_MATRIX, bool EVEN>
+__global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__restrict__ x, int m,
+                                                             const uint16_t *__restrict__ w_base,
+                                                             const uint8_t *__restrict__ signs,
+                                                             const float *__restrict__ alpha, int64_t R,
+                                                             int64_t K, uint16_t *__restrict__ y, int64_t ldy)
+{
+    constexpr int KW = kMfmaWaves;
+    __shared__ __attribute__((aligned(16))) float sgn[64];
+    __shared__ f32x4 red[KW][64];
+    fill_sign_table(sgn);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15, q = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t G = K >> 3;
+    const int T = (int)((K + kSuperK - 1) / kSuperK);
+    const int nt = T > wave ? (T - 1 - wave) / KW + 1 : 0;  // this wave's super-blocks (uniform)
+    const bool row_ok = n0 + j < R;
+    const float a = PER_MATRIX ? alpha[0] : alpha[row_ok ? n0 + j : R - 1];
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);
+    const uint32_t wrow = row_ok ? (uint32_t)((n0 + j) * K * 2 + 16 * q) : kInvalidOffset;
+    const uint32_t srow = row_ok ? (uint32_t)((n0 + j) * G) : kInvalidOffset;
+    const uint32_t xrow = j < m ? (uint32_t)(j * K * 2 + 16 * q) : kInvalidOffset;
+
+    struct Stage {
+        uint4 w[8], x[8];
+        uint32_t s[8];  // EVEN: the 32 sign bytes (dword jj holds chunk 4jj + q in byte q); else byte jj
+    };
+    Stage st[2];
+    // Stages past the wave's last super-block are issued with out-of-range
+    // offsets: no traffic, and zeros (x = 0 adds nothing when consumed).
+    auto issue = [&](int b, int t) {
+        const bool live = t < nt;
+        const int sb = wave + t * KW;
+        const uint32_t so = (uint32_t)sb * (kSuperK * 2);
+        const uint32_t wv = live ? wrow : kInvalidOffset;
+        const uint32_t sv = live ? srow : kInvalidOffset;
+        if constexpr (EVEN) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint4 v = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, sv + 16 * i, (uint32_t)sb * 32u, 0));
+                st[b].s[4 * i] = v.x;
+                st[b].s[4 * i + 1] = v.y;
+                st[b].s[4 * i + 2] = v.z;
+                st[b].s[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                st[b].s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, sv + 4 * jj + q, (uint32_t)sb * 32u, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            bool ok = live;
+            if constexpr (!EVEN)
+                ok = ok && (int64_t)sb * 32 + 4 * jj + q < G;
+            st[b].w[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv + 64 * jj, so, 0));
+            st[b].x[jj] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xrow + 64 * jj : kInvalidOffset, so, 0));
+        }
+    };
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](int b) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const uint32_t byte = EVEN ? (st[b].s[jj] >> (8 * q)) & 0xFFu : st[b].s[jj];
+            const uint4 e = weff8(sgn, byte, st[b].w[jj], a);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st[b].x[jj]),
+                                                          __builtin_bit_cast(bf16x8, e), acc, 0, 0, 0);
+        }
+    };
+    // Scheduling barriers keep each stage's loads in issue order, so the
+    // compiler's wait before a compute leaves the next stage in flight.  The
+    // last two computes may consume dead (all-zero x) stages: no branch.
+    issue(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t + 2 < nt; t += 2) {
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0, t + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(1, t + 3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(0);
+    compute(1);
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        // D layout of the 16 x 16 tile: lane l holds tokens 4 (l / 16) + r of row l % 16
+        const int src = threadIdx.x >> 2, r = threadIdx.x & 3;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < KW; ++w)
+            v += red[w][src][r];
+        const int tok = 4 * (src >> 4) + r;
+        const int64_t row = n0 + (src & 15);
+        if (tok < m && row < R)
+            y[(int64_t)tok * ldy + row] = to_bf16(v);
+    }
+}
+
+// ---------------------------------------------------------------- launch
+// Largest D <= dmax that divides S.
 int pipeline_depth(int64_t S, int dmax)
 {
     int d = dmax;
@@ -281,101 +337,101 @@ int pipeline_depth(int64_t S, int dmax)
     return d;
 }
 
+struct Args {
+    const uint16_t *x;
+    int m;
+    const uint16_t *w;
+    const uint8_t *sg;
+    const float *a;
+    bool pm;
+    int64_t rows, d_in, ldy;
+    uint16_t *y;
+    hipStream_t s;
+};
+
 template <int MT, int RW, int D>
-hipError_t launch_direct(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
-                         const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
-                         hipStream_t s)
+hipError_t launch_stream(const Args &g)
 {
-    const int64_t rows_per_block = 8 * RW;
-    const dim3 grid((unsigned)((d_out + rows_per_block - 1) / rows_per_block)), block(512);
-    if (per_matrix)
-        hipLaunchKernelGGL((gemv_direct<MT, RW, D, true>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, d_in, y);
-    else
-        hipLaunchKernelGGL((gemv_direct<MT, RW, D, false>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, d_in, y);
+    const bool even = (g.d_in >> 3) % 64 == 0;
+    const dim3 grid((unsigned)((g.rows + 8 * RW - 1) / (8 * RW))), block(512);
+#define BD_STREAM(PM, EV)                                                                                   \
+    hipLaunchKernelGGL((gemv_stream<MT, RW, D, PM, EV>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, \
+                       g.d_in, g.y, g.ldy)
+    if (g.pm) {
+        if (even) BD_STREAM(true, true);
+        else BD_STREAM(true, false);
+    } else {
+        if (even) BD_STREAM(false, true);
+        else BD_STREAM(false, false);
+    }
+#undef BD_STREAM
     return hipGetLastError();
 }
 
-template <int MT, int RW, int D>
-hipError_t launch_lds(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
-                      const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
-                      hipStream_t s)
-{
-    const int64_t rows_per_block = 4 * RW;
-    const dim3 grid((unsigned)((d_out + rows_per_block - 1) / rows_per_block)), block(256);
-    constexpr int lds = kMaxLdsBytes;
-    // LDS above the 64 KB default must be requested once per kernel.
-    static const bool lds_ok = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<MT, RW, D, true>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_lds<MT, RW, D, false>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
-    }();
-    if (!lds_ok)
-        return hipErrorInvalidConfiguration;
-    if (per_matrix)
-        hipLaunchKernelGGL((gemv_lds<MT, RW, D, true>), grid, block, lds, s, x, m, w_base, signs, alpha, d_out, d_in, y);
-    else
-        hipLaunchKernelGGL((gemv_lds<MT, RW, D, false>), grid, block, lds, s, x, m, w_base, signs, alpha, d_out, d_in, y);
-    return hipGetLastError();
-}
-
-// D must divide the number of 512-column steps; pick the largest allowed.
 template <int MT, int RW>
-hipError_t dispatch_direct(const uint16_t *x, int m, const uint16_t *w, const uint8_t *sg, const float *a, bool pm,
-                           int64_t d_out, int64_t d_in, uint16_t *y, hipStream_t s, int dmax)
+hipError_t dispatch_stream(const Args &g, int dmax)
 {
-    const int64_t S = ((d_in >> 3) + 63) >> 6;
+    const int64_t S = ((g.d_in >> 3) + 63) >> 6;
     switch (pipeline_depth(S, dmax)) {
-    case 8: if constexpr (MT == 1) return launch_direct<MT, RW, 8>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    case 8: if constexpr (MT == 1) return launch_stream<MT, RW, 8>(g);
             [[fallthrough]];
-    case 7: if constexpr (MT == 1) return launch_direct<MT, RW, 7>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    case 7: if constexpr (MT == 1) return launch_stream<MT, RW, 7>(g);
             [[fallthrough]];
-    case 6: if constexpr (MT == 1) return launch_direct<MT, RW, 6>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    case 6: if constexpr (MT == 1) return launch_stream<MT, RW, 6>(g);
             [[fallthrough]];
-    case 5: if constexpr (MT == 1) return launch_direct<MT, RW, 5>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    case 5: if constexpr (MT == 1) return launch_stream<MT, RW, 5>(g);
             [[fallthrough]];
-    case 4: return launch_direct<MT, RW, 4>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    case 3: return launch_direct<MT, RW, 3>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    case 2: return launch_direct<MT, RW, 2>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    default: return launch_direct<MT, RW, 1>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    case 4: return launch_stream<MT, RW, 4>(g);
+    case 3: return launch_stream<MT, RW, 3>(g);
+    case 2: return launch_stream<MT, RW, 2>(g);
+    default: return launch_stream<MT, RW, 1>(g);
     }
 }
 
-// For the LDS kernels D must divide every slab's step count: the full slab
-// (a power of two) and the last one.
-template <int MT, int RW>
-hipError_t dispatch_lds(const uint16_t *x, int m, const uint16_t *w, const uint8_t *sg, const float *a, bool pm,
-                        int64_t d_out, int64_t d_in, uint16_t *y, hipStream_t s)
+hipError_t launch_mfma(const Args &g)
 {
-    constexpr int slab = kMaxLdsBytes / (16 * 64 * MT);
-    const int64_t S = ((d_in >> 3) + 63) >> 6;
-    const int64_t last = S % slab == 0 ? std::min<int64_t>(S, slab) : S % slab;
-    int d = 4;
-    while (d > 1 && (last % d != 0 || (S > slab && slab % d != 0)))
-        --d;
-    switch (d) {
-    case 4: return launch_lds<MT, RW, 4>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    case 3: return launch_lds<MT, RW, 3>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    case 2: return launch_lds<MT, RW, 2>(x, m, w, sg, a, pm, d_out, d_in, y, s);
-    default: return launch_lds<MT, RW, 1>(x, m, w, sg, a, pm, d_out, d_in, y, s);
+    const bool even = g.d_in % kSuperK == 0;
+    const dim3 grid((unsigned)((g.rows + 15) / 16)), block(64 * kMfmaWaves);
+#define BD_MFMA(PM, EV)                                                                                     \
+    hipLaunchKernelGGL((gemv_mfma<PM, EV>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, g.d_in, g.y, \
+                       g.ldy)
+    if (g.pm) {
+        if (even) BD_MFMA(true, true);
+        else BD_MFMA(true, false);
+    } else {
+        if (even) BD_MFMA(false, true);
+        else BD_MFMA(false, false);
     }
+#undef BD_MFMA
+    return hipGetLastError();
 }
 
 }  // namespace
 
+// Rows are launched in chunks whose W_base stays below 2 GiB (the kernels
+// address it with 32-bit buffer offsets); y keeps its full row stride.
 hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
                        uint16_t *y, hipStream_t s)
 {
-    if (m <= 1)
-        return dispatch_direct<1, 2>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s, 8);
-    if (m <= 2)
-        return dispatch_direct<2, 2>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s, 4);
-    if (m <= 4)
-        return dispatch_direct<4, 2>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s, 4);
-    if (m <= 8)
-        return dispatch_lds<8, 4>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s);
-    return dispatch_lds<16, 4>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s);
+    const int64_t G = d_in >> 3;
+    const int64_t max_rows = std::max<int64_t>(16, (((int64_t)1 << 31) - 1) / (d_in * 2) / 16 * 16);
+    for (int64_t r0 = 0; r0 < d_out; r0 += max_rows) {
+        Args g{x, m, w_base + r0 * d_in, signs + r0 * G, per_matrix ? alpha : alpha + r0, per_matrix,
+               std::min(max_rows, d_out - r0), d_in, d_out, y + r0, s};
+        hipError_t e;
+        if (m <= 1)
+            e = dispatch_stream<1, 1>(g, 8);
+        else if (m <= 2)
+            e = dispatch_stream<2, 2>(g, 4);
+        else if (m <= 4)
+            e = dispatch_stream<4, 2>(g, 4);
+        else
+            e = launch_mfma(g);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace bd
