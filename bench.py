@@ -7,8 +7,8 @@ full pass of the single-layer hot path over one batch:
   compress (per-row alpha) -> compress (per-matrix alpha) -> reconstruct ->
   fused linear at m = 1, 4, 16 tokens with per-row alpha -> the same three
   with the per-matrix alpha,
-each call reading its own weight set out of 16 rotating sets (571 MB of
-weights, more than the 256 MB MALL, so every step streams from HBM).
+each launch reading its own weight set out of 16 rotating sets (571 MB of
+weights, more than the 256 MB MALL, so every launch streams from HBM).
 `value` is the step's algorithmic HBM bytes (inputs read + outputs written,
 per kernel) divided by its time: GB/s.  The steps are captured in HIP graphs
 (one per weight set) so the microsecond-scale decode launches are not bound
@@ -56,12 +56,12 @@ STEP_KERNELS = {
     "compress_row": ("compress.hip", [r"compress_rows<true, false>"]),
     "compress_matrix": ("compress.hip", [r"compress_rows<true, true>", r"alpha_matrix_finish"]),
     "reconstruct": ("reconstruct.hip", [r"reconstruct_rows<false>"]),
-    "linear_m1_row": ("gemv.hip", [r"gemv_direct<1, 2, \d+, false>"]),
-    "linear_m1_matrix": ("gemv.hip", [r"gemv_direct<1, 2, \d+, true>"]),
-    "linear_m4_row": ("gemv.hip", [r"gemv_direct<4, 2, \d+, false>"]),
-    "linear_m4_matrix": ("gemv.hip", [r"gemv_direct<4, 2, \d+, true>"]),
-    "linear_m16_row": ("gemv.hip", [r"gemv_lds<16, 4, \d+, false>"]),
-    "linear_m16_matrix": ("gemv.hip", [r"gemv_lds<16, 4, \d+, true>"]),
+    "linear_m1_row": ("gemv.hip", [r"gemv_stream<1, 1, \d+, false, true>"]),
+    "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true>"]),
+    "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 2, \d+, false, true>"]),
+    "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 2, \d+, true, true>"]),
+    "linear_m16_row": ("gemv.hip", [r"gemv_mfma<false, true>"]),
+    "linear_m16_matrix": ("gemv.hip", [r"gemv_mfma<true, true>"]),
 }
 
 
@@ -166,8 +166,13 @@ class DecodeStep:
         bd.check(rc)
 
     def step(self, i, stream):
-        for name in self.bytes:
-            self.launch(name, i, stream)
+        """Step i: its j-th launch uses weight set (len(bytes) * i + j) mod SETS,
+        so consecutive launches over the replayed steps walk the 16 sets in
+        order and no launch finds its weights still cached (a set comes back
+        after 15 other launches, more than the 256 MB MALL holds)."""
+        n = len(self.bytes)
+        for j, name in enumerate(self.bytes):
+            self.launch(name, (n * i + j) % SETS, stream)
 
     @property
     def step_bytes(self):
