@@ -613,21 +613,291 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
     }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave variant (d_in a multiple of 64): two waves per SIMD, so one
+// wave's barrier, copy issue and LDS waits are covered by the other's MFMAs.
+// Wave (wm, wn) = (wave / 4, wave % 4) owns output rows wm*128 .. +127 and
+// features wn*64 .. +63 of the 256 x 256 tile (4 x 2 MFMA tiles of 32 x 32,
+// 128 accumulators, so two waves fit the register file).  Per K step of 64:
+//  - x tile: direct-to-LDS copies one step ahead, as in gemm_tiles_fast;
+//  - W_base: each wave loads the 32 feature rows 32*wave .. +31 of the tile
+//    straight into VGPRs two steps ahead (1 KB per instruction: 8 rows x 128
+//    contiguous bytes) with their sign bytes, forms W_eff = bf16(W_base +
+//    s alpha) for them once, and writes it to a double-buffered LDS tile in
+//    the MFMA B-operand layout; every wave then reads its 64 features from
+//    there.  W_eff is built exactly once per workgroup and never leaves LDS.
+//  - one barrier per step.
+constexpr int kThreads8 = 512;
+constexpr bool kUseW8 = true;
+
+template <bool PER_MATRIX, bool GATHER, bool SPLIT>
+__global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
+                   const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
+                   int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
+                   const int32_t *__restrict__ table, int32_t n_variants,
+                   int64_t k_split, float *__restrict__ partial)
+{
+    // separate objects per buffer: a read of one is then tied only to the
+    // copies into that one
+    __shared__ __attribute__((aligned(16))) uint8_t XS0[kXsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t XS1[kXsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t WE0[kWsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t WE1[kWsBytes];
+    __shared__ int32_t rows_s[GATHER ? BM : 1];
+    uint8_t *const XSb[2] = {XS0, XS1};
+    uint8_t *const WEb[2] = {WE0, WE1};
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int hi = lane >> 5;
+    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t mt = b % m_tiles, nt = b / m_tiles;
+    const int64_t n0 = nt * BN;
+
+    int64_t m0 = mt * BM;
+    const uint8_t *signs = signs_all;
+    const float *alpha = alpha_all;
+    if constexpr (GATHER) {
+        const int32_t total = table[0];
+        if (mt >= total)
+            return;
+        const int32_t *perm = table + 4;
+        const int32_t *tile_v = perm + M;
+        const int32_t *tile_row0 = tile_v + m_tiles;
+        const int32_t *tile_rows = tile_row0 + m_tiles;
+        const int v = tile_v[mt];
+        const int row0 = tile_row0[mt], nrows = tile_rows[mt];
+        for (int i = threadIdx.x; i < BM; i += kThreads8)
+            rows_s[i] = i < nrows ? perm[row0 + i] : -1;
+        __syncthreads();
+        if (v >= n_variants) {
+            for (int i = 0; i < nrows; ++i) {
+                const int64_t tok = rows_s[i];
+                for (int64_t j = n0 + threadIdx.x; j < min(N, n0 + BN); j += kThreads8)
+                    y[tok * N + j] = 0;
+            }
+            return;
+        }
+        signs = signs_all + (int64_t)v * N * (K >> 3);
+        alpha = PER_MATRIX ? alpha_all + v : alpha_all + (int64_t)v * N;
+        m0 = 0;
+    }
+
+    const int64_t G = K >> 3;
+    const int64_t k_begin = (int64_t)blockIdx.y * k_split;
+    const int T = (int)((min(K, k_begin + k_split) - k_begin) / BK);
+    const uint32_t kx0 = (uint32_t)(k_begin * 2);
+    const uint32_t ks0 = (uint32_t)(k_begin / 8);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, N * K * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, N * G);
+
+    // x copies: instruction j (0..3) of wave w covers tile rows 32w + 8j ..
+    // +7; lane l writes LDS position l & 7 of row 8j + l / 8, which holds
+    // logical chunk (l & 7) ^ ((row >> 1) & 7).
+    const int p = lane & 7;
+    uint32_t xoff[GATHER ? 4 : 2];
+#pragma unroll
+    for (int j = 0; j < (GATHER ? 4 : 2); ++j) {
+        const int row = wave * 32 + j * 8 + (lane >> 3);
+        const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
+        int64_t tok;
+        if constexpr (GATHER)
+            tok = rows_s[row];
+        else
+            tok = m0 + row;
+        xoff[j] = (tok < 0 || tok >= M) ? kInvalidOffset : (uint32_t)((tok * K + c * 8) * 2);
+    }
+    const uint32_t xstride16 = (uint32_t)(16 * K * 2);  // 16 rows further (dense)
+    auto dma_x = [&](int t, int buf) {
+        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t vo, so;
+            if constexpr (GATHER) {
+                vo = xoff[j];
+                so = kb;
+            } else {
+                vo = xoff[j & 1];
+                so = (uint32_t)(j >> 1) * xstride16 + kb;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 4 + j) * 1024), 16, vo, so, 0,
+                                                     0);
+        }
+    };
+
+    // W_base rows of this wave: load i (0..3) covers feature rows
+    // 32*wave + 8i .. +7, lane l -> row 8i + l / 8, chunk l & 7 (8 columns).
+    // One lane offset for i = 0; the 8i rows go in the scalar offset (a row
+    // at or past N lands past the end of W_base / signs: zeros).
+    const int64_t nw = n0 + wave * 32 + (lane >> 3);
+    const uint32_t woff = nw < N ? (uint32_t)((nw * K + p * 8) * 2) : kInvalidOffset;
+    const uint32_t soff = nw < N ? (uint32_t)(nw * G + p) : kInvalidOffset;
+    const uint32_t wrow8 = (uint32_t)(8 * K * 2), srow8 = (uint32_t)(8 * G);
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t n = nw + 8 * i;
+        a[i] = PER_MATRIX ? alpha[0] : (n < N ? alpha[n] : 0.0f);
+    }
+    struct WRaw8 {
+        uint4 w[4];
+        uint32_t s[4];
+    };
+    // group i of the W_base rows (8 rows x 64 columns) and its sign bytes
+    auto load_w = [&](WRaw8 &r, int i, int t) {
+        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
+        const uint32_t ksb = ks0 + (uint32_t)(t * 8);
+        r.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, kb + i * wrow8, 0));
+        r.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff, ksb + i * srow8, 0);
+    };
+    // W_eff of load i -> LDS row n_local = 32*wave + 8i + l/8, position p ^ swizzle
+    auto build_store = [&](const WRaw8 &r, int i, int buf) {
+        const int nl = wave * 32 + i * 8 + (lane >> 3);
+        const int sw = ((i & 1) * 4 + (lane >> 4)) & 7;  // (nl >> 1) & 7
+        const uint4 e = weff_group(r.w[i], r.s[i], a[i]);
+        *reinterpret_cast<uint4 *>(WEb[buf] + nl * 128 + ((p ^ sw) * 16)) = e;
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[mb][nb][v] = 0.0f;
+
+    const int frow = lane & 31;
+    const int fsw = (frow >> 1) & 7;
+    auto read_a = [&](bf16x8 (&A)[4], int buf, int kb) {
+        const uint8_t *base = XSb[buf] + (wm * 128 + frow) * 128 + (((kb * 2 + hi) ^ fsw) * 16);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+            A[mb] = *reinterpret_cast<const bf16x8 *>(base + mb * 32 * 128);
+    };
+    auto read_b = [&](bf16x8 (&B)[2], int buf, int kb) {
+        const uint8_t *base = WEb[buf] + (wn * 64 + frow) * 128 + (((kb * 2 + hi) ^ fsw) * 16);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            B[nb] = *reinterpret_cast<const bf16x8 *>(base + nb * 32 * 128);
+    };
+
+    // ---- prologue: x(0) copy, W(0) loaded and built into WE0, W(1) loaded
+    WRaw8 wr;
+    dma_x(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        load_w(wr, i, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        build_store(wr, i, 0);
+        load_w(wr, i, T > 1 ? 1 : 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Per step t: copy x(t+1) into buffer nxt; run the 32 MFMAs of step t
+    // from buffers cur; after every 8 MFMAs form one group of W_eff(t+1)
+    // (into WE nxt) from the registers and refill those registers with the
+    // same group of W(t+2), one step ahead.
+    auto step = [&](int t, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        constexpr int nxt = 1 - cur;
+        const int t1 = t + 1 < T ? t + 1 : T - 1;
+        const int t2 = t + 2 < T ? t + 2 : T - 1;
+        dma_x(t1, nxt);  // 4 copies
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 A[2][4], B[2][2];
+        read_a(A[0], cur, 0);
+        read_b(B[0], cur, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb < 3) {
+                read_a(A[(kb + 1) & 1], cur, kb + 1);
+                read_b(B[(kb + 1) & 1], cur, kb + 1);
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[kb & 1][nb], acc[mb][nb],
+                                                                          0, 0, 0);
+            build_store(wr, kb, nxt);
+            load_w(wr, kb, t2);  // 2 loads
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // x(t+1) has landed (the 8 W loads issued after it may be in
+        // flight) and W_eff(t+1) is written: then all waves may use buffer nxt
+        wait_vmcnt_lgkm0<8>();
+        __builtin_amdgcn_s_barrier();
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < T)
+        step(t, std::integral_constant<int, 0>{});
+
+    if constexpr (SPLIT) {
+        // fp32 partials in accumulator order: [split][tile][wave][mb][nb][quarter][lane][4]
+        const int64_t tile = nt * m_tiles + mt;
+        const int64_t tiles = (int64_t)gridDim.x;
+        float *base = partial + (((int64_t)blockIdx.y * tiles + tile) * 8 + wave) * (4 * 2 * 4 * 256);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(base + ((mb * 2 + nb) * 4 + q) * 256 + lane * 4) =
+                        make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                    acc[mb][nb][4 * q + 3]);
+    } else {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int64_t j = n0 + wn * 64 + nb * 32 + (lane & 31);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int i = wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                    int64_t tok;
+                    if constexpr (GATHER)
+                        tok = rows_s[i];
+                    else
+                        tok = m0 + i < M ? m0 + i : -1;
+                    const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
+                    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
+                }
+            }
+        }
+    }
+}
+
 // Sum the split-K partials of gemm_tiles_fast in split order (fixed, so the
 // result is deterministic) and write bf16 y.  One thread per 4 accumulators.
+// W8: partials of gemm_tiles_w8 (8 waves x 4 x 2 MFMA tiles) rather than of
+// gemm_tiles_fast (4 waves x 8 x 2); the same 256 x 256 floats per tile.
+template <bool W8>
 __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ partial, int splits, int64_t tiles,
                                                      int64_t m_tiles, int64_t M, int64_t N,
                                                      uint16_t *__restrict__ y)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * 4 waves * 64 chunks * 64 lanes
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * 256 chunks * 64 lanes
     const int lane = (int)(gid & 63);
     const int64_t chunk = gid >> 6;
-    const int q = (int)(chunk & 3), nb = (int)((chunk >> 2) & 1), mb = (int)((chunk >> 3) & 7);
-    const int wave = (int)((chunk >> 6) & 3);
+    const int q = (int)(chunk & 3), nb = (int)((chunk >> 2) & 1);
+    const int mb = W8 ? (int)((chunk >> 3) & 3) : (int)((chunk >> 3) & 7);
+    const int wave = W8 ? (int)((chunk >> 5) & 7) : (int)((chunk >> 6) & 3);
     const int64_t tile = chunk >> 8;
     if (tile >= tiles)
         return;
-    const int64_t stride = tiles * 4 * (8 * 2 * 4 * 256);  // floats per split
+    const int64_t stride = tiles * 256 * 256;  // floats per split
     const float *src = partial + chunk * 256 + lane * 4;
     float4 s = *reinterpret_cast<const float4 *>(src);
     for (int sp = 1; sp < splits; ++sp) {
@@ -638,8 +908,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ p
         s.w += v.w;
     }
     const int64_t mt = tile % m_tiles, nt = tile / m_tiles;
-    const int64_t j = nt * BN + wave * 64 + nb * 32 + (lane & 31);
-    const int64_t i0 = mt * BM + mb * 32 + 8 * q + 4 * (lane >> 5);
+    const int64_t j = nt * BN + (W8 ? (wave & 3) * 64 : wave * 64) + nb * 32 + (lane & 31);
+    const int64_t i0 = mt * BM + (W8 ? (wave >> 2) * 128 : 0) + mb * 32 + 8 * q + 4 * (lane >> 5);
     if (j >= N)
         return;
     const float v4[4] = {s.x, s.y, s.z, s.w};
@@ -746,29 +1016,43 @@ hipError_t launch_tiles(const uint16_t *x, int64_t m, const uint16_t *w_base, co
     const int64_t k_split = splits > 1 ? gemm_k_split(d_in, splits) : d_in;
     const int used = (int)((d_in + k_split - 1) / k_split);
     float *part = used > 1 ? partial : nullptr;
-    const dim3 grid((unsigned)(m_tiles * n_tiles), (unsigned)used), block(kThreads);
+    const dim3 grid((unsigned)(m_tiles * n_tiles), (unsigned)used);
 #define BD_FAST(PM, SP)                                                                                    \
-    hipLaunchKernelGGL((gemm_tiles_fast<PM, GATHER, SP>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out, \
-                       d_in, y, m_tiles, table, n_variants, k_split, part)
-    if (per_matrix) {
-        if (part)
-            BD_FAST(true, true);
-        else
-            BD_FAST(true, false);
+    hipLaunchKernelGGL((gemm_tiles_fast<PM, GATHER, SP>), grid, dim3(kThreads), 0, s, x, m, w_base, signs, alpha, \
+                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part)
+#define BD_W8(PM, SP)                                                                                      \
+    hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs, alpha, \
+                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part)
+    if (kUseW8) {
+        if (per_matrix) {
+            if (part) BD_W8(true, true);
+            else BD_W8(true, false);
+        } else {
+            if (part) BD_W8(false, true);
+            else BD_W8(false, false);
+        }
     } else {
-        if (part)
-            BD_FAST(false, true);
-        else
-            BD_FAST(false, false);
+        if (per_matrix) {
+            if (part) BD_FAST(true, true);
+            else BD_FAST(true, false);
+        } else {
+            if (part) BD_FAST(false, true);
+            else BD_FAST(false, false);
+        }
     }
 #undef BD_FAST
+#undef BD_W8
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || part == nullptr)
         return e;
     const int64_t tiles = m_tiles * n_tiles;
-    const int64_t threads = tiles * 4 * 64 * 64;
-    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used, tiles,
-                       m_tiles, m, d_out, y);
+    const int64_t threads = tiles * 256 * 64;
+    if (kUseW8)
+        hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
+                           tiles, m_tiles, m, d_out, y);
+    else
+        hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
+                           tiles, m_tiles, m, d_out, y);
     return hipGetLastError();
 }
 
