@@ -64,6 +64,30 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Sign table for weff8: entry e holds (bit b of e) ? +1 : -1 for b = 0..3
+// (64 floats in LDS, filled by the first 64 threads of the workgroup).
+__device__ __forceinline__ void fill_sign_table(float *sgn)
+{
+    if (threadIdx.x < 64)
+        sgn[threadIdx.x] = ((threadIdx.x >> 2) >> (threadIdx.x & 3)) & 1 ? 1.0f : -1.0f;
+}
+
+// W_eff for the 8 weights of `w` with sign byte `b` (bit i = weight i): one
+// fma per weight with s = +-1 from the table (s * alpha is exact, so the fma
+// rounds once, exactly as fp32 W + (+-alpha) does), one v_cvt_pk_bf16_f32 per
+// pair.  Same result as weff_group.
+__device__ __forceinline__ uint4 weff8(const float *sgn, uint32_t b, uint4 w, float a)
+{
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(&sgn[(b & 15u) * 4]);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(&sgn[((b >> 4) & 15u) * 4]);
+    uint4 e;
+    e.x = pack_bf16x2(fmaf(lo[0], a, lo_f32(w.x)), fmaf(lo[1], a, hi_f32(w.x)));
+    e.y = pack_bf16x2(fmaf(lo[2], a, lo_f32(w.y)), fmaf(lo[3], a, hi_f32(w.y)));
+    e.z = pack_bf16x2(fmaf(hi[0], a, lo_f32(w.z)), fmaf(hi[1], a, hi_f32(w.z)));
+    e.w = pack_bf16x2(fmaf(hi[2], a, lo_f32(w.w)), fmaf(hi[3], a, hi_f32(w.w)));
+    return e;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer offset of a row that does not exist: beyond every tensor (all

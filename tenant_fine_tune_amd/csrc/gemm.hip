@@ -623,7 +623,8 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
 //  - W_base: each wave loads the 32 feature rows 32*wave .. +31 of the tile
 //    straight into VGPRs two steps ahead (1 KB per instruction: 8 rows x 128
 //    contiguous bytes) with their sign bytes, forms W_eff = bf16(W_base +
-//    s alpha) for them once, and writes it to a double-buffered LDS tile in
+//    s alpha) for them once (one fma per weight, sign table in LDS), and
+//    writes it to a double-buffered LDS tile in
 //    the MFMA B-operand layout; every wave then reads its 64 features from
 //    there.  W_eff is built exactly once per workgroup and never leaves LDS.
 //  - one barrier per step.
@@ -645,8 +646,11 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     __shared__ __attribute__((aligned(16))) uint8_t WE0[kWsBytes];
     __shared__ __attribute__((aligned(16))) uint8_t WE1[kWsBytes];
     __shared__ int32_t rows_s[GATHER ? BM : 1];
+    __shared__ __attribute__((aligned(16))) float sgn[64];
     uint8_t *const XSb[2] = {XS0, XS1};
     uint8_t *const WEb[2] = {WE0, WE1};
+    fill_sign_table(sgn);
+    __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -757,7 +761,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     auto build_store = [&](const WRaw8 &r, int i, int buf) {
         const int nl = wave * 32 + i * 8 + (lane >> 3);
         const int sw = ((i & 1) * 4 + (lane >> 4)) & 7;  // (nl >> 1) & 7
-        const uint4 e = weff_group(r.w[i], r.s[i], a[i]);
+        const uint4 e = weff8(sgn, r.s[i], r.w[i], a[i]);
         *reinterpret_cast<uint4 *>(WEb[buf] + nl * 128 + ((p ^ sw) * 16)) = e;
     };
 

@@ -83,26 +83,6 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[N])
     return s;
 }
 
-// Sign table: entry e holds (bit b of e) ? +1 : -1 for b = 0..3.
-__device__ __forceinline__ void fill_sign_table(float *sgn)
-{
-    if (threadIdx.x < 64)
-        sgn[threadIdx.x] = ((threadIdx.x >> 2) >> (threadIdx.x & 3)) & 1 ? 1.0f : -1.0f;
-}
-
-// W_eff for the 8 weights of `w` with sign byte `b` (bit i = weight i).
-__device__ __forceinline__ uint4 weff8(const float *sgn, uint32_t b, uint4 w, float a)
-{
-    const f32x4 lo = *reinterpret_cast<const f32x4 *>(&sgn[(b & 15u) * 4]);
-    const f32x4 hi = *reinterpret_cast<const f32x4 *>(&sgn[((b >> 4) & 15u) * 4]);
-    uint4 e;
-    e.x = pack_bf16x2(fmaf(lo[0], a, lo_f32(w.x)), fmaf(lo[1], a, hi_f32(w.x)));
-    e.y = pack_bf16x2(fmaf(lo[2], a, lo_f32(w.y)), fmaf(lo[3], a, hi_f32(w.y)));
-    e.z = pack_bf16x2(fmaf(hi[0], a, lo_f32(w.z)), fmaf(hi[1], a, hi_f32(w.z)));
-    e.w = pack_bf16x2(fmaf(hi[2], a, lo_f32(w.w)), fmaf(hi[3], a, hi_f32(w.w)));
-    return e;
-}
-
 // ------------------------------------------------------------------ m <= 4
 // EVEN: d_in / 8 is a multiple of 64 (no ragged last step).  S = the number of
 // 512-column steps is a multiple of D (the host picks D).
