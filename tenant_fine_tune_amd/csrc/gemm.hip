@@ -639,6 +639,8 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
                    const int32_t *__restrict__ table, int32_t n_variants,
                    int64_t k_split, float *__restrict__ partial)
 {
+    // sign table first (at LDS address 0 its lookups need no base)
+    __shared__ __attribute__((aligned(16))) float sgn[64];
     // separate objects per buffer: a read of one is then tied only to the
     // copies into that one
     __shared__ __attribute__((aligned(16))) uint8_t XS0[kXsBytes];
@@ -646,7 +648,6 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     __shared__ __attribute__((aligned(16))) uint8_t WE0[kWsBytes];
     __shared__ __attribute__((aligned(16))) uint8_t WE1[kWsBytes];
     __shared__ int32_t rows_s[GATHER ? BM : 1];
-    __shared__ __attribute__((aligned(16))) float sgn[64];
     uint8_t *const XSb[2] = {XS0, XS1};
     uint8_t *const WEb[2] = {WE0, WE1};
     fill_sign_table(sgn);
@@ -765,14 +766,20 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
         *reinterpret_cast<uint4 *>(WEb[buf] + nl * 128 + ((p ^ sw) * 16)) = e;
     };
 
+    // Accumulators in AGPRs: the empty asm with an AGPR constraint makes the
+    // compiler select the AGPR form of the MFMA (left alone, it keeps them in
+    // VGPRs, where the MFMAs and the W_eff builds contend for the same
+    // register file and barely overlap).
     f32x16 acc[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[mb][nb][v] = 0.0f;
+            asm volatile("" : "+a"(acc[mb][nb]));
+        }
 
     const int frow = lane & 31;
     const int fsw = (frow >> 1) & 7;
@@ -789,9 +796,11 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
             B[nb] = *reinterpret_cast<const bf16x8 *>(base + nb * 32 * 128);
     };
 
-    // ---- prologue: x(0) copy, W(0) loaded and built into WE0, W(1) loaded
+    // ---- prologue: x(0), x(1) copies; W(0) loaded and built into WE0; W(1)
+    // loaded; the k-block 0 fragments of step 0 read
     WRaw8 wr;
     dma_x(0, 0);
+    dma_x(T > 1 ? 1 : 0, 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         load_w(wr, i, 0);
@@ -802,41 +811,52 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    bf16x8 A[2][4], B[2][2];
+    read_a(A[0], 0, 0);
+    read_b(B[0], 0, 0);
 
-    // Per step t: copy x(t+1) into buffer nxt; run the 32 MFMAs of step t
-    // from buffers cur; after every 8 MFMAs form one group of W_eff(t+1)
-    // (into WE nxt) from the registers and refill those registers with the
-    // same group of W(t+2), one step ahead.
+    // Step t (x(t) in XS cur, W_eff(t) in WE cur, k-block 0 fragments in
+    // registers): k-blocks 0..2 read the next k-block's fragments and run
+    // their MFMAs; after every k-block one group of W_eff(t+1) is formed
+    // (into WE nxt) and its registers refilled with W(t+2).  Then, with every
+    // read of buffer cur done, the barrier; after it, x(t+2) is copied into
+    // XS cur, step t+1's k-block 0 fragments are read, and step t's last 8
+    // MFMAs (k-block 3, from registers) cover that transition.
+    auto mfma_kb = [&](int kb) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[kb & 1][nb], acc[mb][nb], 0,
+                                                                      0, 0);
+    };
     auto step = [&](int t, auto cur_c) {
         constexpr int cur = decltype(cur_c)::value;
         constexpr int nxt = 1 - cur;
-        const int t1 = t + 1 < T ? t + 1 : T - 1;
         const int t2 = t + 2 < T ? t + 2 : T - 1;
-        dma_x(t1, nxt);  // 4 copies
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 A[2][4], B[2][2];
-        read_a(A[0], cur, 0);
-        read_b(B[0], cur, 0);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (kb < 3) {
-                read_a(A[(kb + 1) & 1], cur, kb + 1);
-                read_b(B[(kb + 1) & 1], cur, kb + 1);
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[kb & 1][nb], acc[mb][nb],
-                                                                          0, 0, 0);
+        for (int kb = 0; kb < 3; ++kb) {
+            read_a(A[(kb + 1) & 1], cur, kb + 1);
+            read_b(B[(kb + 1) & 1], cur, kb + 1);
+            mfma_kb(kb);
             build_store(wr, kb, nxt);
             load_w(wr, kb, t2);  // 2 loads
             __builtin_amdgcn_sched_barrier(0);
         }
-        // x(t+1) has landed (the 8 W loads issued after it may be in
-        // flight) and W_eff(t+1) is written: then all waves may use buffer nxt
+        build_store(wr, 3, nxt);
+        load_w(wr, 3, t2);
+        __builtin_amdgcn_sched_barrier(0);
+        // x(t+1) has landed (the 8 W loads issued after it may be in flight),
+        // W_eff(t+1) is written and this wave's reads of buffer cur are done
         wait_vmcnt_lgkm0<8>();
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        dma_x(t2, cur);  // 4 copies: x(t+2)
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(A[0], nxt, 0);  // past the last step: valid data, unused
+        read_b(B[0], nxt, 0);
+        mfma_kb(3);
+        __builtin_amdgcn_sched_barrier(0);
     };
     int t = 0;
     for (; t + 1 < T; t += 2) {
@@ -845,6 +865,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     }
     if (t < T)
         step(t, std::integral_constant<int, 0>{});
+    // the last step's copy of x (unused) must land before the workgroup's LDS
+    // is released
+    __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
         // fp32 partials in accumulator order: [split][tile][wave][mb][nb][quarter][lane][4]
