@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the vendor-library reference points (read stream, plain GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     p.add_argument("--kernel-reps", type=int, default=125,
                    help="graph replays per kernel for the per-kernel timings (lower it under a profiler)")
@@ -310,21 +312,78 @@ def run_grouped(torch, bd, synth, reps=10):
                                                 P(signs.data_ptr()), P(alpha.data_ptr()), bd.BD_ALPHA_ROW, N, K,
                                                 P(y.data_ptr()), P(ws.data_ptr()), nws, P(stream.cuda_stream)))
 
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps * 1e3
+    def timed():
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    us = timed()
     flop = 2.0 * M * N * K
     tf = flop / us / 1e6
-    log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s")
+    ids_shuffled = ids
+    ids = torch.sort(ids_shuffled).values.contiguous()  # the same tokens, pre-sorted by variant
+    us_sorted = timed()
+    log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s "
+        f"(ids pre-sorted: {us_sorted:.1f} us)")
     return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
-            "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+            "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+            "us_ids_presorted": round(us_sorted, 1)}
+
+
+# ----------------------------------------------------------------- context
+
+
+def run_context(torch, reps=20):
+    """Reference points measured with the vendor libraries through torch (not
+    the product path): a copy over 16 rotating buffers the size of the decode
+    layer's weights (torch copy_, read + write), and a plain bf16 GEMM without
+    deltas (torch.mm -> hipBLASLt) on the four prefill shapes at m = 2048."""
+    dev = torch.device("cuda")
+    out = {}
+    n = (34 << 20) // 2
+    src = [torch.randn(n, device=dev, dtype=torch.bfloat16) for _ in range(16)]
+    dst = torch.empty_like(src[0])
+    for i in range(16):
+        dst.copy_(src[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(4 * reps):
+        dst.copy_(src[i % 16])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (4 * reps) * 1e3
+    out["copy_34MiB"] = {"us": round(us, 2), "GB/s": round(4 * n / us / 1e3, 1),
+                         "frac_hbm": round(4 * n / us / 1e3 / HBM_PEAK_GBS, 4), "kernel": "torch copy_ (read + write)"}
+    log(f"context: copy of 34 MiB (torch copy_, read + write) {us:.2f} us, {4 * n / us / 1e3:.1f} GB/s")
+    del src, dst
+    gemm = {}
+    for label, N, K in PREFILL_SHAPES:
+        x = torch.randn((PREFILL_M, K), device=dev, dtype=torch.bfloat16)
+        ws = [torch.randn((N, K), device=dev, dtype=torch.bfloat16) for _ in range(2)]
+        y = torch.empty((PREFILL_M, N), device=dev, dtype=torch.bfloat16)
+        for i in range(3):
+            torch.mm(x, ws[i % 2].t(), out=y)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            torch.mm(x, ws[i % 2].t(), out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        tf = 2.0 * PREFILL_M * N * K / us / 1e6
+        gemm[label] = {"us": round(us, 1), "TFLOP/s": round(tf, 1)}
+        log(f"context: plain bf16 GEMM (torch.mm) {label} [{N},{K}] m={PREFILL_M}: {us:.1f} us, {tf:.1f} TFLOP/s")
+        del x, ws, y
+    out["plain_gemm_m2048"] = gemm
+    return out
 
 
 # ---------------------------------------------------------------- 70B stack
@@ -522,6 +581,20 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command):
                                  "algorithmic_bytes": algo[entry], "ratio": round(total / algo[entry], 4)}
         lines.append(f"{entry:18s} {' + '.join(names)[:46]:46s} {n:4d} {tf:12.0f} {tw:12.0f} {total:12.0f} "
                      f"{algo[entry]:13d} {total / algo[entry]:6.3f}")
+    # grouped layer (14 variants sharing one 8192 x 8192 W_base, 4096 tokens), if in the runs
+    rx = re.compile(r"gemm_tiles_w8<false, true, false>")
+    fv = [v for nm, _, v in fetch if rx.search(nm)]
+    wv = [v for nm, _, v in write if rx.search(nm)]
+    if fv and wv:
+        n_ = k_ = 8192
+        tf_, tw_ = statistics.median(fv) * f_fetch, statistics.median(wv) * f_write
+        w_bytes, s_bytes, x_bytes = n_ * k_ * 2, 14 * n_ * k_ // 8, 4096 * k_ * 2
+        out["grouped"] = {"kernel": "gemm_tiles_w8<false, true, false>", "fetch_bytes": round(tf_),
+                          "write_bytes": round(tw_), "w_base_bytes": w_bytes, "signs_bytes": s_bytes,
+                          "x_bytes": x_bytes, "fetch_over_w_base": round(tf_ / w_bytes, 3)}
+        lines.append(f"grouped GEMM (14 variants, 4096 tokens): fetched {tf_:.0f} B, written {tw_:.0f} B per launch; "
+                     f"W_base {w_bytes} B, all 14 sign sets {s_bytes} B, x {x_bytes} B; fetched / W_base = "
+                     f"{tf_ / w_bytes:.3f} (a launch per variant would fetch W_base 14 times)")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
@@ -610,6 +683,7 @@ def main():
 
     prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
     grouped = None if args.no_grouped else run_grouped(torch, bd, synth)
+    context = None if args.no_context else run_context(torch)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args.cpu_seconds)
 
     line = {
@@ -633,6 +707,7 @@ def main():
         "kernels": kernels,
         "prefill": prefill,
         "grouped": grouped,
+        "context": context,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
