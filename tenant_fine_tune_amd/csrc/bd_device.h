@@ -88,6 +88,20 @@ __device__ __forceinline__ uint4 weff8(const float *sgn, uint32_t b, uint4 w, fl
     return e;
 }
 
+// Streaming (nontemporal) 16-byte global load / store and byte load: data
+// touched once, kept out of the way of the caches.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream8(const uint8_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream16(void *p, uint4 v)
+{
+    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, static_cast<u32x4 *>(p));
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer offset of a row that does not exist: beyond every tensor (all

@@ -49,14 +49,16 @@ template <bool FT_F32>
 __device__ __forceinline__ void load_group(const uint4 *wb, const void *w_ft, int64_t r, int64_t C, int64_t g,
                                            uint4 &b, float (&ft)[8])
 {
-    b = wb[g];
+    b = ld_stream16(wb + g);
     if constexpr (FT_F32) {
-        const float4 *f = reinterpret_cast<const float4 *>(static_cast<const float *>(w_ft) + r * C);
-        const float4 a0 = f[2 * g], a1 = f[2 * g + 1];
-        ft[0] = a0.x; ft[1] = a0.y; ft[2] = a0.z; ft[3] = a0.w;
-        ft[4] = a1.x; ft[5] = a1.y; ft[6] = a1.z; ft[7] = a1.w;
+        const uint4 *f = reinterpret_cast<const uint4 *>(static_cast<const float *>(w_ft) + r * C);
+        const uint4 a0 = ld_stream16(f + 2 * g), a1 = ld_stream16(f + 2 * g + 1);
+        ft[0] = __uint_as_float(a0.x); ft[1] = __uint_as_float(a0.y);
+        ft[2] = __uint_as_float(a0.z); ft[3] = __uint_as_float(a0.w);
+        ft[4] = __uint_as_float(a1.x); ft[5] = __uint_as_float(a1.y);
+        ft[6] = __uint_as_float(a1.z); ft[7] = __uint_as_float(a1.w);
     } else {
-        const uint4 f = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w_ft) + r * C)[g];
+        const uint4 f = ld_stream16(reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w_ft) + r * C) + g);
         ft[0] = lo_f32(f.x); ft[1] = hi_f32(f.x); ft[2] = lo_f32(f.y); ft[3] = hi_f32(f.y);
         ft[4] = lo_f32(f.z); ft[5] = hi_f32(f.z); ft[6] = lo_f32(f.w); ft[7] = hi_f32(f.w);
     }
