@@ -9,29 +9,27 @@
 // serves in one launch.
 //
 // Tile: 256 tokens x 256 output features per workgroup, K stepped by 64.
-// Two kernels share the tiling: gemm_tiles_fast (d_in a multiple of 64) and
-// gemm_tiles (any d_in that is a multiple of 8, with a masked K tail).
-// Four waves; wave w owns output features [64w, 64w+64) of the tile for all
-// 256 tokens (8 x 2 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
-// accumulators per lane).  Pipeline, per K step t:
-//  - activations: the tile of step t+1 is copied HBM -> LDS by direct-to-LDS
-//    loads (no VGPRs, no LDS write instructions) into the other of two LDS
-//    buffers; rows are stored unpadded with the 16-byte chunks of row r
-//    permuted by c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 32
-//    consecutive rows spread over all banks;
-//  - weights: each wave loads its own 64 x 64 slice of W_base and the sign
-//    bytes two steps ahead (general kernel: into VGPRs, in the MFMA B-operand
-//    layout, lane l: feature l%32, 8 consecutive k; fast kernel: into LDS by
-//    direct-to-LDS loads, read back in that layout); while the MFMAs of step t
-//    run, the VALU forms step t+1's W_eff = bf16(W_base + +-alpha) fragments
-//    in VGPRs, so each weight is rebuilt exactly once per workgroup and W_eff
-//    itself is never written anywhere;
-//  - one barrier per step.  Every load address is clamped into its tensor
-//    (tail rows/columns read valid data whose results are discarded or
-//    multiplied by zero), so no load sits under a branch.
-// Workgroups are remapped so that the ones sharing an output-feature tile run
-// on the same XCD (blocks are dealt round-robin over the 8 XCDs), so each
-// W_base tile is fetched into one L2 once.
+// Two kernels share the tiling:
+//  - gemm_tiles_w8 (d_in a multiple of 64: every 70B-class shape), eight
+//    waves; its own comment below gives the pipeline;
+//  - gemm_tiles (any d_in that is a multiple of 8, with a masked K tail),
+//    four waves; wave w owns output features [64w, 64w+64) of the tile for
+//    all 256 tokens (8 x 2 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
+//    accumulators per lane).  Per K step t: the activation tile of step t+1
+//    is copied HBM -> LDS by direct-to-LDS loads (no VGPRs, no LDS write
+//    instructions) into the other of two LDS buffers; each wave loads its
+//    own 64 x 64 slice of W_base and the sign bytes two steps ahead into
+//    VGPRs, in the MFMA B-operand layout (lane l: feature l%32, 8 consecutive
+//    k), and while the MFMAs of step t run the VALU forms step t+1's
+//    W_eff = bf16(W_base + +-alpha) fragments in VGPRs; one barrier per step.
+// In both, activation rows sit in LDS unpadded with the 16-byte chunks of row
+// r permuted by c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 32
+// consecutive rows spread over all banks; each weight is rebuilt exactly once
+// per workgroup and W_eff is never written to HBM; out-of-range loads use
+// buffer offsets past the end (they read zero), so no load sits under a
+// branch.  Workgroups are remapped so that the ones sharing an
+// output-feature tile run on the same XCD (blocks are dealt round-robin over
+// the 8 XCDs), so each W_base tile is fetched into one L2 once.
 #include <type_traits>
 
 #include "bd_device.h"
@@ -43,6 +41,7 @@ namespace {
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
+constexpr int64_t kCus = 256;
 
 __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t nb)
 {
@@ -295,323 +294,9 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
 }
 
 // ---------------------------------------------------------------------------
-// Fast path (d_in a multiple of 64): the W_base slices and sign bytes of the
-// next steps are also copied HBM -> LDS by direct-to-LDS loads, two steps
-// ahead, instead of being staged in VGPRs.  Each wave copies and reads only
-// its own 64 feature rows, so the copies need no barrier, only the wave's
-// own wait.  The registers this frees hold a second set of A fragments, so
-// the LDS reads of k block kb+1 are in flight while the MFMAs of kb run.
-// LDS (static, 133 KB): x tiles 2 x 32 KB, W tiles 2 x 32 KB, sign tiles
-// 2 x 2 KB, gathered rows 1 KB.
+// LDS tiles of the eight-wave kernel: x 2 x 32 KB, W_eff 2 x 32 KB.
 constexpr int kXsBytes = BM * BK * 2;                    // 32768
 constexpr int kWsBytes = BN * BK * 2;                    // 32768
-constexpr int kSsBytes = BN * BK / 8;                    // 2048
-
-template <bool PER_MATRIX, bool GATHER, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
-                     const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
-                     int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
-                     const int32_t *__restrict__ table, int32_t n_variants,
-                     int64_t k_split, float *__restrict__ partial)
-{
-    // separate objects, so the compiler can tell a read of one buffer from
-    // a copy in flight into another and does not wait for every copy
-    __shared__ __attribute__((aligned(16))) uint8_t XS0[kXsBytes], XS1[kXsBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t WS0[kWsBytes], WS1[kWsBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t SS0[kSsBytes], SS1[kSsBytes];
-    __shared__ int32_t rows_s[BM];
-    uint8_t *const XSb[2] = {XS0, XS1};
-    uint8_t *const WSb[2] = {WS0, WS1};
-    uint8_t *const SSb[2] = {SS0, SS1};
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
-    const int hi = lane >> 5;
-    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t mt = b % m_tiles, nt = b / m_tiles;
-    const int64_t n0 = nt * BN;
-
-    int64_t m0 = mt * BM;
-    const uint8_t *signs = signs_all;
-    const float *alpha = alpha_all;
-    if constexpr (GATHER) {
-        const int32_t total = table[0];
-        if (mt >= total)
-            return;
-        const int32_t *perm = table + 4;
-        const int32_t *tile_v = perm + M;
-        const int32_t *tile_row0 = tile_v + m_tiles;
-        const int32_t *tile_rows = tile_row0 + m_tiles;
-        const int v = tile_v[mt];
-        const int row0 = tile_row0[mt], nrows = tile_rows[mt];
-        for (int i = threadIdx.x; i < BM; i += kThreads)
-            rows_s[i] = i < nrows ? perm[row0 + i] : -1;
-        __syncthreads();
-        if (v >= n_variants) {
-            for (int i = 0; i < nrows; ++i) {
-                const int64_t tok = rows_s[i];
-                for (int64_t j = n0 + threadIdx.x; j < min(N, n0 + BN); j += kThreads)
-                    y[tok * N + j] = 0;
-            }
-            return;
-        }
-        signs = signs_all + (int64_t)v * N * (K >> 3);
-        alpha = PER_MATRIX ? alpha_all + v : alpha_all + (int64_t)v * N;
-        m0 = 0;
-    }
-
-    const int64_t G = K >> 3;
-    // split-K: blockIdx.y takes columns [k_begin, k_begin + k_split) of K
-    const int64_t k_begin = (int64_t)blockIdx.y * k_split;
-    const int T = (int)((min(K, k_begin + k_split) - k_begin) / BK);
-    const uint32_t kx0 = (uint32_t)(k_begin * 2);   // byte offset of k_begin in a bf16 row
-    const uint32_t ks0 = (uint32_t)(k_begin / 8);   // byte offset of k_begin in a sign row
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, M * K * 2);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, N * K * 2);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, N * G);
-
-    // DMA instruction j of a wave covers 8 rows (8j .. 8j+7 of its 64); lane
-    // l writes chunk position l&7 of row 8j + l/8, i.e. logical chunk
-    // (l&7) ^ ((row >> 1) & 7), which only depends on the parity of j.
-    const int p = lane & 7;
-    uint32_t xoff[GATHER ? 8 : 2], woff[2];
-#pragma unroll
-    for (int j = 0; j < (GATHER ? 8 : 2); ++j) {
-        const int row = wave * 64 + j * 8 + (lane >> 3);
-        const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
-        int64_t tok;
-        if constexpr (GATHER)
-            tok = rows_s[row];
-        else
-            tok = m0 + row;
-        xoff[j] = (tok < 0 || tok >= M) ? kInvalidOffset : (uint32_t)((tok * K + c * 8) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
-        const int64_t n = n0 + wave * 64 + j * 8 + (lane >> 3);
-        woff[j] = n < N ? (uint32_t)((n * K + c * 8) * 2) : kInvalidOffset;
-    }
-    // sign tile: instruction j covers rows 32j .. 32j+31, lane l -> row
-    // 32j + l/2, dword l&1 of the row's 8 bytes
-    uint32_t soff;
-    {
-        const int64_t n = n0 + wave * 64 + (lane >> 1);
-        soff = n < N ? (uint32_t)(n * G + (lane & 1) * 4) : kInvalidOffset;
-    }
-    const uint32_t xstride = (uint32_t)(8 * K * 2);   // 8 rows further (dense)
-    const uint32_t xstride_w = xstride;               // same for W rows
-    const uint32_t sstride = (uint32_t)(32 * G);      // 32 rows further
-
-    // Per-step offsets (and the uniform part of the row offset) go in the
-    // scalar offset: with d_in a multiple of 64 a valid row never steps past
-    // its tensor, and an invalid row (offset >= 2^31) stays out of range.
-    auto dma_x = [&](int t, int buf) {
-        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t vo, so;
-            if constexpr (GATHER) {
-                vo = xoff[j];
-                so = kb;
-            } else {
-                vo = xoff[j & 1];
-                so = (uint32_t)(j >> 1) * 2 * xstride + kb;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 8 + j) * 1024), 16,
-                                                     vo, so, 0, 0);
-        }
-    };
-    auto dma_w = [&](int t, int buf) {
-        const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(WSb[buf] + wave * 8192 + j * 1024), 16,
-                                                     woff[j & 1], (uint32_t)(j >> 1) * 2 * xstride_w + kb, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(SSb[buf] + wave * 512 + j * 256), 4,
-                                                     soff, (uint32_t)j * sstride + ks0 + (uint32_t)(t * 8), 0, 0);
-    };
-
-    float a[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t n = n0 + wave * 64 + nb * 32 + (lane & 31);
-        a[nb] = PER_MATRIX ? alpha[0] : (n < N ? alpha[n] : 0.0f);
-    }
-    // this lane's B rows inside the wave's W tile, and their swizzle
-    const int brow = lane & 31;
-    const int bsw = (brow >> 1) & 7;  // same for brow and brow + 32
-    struct Raw {
-        uint4 w[2][4];
-        uint2 s[2];
-    };
-    auto read_w = [&](Raw &r, int buf) {
-        const uint8_t *wt = WSb[buf] + wave * 8192;
-        const uint8_t *st = SSb[buf] + wave * 512;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int row = nb * 32 + brow;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                r.w[nb][kb] = *reinterpret_cast<const uint4 *>(wt + row * 128 + (((kb * 2 + hi) ^ bsw) * 16));
-            r.s[nb] = *reinterpret_cast<const uint2 *>(st + row * 8);
-        }
-    };
-    auto build = [&](bf16x8 (&B)[2][4], const Raw &r, int nb, int kb) {
-        const int byte_i = kb * 2 + hi;
-        const uint32_t word = byte_i < 4 ? r.s[nb].x : r.s[nb].y;
-        const uint32_t byte = (word >> (8 * (byte_i & 3))) & 0xFFu;
-        B[nb][kb] = __builtin_bit_cast(bf16x8, weff_group(r.w[nb][kb], byte, a[nb]));
-    };
-
-    f32x16 acc[8][2];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[mb][nb][v] = 0.0f;
-
-    const int arow = lane & 31;
-    const int asw = (arow >> 1) & 7;
-    auto read_a = [&](bf16x8 (&A)[8], int buf, int kb) {
-        const uint8_t *base = XSb[buf] + arow * 128 + (((kb * 2 + hi) ^ asw) * 16);
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-            A[mb] = *reinterpret_cast<const bf16x8 *>(base + mb * 32 * 128);
-    };
-
-    // ---- prologue
-    bf16x8 B[2][2][4];
-    {
-        dma_x(0, 0);
-        dma_w(0, 0);
-        dma_w(T > 1 ? 1 : 0, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        Raw r;
-        read_w(r, 0);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                build(B[0], r, nb, kb);
-    }
-
-    auto step = [&](int t, auto cur_c) {
-        constexpr int cur = decltype(cur_c)::value;
-        constexpr int nxt = 1 - cur;
-        const int t1 = t + 1 < T ? t + 1 : T - 1;
-        const int t2 = t + 2 < T ? t + 2 : T - 1;
-        // Issue order matters: the explicit vmcnt waits below count the ops
-        // issued after a given copy, so the groups are kept in order.
-        dma_x(t1, nxt);   // 8 ops
-        __builtin_amdgcn_sched_barrier(0);
-        dma_w(t2, cur);   // 10 ops; W tile buffer `cur` held W(t), already built into B[cur]
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<18>();  // this wave's W(t+1) tile has landed (8 + 10 ops issued since)
-        Raw r;
-        read_w(r, nxt);
-        bf16x8 A[2][8];
-        read_a(A[0], cur, 0);
-        // 64 slots, each one MFMA of step t; every second slot also forms one
-        // packed W_eff pair of step t+1 (32 pairs: 2 feature blocks x 4 k
-        // blocks x 4 pairs).  sched_barrier between slots keeps this order,
-        // so the VALU work issues while the matrix core is busy.
-        uint32_t Bn[2][4][4];
-        uint32_t sbyte = 0;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (kb < 3)
-                read_a(A[(kb + 1) & 1], cur, kb + 1);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int slot = kb * 16 + mb * 2 + nb;
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[cur][nb][kb], acc[mb][nb],
-                                                                          0, 0, 0);
-                    if (slot & 1) {
-                        const int q = slot >> 1;  // pair 0..31
-                        const int bnb = q >> 4, bkb = (q >> 2) & 3, pr = q & 3;
-                        if (pr == 0) {
-                            const int byte_i = bkb * 2 + hi;
-                            const uint32_t word = byte_i < 4 ? r.s[bnb].x : r.s[bnb].y;
-                            sbyte = (word >> (8 * (byte_i & 3))) & 0xFFu;
-                        }
-                        const uint4 &w = r.w[bnb][bkb];
-                        const uint32_t wv = pr == 0 ? w.x : pr == 1 ? w.y : pr == 2 ? w.z : w.w;
-                        Bn[bnb][bkb][pr] = weff_pair(wv, sbyte, 2 * pr, a[bnb]);
-                        // pin the pair here: without this, IR code sinking moves
-                        // every build down to its use after the last MFMA
-                        asm volatile("" : "+v"(Bn[bnb][bkb][pr]));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                B[nxt][nb][kb] = __builtin_bit_cast(bf16x8, make_uint4(Bn[nb][kb][0], Bn[nb][kb][1], Bn[nb][kb][2],
-                                                                       Bn[nb][kb][3]));
-        __builtin_amdgcn_sched_barrier(0);
-        // x(t+1) has landed (W(t+2) may stay in flight) and this wave's LDS
-        // reads are done; then a bare barrier: __syncthreads()' fence would
-        // also wait for the W(t+2) copies, which nobody else reads.
-        wait_vmcnt_lgkm0<10>();
-        __builtin_amdgcn_s_barrier();
-    };
-    int t = 0;
-    for (; t + 1 < T; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        step(t + 1, std::integral_constant<int, 1>{});
-    }
-    if (t < T)
-        step(t, std::integral_constant<int, 0>{});
-
-    if constexpr (SPLIT) {
-        // split-K: fp32 partial sums in accumulator order, 1 KB per (wave, mb,
-        // nb, quarter) chunk, reduced in split order by splitk_reduce
-        const int64_t tile = nt * m_tiles + mt;
-        const int64_t tiles = (int64_t)gridDim.x;
-        float *base = partial + (((int64_t)blockIdx.y * tiles + tile) * 4 + wave) * (8 * 2 * 4 * 256);
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4 *>(base + ((mb * 2 + nb) * 4 + q) * 256 + lane * 4) =
-                        make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
-                                    acc[mb][nb][4 * q + 3]);
-    } else {
-        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, M * N * 2);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int64_t j = n0 + wave * 64 + nb * 32 + (lane & 31);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int i = mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-                    int64_t tok;
-                    if constexpr (GATHER)
-                        tok = rows_s[i];
-                    else
-                        tok = m0 + i < M ? m0 + i : -1;
-                    const uint32_t off = (tok >= 0 && j < N) ? (uint32_t)((tok * N + j) * 2) : kInvalidOffset;
-                    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(acc[mb][nb][v]), ry, off, 0, 0);
-                }
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Eight-wave variant (d_in a multiple of 64): two waves per SIMD, so one
@@ -619,7 +304,7 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
 // Wave (wm, wn) = (wave / 4, wave % 4) owns output rows wm*128 .. +127 and
 // features wn*64 .. +63 of the 256 x 256 tile (4 x 2 MFMA tiles of 32 x 32,
 // 128 accumulators, so two waves fit the register file).  Per K step of 64:
-//  - x tile: direct-to-LDS copies one step ahead, as in gemm_tiles_fast;
+//  - x tile: direct-to-LDS copies one step ahead, into two LDS buffers;
 //  - W_base: each wave loads the 32 feature rows 32*wave .. +31 of the tile
 //    straight into VGPRs two steps ahead (1 KB per instruction: 8 rows x 128
 //    contiguous bytes) with their sign bytes, forms W_eff = bf16(W_base +
@@ -629,7 +314,6 @@ void gemm_tiles_fast(const uint16_t *__restrict__ x, int64_t M, const uint16_t *
 //    there.  W_eff is built exactly once per workgroup and never leaves LDS.
 //  - one barrier per step.
 constexpr int kThreads8 = 512;
-constexpr bool kUseW8 = true;
 
 template <bool PER_MATRIX, bool GATHER, bool SPLIT>
 __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -637,7 +321,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
                    const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
                    int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
                    const int32_t *__restrict__ table, int32_t n_variants,
-                   int64_t k_split, float *__restrict__ partial)
+                   int64_t k_split, float *__restrict__ partial, int64_t tile0)
 {
     // sign table first (at LDS address 0 its lookups need no base)
     __shared__ __attribute__((aligned(16))) float sgn[64];
@@ -657,7 +341,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int hi = lane >> 5;
-    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+    // this launch covers tiles tile0 .. tile0 + gridDim.x - 1
+    const int64_t local = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t b = tile0 + local;
     const int64_t mt = b % m_tiles, nt = b / m_tiles;
     const int64_t n0 = nt * BN;
 
@@ -870,10 +556,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
-        // fp32 partials in accumulator order: [split][tile][wave][mb][nb][quarter][lane][4]
-        const int64_t tile = nt * m_tiles + mt;
+        // fp32 partials in accumulator order: [split][tile - tile0][wave][mb][nb][quarter][lane][4]
         const int64_t tiles = (int64_t)gridDim.x;
-        float *base = partial + (((int64_t)blockIdx.y * tiles + tile) * 8 + wave) * (4 * 2 * 4 * 256);
+        float *base = partial + (((int64_t)blockIdx.y * tiles + local) * 8 + wave) * (4 * 2 * 4 * 256);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -906,21 +591,19 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     }
 }
 
-// Sum the split-K partials of gemm_tiles_fast in split order (fixed, so the
-// result is deterministic) and write bf16 y.  One thread per 4 accumulators.
-// W8: partials of gemm_tiles_w8 (8 waves x 4 x 2 MFMA tiles) rather than of
-// gemm_tiles_fast (4 waves x 8 x 2); the same 256 x 256 floats per tile.
-template <bool W8>
+// Sum the split-K partials of gemm_tiles_w8 in split order (fixed, so the
+// result is deterministic) and write bf16 y.  One thread per 4 accumulators;
+// partial tile i holds output tile tile0 + i.
 __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ partial, int splits, int64_t tiles,
-                                                     int64_t m_tiles, int64_t M, int64_t N,
+                                                     int64_t tile0, int64_t m_tiles, int64_t M, int64_t N,
                                                      uint16_t *__restrict__ y)
 {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * 256 chunks * 64 lanes
     const int lane = (int)(gid & 63);
     const int64_t chunk = gid >> 6;
     const int q = (int)(chunk & 3), nb = (int)((chunk >> 2) & 1);
-    const int mb = W8 ? (int)((chunk >> 3) & 3) : (int)((chunk >> 3) & 7);
-    const int wave = W8 ? (int)((chunk >> 5) & 7) : (int)((chunk >> 6) & 3);
+    const int mb = (int)((chunk >> 3) & 3);
+    const int wave = (int)((chunk >> 5) & 7);
     const int64_t tile = chunk >> 8;
     if (tile >= tiles)
         return;
@@ -934,9 +617,9 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ p
         s.z += v.z;
         s.w += v.w;
     }
-    const int64_t mt = tile % m_tiles, nt = tile / m_tiles;
-    const int64_t j = nt * BN + (W8 ? (wave & 3) * 64 : wave * 64) + nb * 32 + (lane & 31);
-    const int64_t i0 = mt * BM + (W8 ? (wave >> 2) * 128 : 0) + mb * 32 + 8 * q + 4 * (lane >> 5);
+    const int64_t mt = (tile0 + tile) % m_tiles, nt = (tile0 + tile) / m_tiles;
+    const int64_t j = nt * BN + (wave & 3) * 64 + nb * 32 + (lane & 31);
+    const int64_t i0 = mt * BM + (wave >> 2) * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
     if (j >= N)
         return;
     const float v4[4] = {s.x, s.y, s.z, s.w};
@@ -1030,76 +713,76 @@ hipError_t launch_tiles2(const uint16_t *x, int64_t m, const uint16_t *w_base, c
     return hipGetLastError();
 }
 
+// One launch of gemm_tiles_w8 over tiles tile0 .. tile0 + count - 1, K cut
+// into `splits` ranges (partials into `partial`, then summed by
+// splitk_reduce) or unsplit.
 template <bool GATHER>
-hipError_t launch_tiles(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
-                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
-                        int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s,
-                        float *partial = nullptr, int splits = 1)
+hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
+                     const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
+                     int64_t m_tiles, const int32_t *table, int32_t n_variants, int64_t tile0, int64_t count,
+                     int splits, float *partial, hipStream_t s)
 {
-    if (d_in % 64 != 0)
-        return launch_tiles2<GATHER, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, table,
-                                            n_variants, s);
-    const int64_t n_tiles = (d_out + BN - 1) / BN;
     const int64_t k_split = splits > 1 ? gemm_k_split(d_in, splits) : d_in;
     const int used = (int)((d_in + k_split - 1) / k_split);
     float *part = used > 1 ? partial : nullptr;
-    const dim3 grid((unsigned)(m_tiles * n_tiles), (unsigned)used);
-#define BD_FAST(PM, SP)                                                                                    \
-    hipLaunchKernelGGL((gemm_tiles_fast<PM, GATHER, SP>), grid, dim3(kThreads), 0, s, x, m, w_base, signs, alpha, \
-                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part)
+    const dim3 grid((unsigned)count, (unsigned)used);
 #define BD_W8(PM, SP)                                                                                      \
     hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs, alpha, \
-                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part)
-    if (kUseW8) {
-        if (per_matrix) {
-            if (part) BD_W8(true, true);
-            else BD_W8(true, false);
-        } else {
-            if (part) BD_W8(false, true);
-            else BD_W8(false, false);
-        }
+                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0)
+    if (per_matrix) {
+        if (part) BD_W8(true, true);
+        else BD_W8(true, false);
     } else {
-        if (per_matrix) {
-            if (part) BD_FAST(true, true);
-            else BD_FAST(true, false);
-        } else {
-            if (part) BD_FAST(false, true);
-            else BD_FAST(false, false);
-        }
+        if (part) BD_W8(false, true);
+        else BD_W8(false, false);
     }
-#undef BD_FAST
 #undef BD_W8
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || part == nullptr)
         return e;
-    const int64_t tiles = m_tiles * n_tiles;
-    const int64_t threads = tiles * 256 * 64;
-    if (kUseW8)
-        hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
-                           tiles, m_tiles, m, d_out, y);
-    else
-        hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
-                           tiles, m_tiles, m, d_out, y);
+    const int64_t threads = count * 256 * 64;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used, count,
+                       tile0, m_tiles, m, d_out, y);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Split-K: with few output tiles (small d_out or few tokens) the K loop is
-// cut into equal 64-aligned ranges so the grid covers the 256 CUs; each range
-// keeps at least 512 columns (8 steps) to amortise the pipeline fill.
-int gemm_splits(int64_t m, int64_t d_out, int64_t d_in)
+// How a dense prefill call is cut over the 256 CUs (one 256 x 256 tile per
+// CU at a time):
+//  - few tiles (under 192): the K loop of every tile is cut into equal
+//    64-aligned ranges so the grid covers the CUs; each range keeps at least
+//    512 columns (8 steps) to amortise the pipeline fill;
+//  - more tiles than CUs with a last partial wave of at most half the CUs:
+//    that wave's tiles run as a second launch with K cut in 2 (or 4, 8) so
+//    it fills the chip and ends sooner, when every range keeps at least 2048
+//    columns (the fixed cost of summing the partials is then repaid);
+//  - otherwise one unsplit launch.
+GemmPlan gemm_plan(int64_t m, int64_t d_out, int64_t d_in)
 {
+    GemmPlan p{1, 0, 1};
     if (d_in % 64 != 0)
-        return 1;
+        return p;
     const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
-    if (tiles >= 192)
-        return 1;
-    int sp = 1;
-    while (sp < 16 && tiles * sp < 256 && d_in / (2 * sp) >= 512)
-        sp *= 2;
-    const int64_t ks = gemm_k_split(d_in, sp);
-    return (int)((d_in + ks - 1) / ks);
+    if (tiles < 192) {
+        int sp = 1;
+        while (sp < 16 && tiles * sp < kCus && d_in / (2 * sp) >= 512)
+            sp *= 2;
+        const int64_t ks = gemm_k_split(d_in, sp);
+        p.splits = (int)((d_in + ks - 1) / ks);
+        return p;
+    }
+    const int64_t rem = tiles % kCus;
+    if (tiles > kCus && rem > 0 && 2 * rem <= kCus) {
+        int sp = 1;
+        while (sp < 8 && rem * 2 * sp <= kCus && d_in / (2 * sp) >= 2048)
+            sp *= 2;
+        if (sp > 1) {
+            p.tail = rem;
+            p.tail_splits = sp;
+        }
+    }
+    return p;
 }
 
 int64_t gemm_k_split(int64_t d_in, int splits)
@@ -1109,11 +792,14 @@ int64_t gemm_k_split(int64_t d_in, int splits)
 
 size_t gemm_workspace_bytes(int64_t m, int64_t d_out, int64_t d_in)
 {
-    const int sp = gemm_splits(m, d_out, d_in);
-    if (sp <= 1)
+    const GemmPlan p = gemm_plan(m, d_out, d_in);
+    const size_t tile = (size_t)BM * BN * sizeof(float);
+    if (p.tail > 0)
+        return (size_t)p.tail_splits * (size_t)p.tail * tile;
+    if (p.splits <= 1)
         return 0;
     const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
-    return (size_t)sp * (size_t)tiles * BM * BN * sizeof(float);
+    return (size_t)p.splits * (size_t)tiles * tile;
 }
 
 hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
@@ -1121,8 +807,21 @@ hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, con
                        uint16_t *y, void *workspace, hipStream_t s)
 {
     const int64_t m_tiles = (m + BM - 1) / BM;
-    return launch_tiles<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, s,
-                               static_cast<float *>(workspace), gemm_splits(m, d_out, d_in));
+    if (d_in % 64 != 0)
+        return launch_tiles2<false, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr,
+                                           0, s);
+    const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
+    const GemmPlan p = gemm_plan(m, d_out, d_in);
+    float *part = static_cast<float *>(workspace);
+    if (p.tail == 0)
+        return launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, 0,
+                                tiles, p.splits, part, s);
+    const hipError_t e = launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles,
+                                          nullptr, 0, 0, tiles - p.tail, 1, nullptr, s);
+    if (e != hipSuccess)
+        return e;
+    return launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0,
+                            tiles - p.tail, p.tail, p.tail_splits, part, s);
 }
 
 int64_t grouped_max_tiles(int64_t m, int32_t n_variants)
@@ -1145,7 +844,11 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    return launch_tiles<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, s);
+    if (d_in % 64 != 0)
+        return launch_tiles2<true, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace,
+                                          n_variants, s);
+    return launch_w8<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, 0,
+                           T * ((d_out + BN - 1) / BN), 1, nullptr, s);
 }
 
 }  // namespace bd

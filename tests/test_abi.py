@@ -101,13 +101,20 @@ def test_linear_validation(bd):
 
 
 def test_linear_split_k_workspace(bd):
-    """Prefill with few 256 x 256 output tiles splits K; the workspace holds
-    one fp32 256 x 256 partial per tile and split."""
+    """Prefill with few 256 x 256 output tiles splits K, and so does a last
+    partial wave of at most 128 tiles; the workspace holds one fp32 256 x 256
+    partial per split tile and range."""
     W = bd.lib.bitdelta_linear_workspace
     tile = 256 * 256 * 4
     assert W(16, 64, 4096) == 0                    # decode path
     assert W(2048, 8192, 8192) == 0                # 256 tiles fill the chip
-    assert W(2048, 28672, 8192) == 0
+    assert W(2048, 8192, 28672) == 0
+    assert W(2048, 28672, 8192) == 2 * 128 * tile  # 896 tiles: last 128 in 2 K ranges
+    assert W(4000, 4100, 4096) == 2 * 16 * tile    # 272 tiles: K/2 = 2048 is the floor
+    assert W(256, 256 * 264, 16384) == 8 * 8 * tile
+    assert W(4096, 6400, 8192) == 0                # last wave of 144 tiles: over half the CUs
+    assert W(4096, 4352, 2048) == 0                # K/2 = 1024: too short to repay the sum
+    assert W(512, 28672, 8192) == 0                # 224 tiles: one wave
     assert W(600, 64, 4096) == 8 * 3 * tile        # 3 tiles, K/8 = 512 per split
     assert W(2048, 1024, 8192) == 8 * 32 * tile    # 32 tiles x 8 splits = 256
     assert W(40, 1024, 8192) == 16 * 4 * tile      # capped at 16 splits

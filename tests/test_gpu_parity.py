@@ -222,6 +222,39 @@ def test_identity_prefill_split_k(bd, shape):
     assert same_bits_pm0(y, weff.T)
 
 
+@pytest.mark.parametrize("case", [((4100, 4096), 4000), ((4352, 8192), 4096)],
+                         ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
+def test_last_wave_split_dyadic_exact(bd, case):
+    """More tiles than CUs with a last partial wave (16 or 17 tiles of 272):
+    that wave runs as a second launch with K cut in ranges.  Exact-arithmetic
+    inputs: sampled output features, every one of the last tile column,
+    bit for bit; repeated calls give the same bits."""
+    (R, C), M = case
+    tile = 256 * 256 * 4
+    assert bd.lib.bitdelta_linear_workspace(M, R, C) >= 2 * 16 * tile
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=60 + M % 7)
+    xd, wd, sd, ad = bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])
+    y = host_bits(bd.linear(xd, wd, sd, ad))
+    rows = np.unique(np.concatenate([np.arange(4096, R), [0, 255, 256, 2047, 4095],
+                                     synth.u64(16, 0, 9100 + R) % np.uint64(R)]).astype(np.int64))
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0], rows=rows)
+    assert np.array_equal(synth.bf16_bits_to_f32(y[:, rows]).astype(np.float64), y64)
+    x2 = bf16_dev(synth.activations(M, C, seed=61, index=M))
+    assert torch.equal(bd.linear(x2, wd, sd, ad), bd.linear(x2, wd, sd, ad))
+
+
+def test_identity_last_wave_split(bd):
+    """x = I on 4100 x 4096 (272 tiles, the last 16 split in K): each y element
+    comes from one K range, the other adds zeros, so y = W_eff^T bit for bit."""
+    R, C = 4100, 4096
+    assert bd.lib.bitdelta_linear_workspace(C, R, C) > 0
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=13)
+    weff = oracle.reconstruct(w_base, so, ao)
+    eye = torch.eye(C, dtype=torch.bfloat16, device="cuda")
+    y = host_bits(bd.linear(eye, wd, sd, ad))
+    assert same_bits_pm0(y, weff.T)
+
+
 def test_zero_tokens_and_misaligned(bd):
     R, C = 64, 128
     w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=8)
