@@ -572,8 +572,13 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command):
         names, n = [], 0
         for pat in pats:
             rx = re.compile(pat)
-            fv = [v for nm, _, v in fetch if rx.search(nm)]
-            wv = [v for nm, _, v in write if rx.search(nm)]
+            # the decode step's dispatches: the grid seen most often (other
+            # calls of the same kernel, e.g. the grouped run's compresses,
+            # have other grids)
+            grids = [g for nm, g, _ in fetch if rx.search(nm)]
+            grid = max(set(grids), key=grids.count) if grids else None
+            fv = [v for nm, g, v in fetch if rx.search(nm) and g == grid]
+            wv = [v for nm, g, v in write if rx.search(nm) and g == grid]
             if not fv or not wv:
                 raise SystemExit(f"no dispatches of {pat} in the counter CSVs")
             tf += statistics.median(fv) * f_fetch
