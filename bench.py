@@ -34,6 +34,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -92,6 +93,9 @@ def parse():
                         "profiles/traffic.json and prints a table")
     p.add_argument("--summarize-trace", metavar="TRACE_CSV",
                    help="no GPU: per (kernel, grid) dispatch count and durations from a kernel_trace CSV")
+    p.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
+                   help="print MFMA busy, clock and VALU/LDS per MFMA of the prefill kernels from a "
+                        "rocprofv3 --pmc run of the MFMA counters, and exit")
     p.add_argument("--copy-mb", type=int, default=256, help="--copy-probe-mb of the counter runs")
     p.add_argument("--command", default="", help="command line recorded in profiles/traffic.json")
     return p.parse_args()
@@ -221,10 +225,16 @@ def run_decode(torch, bd, synth, steps, warmup, kernel_reps):
     kernels = {}
     for name, nbytes in ds.bytes.items():
         g = capture(torch, lambda s, name=name: [ds.launch(name, i, s) for i in range(SETS)])
-        reps = max(1, kernel_reps)
-        t, _ = time_graphs(torch, [g], reps, 4)
-        us = t / (reps * SETS) * 1e6
-        kernels[name] = {"us": round(us, 3), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+        # 5 repeats of reps / 5 replays: "us" is the average launch over all of
+        # them, next to the median and the min of the 5 repeat averages
+        reps = max(5, kernel_reps) // 5
+        rep_us = []
+        for r in range(5):
+            t, _ = time_graphs(torch, [g], reps, 4 if r == 0 else 1)
+            rep_us.append(t / (reps * SETS) * 1e6)
+        us = sum(rep_us) / 5
+        kernels[name] = {"us": round(us, 3), "us_median5": round(statistics.median(rep_us), 3),
+                         "us_min5": round(min(rep_us), 3), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
                          "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
         del g
     del step_graphs
@@ -260,17 +270,21 @@ def run_prefill(torch, bd, synth, reps=10):
         for i in range(3):
             call(i, stream)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            call(i, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        rep_us = []
+        for r in range(5):  # 5 repeats of reps calls
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                call(i, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rep_us.append(e0.elapsed_time(e1) / reps * 1e3)
+        us = sum(rep_us) / 5
         flop = 2.0 * PREFILL_M * N * K
         tf = flop / us / 1e6
-        out[label] = {"d_out": N, "d_in": K, "m": PREFILL_M, "us": round(us, 1), "TFLOP/s": round(tf, 1),
-                      "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+        out[label] = {"d_out": N, "d_in": K, "m": PREFILL_M, "us": round(us, 1),
+                      "us_median5": round(statistics.median(rep_us), 1), "us_min5": round(min(rep_us), 1),
+                      "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
         log(f"prefill {label} [{N},{K}] m={PREFILL_M}: {us:.1f} us, {tf:.1f} TFLOP/s")
         del sets, x, y
         torch.cuda.empty_cache()
@@ -642,6 +656,55 @@ def summarize_trace(trace_csv, gap=12):
               f"{statistics.median(v):9.2f} {min(v):9.2f}")
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU",
+                 "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(counter_csv, gap=12):
+    """MFMA use of the prefill / grouped kernels from a rocprofv3 --pmc run of
+    MFMA_COUNTERS (its CSV carries each dispatch's start and end).  Per run of
+    dispatches of one (kernel, grid): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
+    over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, the average graphics clock =
+    GRBM_GUI_ACTIVE / 8 over the dispatch's duration, and the MFMA rate these
+    two imply (1024 bf16 flop per SIMD per clock)."""
+    import csv
+
+    disp = {}
+    for r in csv.DictReader(open(counter_csv)):
+        name = _short(r["Kernel_Name"])
+        if not ("gemm_tiles" in name or "splitk_reduce" in name):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": name, "grid": int(r["Grid_Size"]),
+                                                    "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+                                                    "c": {}})
+        d["c"][r["Counter_Name"]] = float(r["Counter_Value"])
+    runs, open_run = [], {}
+    for i in sorted(disp):
+        d = disp[i]
+        k = (d["name"], d["grid"])
+        if k in open_run and i - open_run[k][0] <= gap:
+            j = open_run[k][1]
+        else:
+            runs.append([k, i, []])
+            j = len(runs) - 1
+        runs[j][2].append(d)
+        open_run[k] = (i, j)
+    print(f"{'kernel':40s} {'threads':>9s} {'first':>6s} {'n':>3s} {'avg us':>8s} {'MFMA inst':>10s} "
+          f"{'busy %':>6s} {'clock GHz':>9s} {'MFMA TF/s':>9s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'bank cf':>7s}")
+    for (name, threads), first, v in runs:
+        us = statistics.mean(d["us"] for d in v)
+        c = {n: statistics.mean(d["c"].get(n, 0.0) for d in v) for n in MFMA_COUNTERS}
+        xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024) if xcd_cycles else 0.0
+        clock = xcd_cycles / us / 1e3 if us else 0.0
+        tf = busy * 1024 * 1024 * clock / 1e3
+        mf = c["SQ_INSTS_MFMA"]
+        per = (f"{c['SQ_INSTS_VALU'] / mf:9.2f} {c['SQ_INSTS_LDS'] / mf:8.2f}" if mf else f"{'-':>9s} {'-':>8s}")
+        print(f"{name[:40]:40s} {threads:9d} {first:6d} {len(v):3d} {us:8.1f} {mf:10.0f} "
+              f"{100 * busy:6.1f} {clock:9.2f} {tf:9.0f} {per} {c['SQ_LDS_BANK_CONFLICT']:7.0f}")
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -649,6 +712,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
