@@ -323,8 +323,11 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
                    const int32_t *__restrict__ table, int32_t n_variants,
                    int64_t k_split, float *__restrict__ partial, int64_t tile0)
 {
-    // sign table first (at LDS address 0 its lookups need no base)
-    __shared__ __attribute__((aligned(16))) float sgn[64];
+    // sign table: its 256-byte alignment makes the compiler place it first,
+    // at LDS address 0, so a lookup address is just the masked nibble (after
+    // the 128 KB of tiles its base would not fit the 16-bit instruction
+    // offset and cost an extra VALU op per lookup)
+    __shared__ __attribute__((aligned(256))) float sgn[64];
     // separate objects per buffer: a read of one is then tied only to the
     // copies into that one
     __shared__ __attribute__((aligned(16))) uint8_t XS0[kXsBytes];
@@ -503,11 +506,13 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 
     // Step t (x(t) in XS cur, W_eff(t) in WE cur, k-block 0 fragments in
     // registers): k-blocks 0..2 read the next k-block's fragments and run
-    // their MFMAs; after every k-block one group of W_eff(t+1) is formed
-    // (into WE nxt) and its registers refilled with W(t+2).  Then, with every
-    // read of buffer cur done, the barrier; after it, x(t+2) is copied into
-    // XS cur, step t+1's k-block 0 fragments are read, and step t's last 8
-    // MFMAs (k-block 3, from registers) cover that transition.
+    // their MFMAs; after them the four groups of W_eff(t+1) are formed (two
+    // after k-block 0, one after each of k-blocks 1 and 2, so every build has
+    // MFMAs to overlap) into WE nxt, each group's registers refilled with
+    // W(t+2).  Then, with every read of buffer cur done, the barrier; after
+    // it, x(t+2) is copied into XS cur, step t+1's k-block 0 fragments are
+    // read, and step t's last 8 MFMAs (k-block 3, from registers) cover that
+    // transition.
     auto mfma_kb = [&](int kb) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
@@ -525,13 +530,14 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
             read_a(A[(kb + 1) & 1], cur, kb + 1);
             read_b(B[(kb + 1) & 1], cur, kb + 1);
             mfma_kb(kb);
-            build_store(wr, kb, nxt);
-            load_w(wr, kb, t2);  // 2 loads
+            if (kb == 0) {
+                build_store(wr, 0, nxt);
+                load_w(wr, 0, t2);
+            }
+            build_store(wr, kb + 1, nxt);
+            load_w(wr, kb + 1, t2);  // 2 loads
             __builtin_amdgcn_sched_barrier(0);
         }
-        build_store(wr, 3, nxt);
-        load_w(wr, 3, t2);
-        __builtin_amdgcn_sched_barrier(0);
         // x(t+1) has landed (the 8 W loads issued after it may be in flight),
         // W_eff(t+1) is written and this wave's reads of buffer cur are done
         wait_vmcnt_lgkm0<8>();
