@@ -633,10 +633,11 @@ def _short(name):
     return re.sub(r"\(.*", "", name)
 
 
-def summarize_counters(fetch_csv, write_csv, copy_mb, command):
+def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
     """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each decode-step
     kernel by what the same counters read for a copy of copy_mb MiB, and
-    record HBM bytes per launch next to the algorithmic bytes."""
+    record HBM bytes per launch next to the algorithmic bytes (traffic.json
+    in out_dir, by default profiles/)."""
     import csv
     import re
     import statistics
@@ -694,8 +695,9 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command):
         lines.append(f"grouped GEMM (14 variants, 4096 tokens): fetched {tf_:.0f} B, written {tw_:.0f} B per launch; "
                      f"W_base {w_bytes} B, all 14 sign sets {s_bytes} B, x {x_bytes} B; fetched / W_base = "
                      f"{tf_ / w_bytes:.3f} (a launch per variant would fetch W_base 14 times)")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print("\n".join(lines))

@@ -58,9 +58,9 @@ struct WRaw {
     uint32_t s[2][2];  // [nb]: sign bytes of the 64 columns of the step (8 bytes)
 };
 
-// K64: d_in is a multiple of 64, so a step's 8 sign bytes are one aligned
-// 8-byte load; otherwise they are fetched byte by byte.
-template <bool PER_MATRIX, bool GATHER, bool K64>
+// General kernel (d_in a multiple of 8, not of 64): sign rows are not
+// 8-byte aligned, so a step's 8 sign bytes are fetched byte by byte.
+template <bool PER_MATRIX, bool GATHER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
                 const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
@@ -172,19 +172,13 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
             for (int kb = 0; kb < 4; ++kb)
                 r.w[nb][kb] = __builtin_bit_cast(
                     uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + k0b + kb * 32, 0, 0));
-            if constexpr (K64) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, soff[nb] + (uint32_t)(t * 8), 0, 0);
-                r.s[nb][0] = v[0];
-                r.s[nb][1] = v[1];
-            } else {
-                uint32_t v[2] = {0, 0};
+            uint32_t v[2] = {0, 0};
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    v[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff[nb] + (uint32_t)(t * 8) + i, 0, 0)
-                                 << (8 * (i & 3));
-                r.s[nb][0] = v[0];
-                r.s[nb][1] = v[1];
-            }
+            for (int i = 0; i < 8; ++i)
+                v[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, soff[nb] + (uint32_t)(t * 8) + i, 0, 0)
+                             << (8 * (i & 3));
+            r.s[nb][0] = v[0];
+            r.s[nb][1] = v[1];
         }
     };
     auto build_b = [&](bf16x8 (&B)[2][4], const WRaw &r, int t) {
@@ -258,7 +252,7 @@ void gemm_tiles(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__res
         __builtin_amdgcn_sched_barrier(0);
         // x(t+1) must have landed; W(t+2) (4 x 16-byte loads per feature
         // block plus its sign loads) may stay in flight
-        wait_vmcnt<K64 ? 10 : 24>();
+        wait_vmcnt<24>();
         __syncthreads();
     };
     int t = 0;
@@ -703,18 +697,19 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tokens(const int32_t *_
     }
 }
 
-template <bool GATHER, bool K64>
-hipError_t launch_tiles2(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
+// The general kernel over all m_tiles x n_tiles tiles (d_in not a multiple of 64).
+template <bool GATHER>
+hipError_t launch_general(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                          const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                          int64_t m_tiles, const int32_t *table, int32_t n_variants, hipStream_t s)
 {
     const int64_t n_tiles = (d_out + BN - 1) / BN;
     const dim3 grid((unsigned)(m_tiles * n_tiles)), block(kThreads);
     if (per_matrix)
-        hipLaunchKernelGGL((gemm_tiles<true, GATHER, K64>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
+        hipLaunchKernelGGL((gemm_tiles<true, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
                            d_in, y, m_tiles, table, n_variants);
     else
-        hipLaunchKernelGGL((gemm_tiles<false, GATHER, K64>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
+        hipLaunchKernelGGL((gemm_tiles<false, GATHER>), grid, block, 0, s, x, m, w_base, signs, alpha, d_out,
                            d_in, y, m_tiles, table, n_variants);
     return hipGetLastError();
 }
@@ -735,7 +730,10 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
 #define BD_W8(PM, SP)                                                                                      \
     hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs, alpha, \
                        d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0)
-    if (per_matrix) {
+    if constexpr (GATHER) {  // the grouped GEMM never splits K
+        if (per_matrix) BD_W8(true, false);
+        else BD_W8(false, false);
+    } else if (per_matrix) {
         if (part) BD_W8(true, true);
         else BD_W8(true, false);
     } else {
@@ -744,7 +742,7 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
     }
 #undef BD_W8
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || part == nullptr)
+    if (e != hipSuccess || GATHER || part == nullptr)
         return e;
     const int64_t threads = count * 256 * 64;
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used, count,
@@ -814,7 +812,7 @@ hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, con
 {
     const int64_t m_tiles = (m + BM - 1) / BM;
     if (d_in % 64 != 0)
-        return launch_tiles2<false, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr,
+        return launch_general<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr,
                                            0, s);
     const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
     const GemmPlan p = gemm_plan(m, d_out, d_in);
@@ -851,7 +849,7 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
     if (e != hipSuccess)
         return e;
     if (d_in % 64 != 0)
-        return launch_tiles2<true, false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace,
+        return launch_general<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace,
                                           n_variants, s);
     return launch_w8<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, 0,
                            T * ((d_out + BN - 1) / BN), 1, nullptr, s);

@@ -1,0 +1,134 @@
+"""CPU tier: bench.py's host logic (no GPU): the one-GPU guard, the
+summaries that turn rocprofv3 CSVs into the committed profiles, and the
+staleness check of the recorded HBM traffic."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _write_csv(path, fields, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_more_than_one_gpu_exits():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_summarize_trace_splits_runs(tmp_path, capsys):
+    """Runs of one (kernel, grid) end when more than 12 other dispatches pass."""
+    rows, i = [], 0
+
+    def add(name, grid, us, n):
+        nonlocal i
+        for _ in range(n):
+            i += 1
+            rows.append({"Dispatch_Id": i, "Kernel_Name": f"void bd::(anonymous namespace)::{name}(int)",
+                         "Grid_Size_X": grid, "Grid_Size_Y": 1, "Workgroup_Size_X": 256,
+                         "Start_Timestamp": 1000 * i, "End_Timestamp": 1000 * i + int(us * 1000)})
+
+    add("kern_a", 1024, 5.0, 3)
+    add("kern_b", 2048, 7.0, 13)
+    add("kern_a", 1024, 9.0, 2)
+    path = tmp_path / "trace.csv"
+    _write_csv(path, list(rows[0]), rows)
+    bench.summarize_trace(str(path))
+    lines = [ln.split() for ln in capsys.readouterr().out.splitlines()[1:]]
+    got = [(ln[0], int(ln[1]), int(ln[4]), float(ln[5])) for ln in lines]
+    assert got == [("bd::kern_a", 1024, 3, 5.0), ("bd::kern_b", 2048, 13, 7.0), ("bd::kern_a", 1024, 2, 9.0)]
+
+
+def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
+    """A copy of 256 MiB that FETCH_SIZE reads as half its bytes gives the
+    factor 2; each entry's bytes are the median of its dispatches on the
+    grid seen most often (a stray grid of the same kernel is ignored)."""
+    copy_mb = 256
+    fetch_rows, write_rows = [], []
+
+    def add(name, grid, fetch_b, write_b, n=3):
+        for _ in range(n):
+            base = {"Kernel_Name": f"void bd::(anonymous namespace)::{name}(int)", "Grid_Size": grid}
+            fetch_rows.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": fetch_b / 2 / 1024})
+            write_rows.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": write_b / 1024})
+
+    add("__amd_rocclr_copyBuffer", 4096, copy_mb << 20, copy_mb << 20, n=1)
+    algo = bench.DecodeStep.algorithmic_bytes()
+    names = {"compress_row": ["compress_rows<true, false>"],
+             "compress_matrix": ["compress_rows<true, true>", "alpha_matrix_finish"],
+             "reconstruct": ["reconstruct_rows<false>"],
+             "linear_m1_row": ["gemv_stream<1, 1, 8, false, true>"],
+             "linear_m1_matrix": ["gemv_stream<1, 1, 8, true, true>"],
+             "linear_m4_row": ["gemv_stream<4, 2, 4, false, true>"],
+             "linear_m4_matrix": ["gemv_stream<4, 2, 4, true, true>"],
+             "linear_m16_row": ["gemv_mfma<false, true>"],
+             "linear_m16_matrix": ["gemv_mfma<true, true>"]}
+    assert set(names) == set(bench.STEP_KERNELS)
+    for entry, kernels in names.items():
+        for k in kernels:
+            add(k, 1048576, algo[entry] // len(kernels), 4096)
+    add("compress_rows<true, false>", 64, 10 ** 9, 10 ** 9, n=2)   # another call of the kernel
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    _write_csv(tmp_path / "f.csv", fields, fetch_rows)
+    _write_csv(tmp_path / "w.csv", fields, write_rows)
+    bench.summarize_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy_mb, "cmd", out_dir=str(tmp_path))
+    rec = json.load(open(tmp_path / "traffic.json"))
+    assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
+    assert rec["kernels"]["compress_row"]["fetch_bytes"] == algo["compress_row"]
+    e = rec["kernels"]["reconstruct"]
+    assert e["fetch_bytes"] == algo["reconstruct"] and e["write_bytes"] == 4096
+    assert e["ratio"] == pytest.approx((algo["reconstruct"] + 4096) / algo["reconstruct"], abs=1e-4)
+    cm = rec["kernels"]["compress_matrix"]
+    assert cm["fetch_bytes"] == 2 * (algo["compress_matrix"] // 2) and cm["write_bytes"] == 2 * 4096
+    assert cm["source_sha"] == bench.source_sha("compress.hip")
+
+
+def test_summarize_mfma_busy_and_clock(tmp_path, capsys):
+    """busy = MFMA busy cycles over (GRBM_GUI_ACTIVE / 8) x 1024 SIMDs; clock =
+    (GRBM_GUI_ACTIVE / 8) over the dispatch's duration."""
+    us, ghz, busy = 100.0, 1.8, 0.5
+    xcd_cycles = ghz * 1e3 * us
+    vals = {"GRBM_GUI_ACTIVE": 8 * xcd_cycles, "SQ_VALU_MFMA_BUSY_CYCLES": busy * xcd_cycles * 1024,
+            "SQ_INSTS_MFMA": 1000, "SQ_INSTS_VALU": 4000, "SQ_INSTS_LDS": 1500, "SQ_LDS_BANK_CONFLICT": 0,
+            "SQ_BUSY_CYCLES": 1, "SQ_WAVE_CYCLES": 1, "SQ_ACTIVE_INST_VALU": 1}
+    assert set(vals) == set(bench.MFMA_COUNTERS)
+    rows = []
+    for d in (1, 2):
+        for n, v in vals.items():
+            rows.append({"Dispatch_Id": d, "Kernel_Name": "void bd::(anonymous namespace)::gemm_tiles_w8<false, false, false>(int)",
+                         "Grid_Size": 131072, "Counter_Name": n, "Counter_Value": v,
+                         "Start_Timestamp": 10 ** 6 * d, "End_Timestamp": 10 ** 6 * d + int(us * 1000)})
+    _write_csv(tmp_path / "c.csv", list(rows[0]), rows)
+    bench.summarize_mfma(str(tmp_path / "c.csv"))
+    line = capsys.readouterr().out.splitlines()[1].split()
+    # kernel name has spaces: count from the end
+    n, avg_us, mf, b, clk, tf, valu, lds, cf = line[-9:]
+    assert int(n) == 2 and float(avg_us) == pytest.approx(us)
+    assert float(b) == pytest.approx(100 * busy) and float(clk) == pytest.approx(ghz)
+    assert float(tf) == pytest.approx(busy * 1024 * 1024 * ghz / 1e3, abs=1)
+    assert float(valu) == pytest.approx(4.0) and float(lds) == pytest.approx(1.5)
+
+
+def test_traffic_is_dropped_when_the_kernel_source_changed(monkeypatch):
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    entry = "compress_row"
+    assert entry in rec["kernels"]
+    monkeypatch.setattr(bench, "source_sha", lambda src: rec["kernels"][entry]["source_sha"])
+    assert bench.traffic_for(entry) == rec["kernels"][entry]["bytes_per_launch"]
+    monkeypatch.setattr(bench, "source_sha", lambda src: "0" * 16)
+    assert bench.traffic_for(entry) is None
