@@ -38,6 +38,8 @@ def _bind(lib):
     lib.oracle_linear_grouped_rows.argtypes = [P, I64, P, ctypes.c_int32, P, P, P, I, I64, I64,
                                                P, I64, P, P]
     lib.oracle_linear_grouped_rows.restype = I
+    lib.oracle_similarity.argtypes = [P, P, I, ctypes.c_int32, I64, I64, P, P]
+    lib.oracle_similarity.restype = I
     lib.oracle_num_threads.restype = I
     lib.oracle_set_num_threads.argtypes = [I]
     return lib
@@ -168,6 +170,24 @@ class Oracle:
         return y, sc
 
 
+    def similarity(self, signs, alpha, per_matrix: bool = False):
+        """Gram matrix and cosines of the variants' task vectors (R7).
+
+        signs: uint8 [V, R, C/8]; alpha: fp32 [V, R] or [V].
+        Returns (gram [V, V], cos [V, V]) as float64.
+        """
+        lib = self.lib
+        signs = _c(signs, np.uint8)
+        alpha = _c(alpha, np.float32)
+        V, R, G = signs.shape
+        gram = np.zeros((V, V), dtype=np.float64)
+        cos = np.zeros((V, V), dtype=np.float64)
+        rc = lib.oracle_similarity(_ptr(signs), _ptr(alpha), int(per_matrix), V, R, 8 * G, _ptr(gram), _ptr(cos))
+        if rc != 0:
+            raise ValueError(f"oracle_similarity failed ({rc})")
+        return gram, cos
+
+
 _default = None
 
 
@@ -208,3 +228,7 @@ def linear(*a, **k):
 
 def linear_grouped(*a, **k):
     return default().linear_grouped(*a, **k)
+
+
+def similarity(*a, **k):
+    return default().similarity(*a, **k)

@@ -17,6 +17,9 @@
  *         alpha[:,None] * signs, then a plain linear y = x W_eff^T).
  *   [ID]  "Infrastructure Details": storage format, signs packed 8 per byte
  *         ([4096,4096] -> [4096,512]) and fp32 alpha, one per output row.
+ *   [KM]  "K-Merge: Online LoRA Adapter Management for the Edge": step 1 of
+ *         its policy compares a new adapter with every pooled one by the
+ *         cosine similarity of their task vectors.
  *
  * Readings where the post is silent (each one is listed in the design notes):
  *   R1 sign(0): Delta >= 0 (including -0) is stored as bit 1 = +1; bit 0 = -1.
@@ -30,6 +33,18 @@
  *      dtypes are resolved by adding in fp32 and rounding once to bf16.
  *   R6 linear: y = x W_eff^T accumulated in fp64 (products of two bf16 values
  *      are exact in fp64).  The GPU returns bf16; tests compare against y64.
+ *   R7 similarity ([KM]): the task vector of a variant is the delta a BitDelta
+ *      server holds, tau[r][j] = alpha[r] * s[r][j] with s = +1 for bit 1 and
+ *      -1 for bit 0; the similarity of two variants is the cosine of their
+ *      task vectors over one matrix, from the dot products (Gram matrix).
+ *
+ * Fixed order for the Gram matrix (R7).  For variants a, b and row r,
+ * c_ab[r] = sum_j s_a[r][j] s_b[r][j] is an integer (exact).  The row term is
+ * ((double)alpha_a[r] * (double)alpha_b[r]) * (double)c_ab[r]: the first
+ * product is exact in fp64, the second rounds once.  Row terms go into 256
+ * fp64 partials, row r into p[r mod 256] in increasing r, then the halving
+ * tree below; gram[a][b] = p[0].  cos[a][b] = gram[a][b] /
+ * sqrt(gram[a][a] * gram[b][b]) in fp64 (0 when either norm is 0).
  *
  * Fixed summation order for alpha (R4).  For row r with C columns, split the
  * columns into 8-column groups g = 0 .. C/8-1.  There are 256 fp64 partial
@@ -252,6 +267,52 @@ int oracle_linear_grouped_rows(const uint16_t *x, int64_t M, const int32_t *ids,
                 scale[m * n_rows + t] = sc;
         }
     }
+    return 0;
+}
+
+/* ---- similarity of task vectors ([KM] step 1, R7) ----------------------- */
+
+/* signs: [V, R, C/8]; alpha: [V, R] (per_matrix = 0) or [V] (per_matrix = 1).
+ * gram, cosv: [V, V] fp64, row-major (both triangles written).
+ * Returns 0, or -1 when C is not a positive multiple of 8 or V < 1. */
+int oracle_similarity(const uint8_t *signs, const float *alpha, int per_matrix, int32_t V,
+                      int64_t R, int64_t C, double *gram, double *cosv)
+{
+    if (R < 0 || C <= 0 || C % 8 != 0 || V < 1)
+        return -1;
+    const int64_t G = C / 8;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ab = 0; ab < (int64_t)V * V; ++ab) {
+        int32_t a = (int32_t)(ab / V), b = (int32_t)(ab % V);
+        if (b < a)
+            continue;
+        double p[256];
+        for (int k = 0; k < 256; ++k)
+            p[k] = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+            const uint8_t *ra = signs + ((int64_t)a * R + r) * G;
+            const uint8_t *rb = signs + ((int64_t)b * R + r) * G;
+            int64_t c = 0;
+            for (int64_t j = 0; j < C; ++j) {
+                int sa = ((ra[j >> 3] >> (j & 7)) & 1) ? 1 : -1;
+                int sb = ((rb[j >> 3] >> (j & 7)) & 1) ? 1 : -1;
+                c += sa * sb;
+            }
+            float fa = per_matrix ? alpha[a] : alpha[(int64_t)a * R + r];
+            float fb = per_matrix ? alpha[b] : alpha[(int64_t)b * R + r];
+            double term = ((double)fa * (double)fb) * (double)c;
+            p[r % 256] = p[r % 256] + term;
+        }
+        double g = halving_tree_256(p);
+        gram[(int64_t)a * V + b] = g;
+        gram[(int64_t)b * V + a] = g;
+    }
+    for (int32_t a = 0; a < V; ++a)
+        for (int32_t b = 0; b < V; ++b) {
+            double na = gram[(int64_t)a * V + a], nb = gram[(int64_t)b * V + b];
+            double d = sqrt(na * nb);
+            cosv[(int64_t)a * V + b] = d > 0.0 ? gram[(int64_t)a * V + b] / d : 0.0;
+        }
     return 0;
 }
 

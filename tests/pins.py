@@ -341,8 +341,84 @@ def pin_shape_4096(o):
     assert np.all(signs == 0xFF) and np.all(alpha == 0)
 
 
+# --------------------------------------------------------------- similarity
+
+
+def _sim_case(V, R, C, seed, dyadic):
+    sb = synth.u64((V, R, C // 8), seed, 7101).astype(np.uint8)
+    if dyadic:   # alpha = k 2^-10, k in 1..16: every product and sum below is exact in fp64
+        alpha = ((1 + synth.u64((V, R), seed, 7102) % np.uint64(16)).astype(np.float64) * 2.0 ** -10).astype(np.float32)
+    else:
+        alpha = np.abs(synth.normal_f32((V, R), 1e-3, seed, 7103)).astype(np.float32) + np.float32(1e-5)
+    return sb, alpha
+
+
+def _unpack_pm1(sb):
+    """+-1 as int64 from packed bytes, LSB first (numpy's little-endian unpacking)."""
+    bits = np.unpackbits(sb, axis=-1, bitorder="little").astype(np.int64)
+    return 2 * bits - 1
+
+
+def pin_similarity_exact_rational(o):
+    """K-Merge's cosine similarity of task vectors: with dyadic alpha the Gram
+    matrix is exact, so it must equal the exact rational sum over every weight
+    of tau_a tau_b (tau = alpha * s), per-row and per-matrix alpha; the
+    cosines match the exact value to fp64 rounding."""
+    V, R, C = 3, 7, 24
+    sb, alpha = _sim_case(V, R, C, seed=51, dyadic=True)
+    s = _unpack_pm1(sb)
+    for per_matrix in (False, True):
+        al = alpha[:, 0].copy() if per_matrix else alpha
+        gram, cos = o.similarity(sb, al, per_matrix=per_matrix)
+        for a in range(V):
+            for b in range(V):
+                exact = Fraction(0)
+                for r in range(R):
+                    fa = Fraction(float(al[a] if per_matrix else al[a, r]))
+                    fb = Fraction(float(al[b] if per_matrix else al[b, r]))
+                    exact += fa * fb * int(np.dot(s[a, r], s[b, r]))
+                assert gram[a, b] == float(exact), (per_matrix, a, b)
+        for a in range(V):
+            for b in range(V):
+                ref = float(gram[a, b]) / math.sqrt(float(gram[a, a]) * float(gram[b, b]))
+                assert abs(cos[a, b] - ref) <= 2 * np.spacing(abs(ref) + 1e-300)
+
+
+def pin_similarity_vs_numpy(o):
+    """Random alpha, rows past 256 (every partial visited twice): the Gram
+    matrix agrees with numpy's float64 einsum over the unpacked task vectors
+    to a relative 1e-12 (a different summation order)."""
+    V, R, C = 4, 300, 64
+    sb, alpha = _sim_case(V, R, C, seed=52, dyadic=False)
+    tau = alpha.astype(np.float64)[:, :, None] * _unpack_pm1(sb).astype(np.float64)
+    ref = np.einsum("arj,brj->ab", tau, tau)
+    gram, cos = o.similarity(sb, alpha)
+    assert np.allclose(gram, ref, rtol=1e-12, atol=0)
+    nrm = np.sqrt(np.diag(ref))
+    assert np.allclose(cos, ref / nrm[:, None] / nrm[None, :], rtol=1e-12, atol=1e-15)
+
+
+def pin_similarity_invariants(o):
+    """Symmetry, unit self-similarity, -1 for the complementary sign pattern
+    with the same alpha, equivariance under a permutation of the variants,
+    and near-zero cosine for independent random signs."""
+    V, R, C = 5, 40, 128
+    sb, alpha = _sim_case(V, R, C, seed=53, dyadic=False)
+    sb[3] = ~sb[0]
+    alpha[3] = alpha[0]
+    gram, cos = o.similarity(sb, alpha)
+    assert np.array_equal(gram, gram.T)
+    assert np.all(np.abs(np.diag(cos) - 1.0) <= 2.0 ** -52)
+    assert gram[0, 3] == -gram[0, 0] and abs(cos[0, 3] + 1.0) <= 2.0 ** -52
+    perm = np.array([2, 4, 0, 1, 3])
+    gp, _ = o.similarity(sb[perm], alpha[perm])
+    assert np.array_equal(gp, gram[np.ix_(perm, perm)])
+    for a, b in ((0, 1), (1, 2), (2, 4)):
+        assert abs(cos[a, b]) < 6.0 / math.sqrt(R * C)
+
+
 ALL = [pin_bf16_widen, pin_bf16_round, pin_bf16_hand_ties, pin_compress_handbuilt,
        pin_compress_packing_vs_numpy, pin_alpha_exact_mean, pin_alpha_laplace,
        pin_alpha_least_squares, pin_reconstruct_hand_cases, pin_reconstruct_vs_torch,
        pin_linear_exact_rational, pin_linear_vs_numpy, pin_linear_dyadic, pin_grouped,
-       pin_shape_4096]
+       pin_shape_4096, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants]

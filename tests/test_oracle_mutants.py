@@ -38,6 +38,12 @@ MUTANTS = {
     "variant_alpha_stride": ("per_matrix ? alpha + v : alpha + (int64_t)v * R;",
                              "per_matrix ? alpha + v : alpha + (int64_t)v;"),
     "variant_ignored": ("const uint8_t *sv = signs + (int64_t)v * R * (C / 8);", "const uint8_t *sv = signs;"),
+    "similarity_agreements_only": ("c += sa * sb;", "c += (sa == sb);"),
+    "similarity_alpha_twice": ("double term = ((double)fa * (double)fb) * (double)c;",
+                               "double term = ((double)fa * (double)fa) * (double)c;"),
+    "similarity_no_sqrt": ("double d = sqrt(na * nb);", "double d = na * nb;"),
+    "similarity_row_of_b": ("const uint8_t *rb = signs + ((int64_t)b * R + r) * G;",
+                            "const uint8_t *rb = signs + ((int64_t)a * R + r) * G;"),
 }
 
 
