@@ -33,7 +33,7 @@
  *    bitdelta_last_error() gives the detail (thread-local).
  *  - Alignment: bf16 and fp32 matrices (x, y, W_base, W_ft, W_eff) must be
  *    16-byte aligned, alpha and variant ids 4-byte aligned, workspaces as
- *    stated per call; signs need no alignment.
+ *    stated per call; signs need no alignment (bitdelta_similarity: 4).
  *  - d_in must be a positive multiple of 8 (whole sign bytes); d_out > 0;
  *    m >= 0 (m = 0 is a no-op returning BD_OK).
  *  - Calls are thread-safe; concurrent calls on different streams may share
@@ -145,6 +145,37 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
                                   const uint8_t *signs, const float *alpha, int alpha_mode,
                                   int64_t d_out, int64_t d_in, bd_bf16 *y,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* -------------------------------------------------------------- similarity
+ * "K-Merge: Online LoRA Adapter Management for the Edge", step 1 of the
+ * pool policy: the cosine similarity of two variants' task vectors.  The task
+ * vector of variant v over one matrix is its BitDelta delta
+ * tau_v[r][j] = alpha_v[r] * s_v[r][j] (s = +1 for bit 1, -1 for bit 0).
+ * Outputs, host-readable after the stream completes (fp64, [n_variants,
+ * n_variants] row-major, both triangles):
+ *   gram[a][b]   = <tau_a, tau_b>, summed in a fixed order: per row r the
+ *                  integer c = sum_j s_a s_b (exact), the term
+ *                  (alpha_a[r] * alpha_b[r]) * c in fp64 (one rounding);
+ *                  row r into partial r mod 256 in increasing r, then the
+ *                  halving tree p[k] += p[k + s], s = 128 .. 1.  The same
+ *                  bits on every call and every GPU.
+ *   cosine[a][b] = gram[a][b] / sqrt(gram[a][a] * gram[b][b]) (0 when a
+ *                  norm is 0).
+ * signs: uint8 [n_variants, d_out, d_in/8], 4-byte aligned, with d_in a
+ * multiple of 32 (4-byte aligned sign rows) and n_variants * d_out * d_in/8
+ * below 2 GiB (BD_ESHAPE otherwise); alpha: fp32 [n_variants, d_out]
+ * (BD_ALPHA_ROW) or [n_variants] (BD_ALPHA_MATRIX); n_variants in [1, 16]
+ * (BD_EINVAL otherwise).  gram and cosine: device fp64 [n_variants^2],
+ * 8-byte aligned.
+ * workspace: at least bitdelta_similarity_workspace() bytes (int32 per row
+ * and pair of variants; 0 for one variant), 4-byte aligned; owned by the
+ * caller, scratch on entry, undefined after; calls in flight at once must
+ * not share one. */
+size_t bitdelta_similarity_workspace(int32_t n_variants, int64_t d_out, int64_t d_in);
+bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alpha_mode,
+                              int32_t n_variants, int64_t d_out, int64_t d_in,
+                              double *gram, double *cosine,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -9,14 +9,16 @@ library is missing or a call fails, an exception is raised.
 Method: "BitDelta: Serving 14 Zen Models from One GPU Cluster" (hanzo.blog,
 2026-02-28), "Mathematical Foundation", "Serving Architecture" and
 "Infrastructure Details"; `linear` mirrors the post's conceptual
-fused_bitdelta_linear(x, w_base, delta_sign, alpha) signature.
+fused_bitdelta_linear(x, w_base, delta_sign, alpha) signature.  `similarity`
+is step 1 of "K-Merge: Online LoRA Adapter Management for the Edge" on the
+variants' BitDelta task vectors.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped",
+__all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE",
            "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
 
@@ -45,6 +47,8 @@ EXPORTS = {
     "bitdelta_linear": (_INT, [_P, _I64, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
     "bitdelta_linear_grouped_workspace": (_SZ, [_I64, _I32, _I64, _I64]),
     "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
+    "bitdelta_similarity_workspace": (_SZ, [_I32, _I64, _I64]),
+    "bitdelta_similarity": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -202,3 +206,29 @@ def linear_grouped(x, variant_ids, w_base, signs, alpha, per_matrix: bool | None
     check(lib.bitdelta_linear_grouped(_ptr(x), m, _ptr(variant_ids), V, _ptr(w_base), _ptr(signs), _ptr(alpha),
                                       mode, d_out, d_in, _ptr(y), _ptr(ws), nws, _stream(x.device)))
     return y
+
+
+def similarity(signs, alpha, per_matrix: bool | None = None):
+    """Gram matrix <tau_a, tau_b> and cosines of V variants' task vectors
+    tau_v = alpha_v * sign_v over one matrix.  signs [V, d_out, d_in/8];
+    alpha [V, d_out] or [V].  Returns (gram, cosine), float64 [V, V] on the
+    signs' device."""
+    torch = _torch()
+    _dev_tensor(signs, torch.uint8, "signs")
+    _dev_tensor(alpha, torch.float32, "alpha")
+    if signs.dim() != 3:
+        raise ValueError("signs must be [V, d_out, d_in/8]")
+    V, d_out, g = signs.shape
+    d_in = 8 * g
+    if per_matrix is None:
+        per_matrix = alpha.dim() == 1 and d_out != 1
+    if alpha.numel() != (V if per_matrix else V * d_out):
+        raise ValueError("alpha must be [V, d_out] (per row) or [V] (per matrix)")
+    mode = BD_ALPHA_MATRIX if per_matrix else BD_ALPHA_ROW
+    gram = torch.empty((V, V), dtype=torch.float64, device=signs.device)
+    cos = torch.empty((V, V), dtype=torch.float64, device=signs.device)
+    nws = lib.bitdelta_similarity_workspace(V, d_out, d_in)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=signs.device)
+    check(lib.bitdelta_similarity(_ptr(signs), _ptr(alpha), mode, V, d_out, d_in, _ptr(gram), _ptr(cos), _ptr(ws),
+                                  nws, _stream(signs.device)))
+    return gram, cos

@@ -265,4 +265,45 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
                   "bitdelta_linear_grouped");
 }
 
+size_t bitdelta_similarity_workspace(int32_t n_variants, int64_t d_out, int64_t d_in)
+{
+    (void)d_in;
+    if (n_variants < 1 || n_variants > bd::kSimilarityMaxVariants)
+        return 0;
+    return bd::similarity_workspace_bytes(n_variants, d_out);
+}
+
+bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alpha_mode, int32_t n_variants,
+                              int64_t d_out, int64_t d_in, double *gram, double *cosine, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    BD_TRY(check_mode(alpha_mode));
+    if (n_variants < 1 || n_variants > bd::kSimilarityMaxVariants)
+        return fail(BD_EINVAL, "n_variants must be in [1, %d] (got %d)", bd::kSimilarityMaxVariants, n_variants);
+    BD_TRY(check_matrix(d_out, d_in));
+    if (d_in % 32 != 0)
+        return fail(BD_ESHAPE, "similarity needs d_in a multiple of 32 (got %lld)", (long long)d_in);
+    if ((int64_t)n_variants * d_out * (d_in / 8) >= ((int64_t)1 << 31))
+        return fail(BD_ESHAPE, "similarity sign tensor [%d, %lld, %lld] must be below 2 GiB", n_variants,
+                    (long long)d_out, (long long)(d_in / 8));
+    const size_t need = bitdelta_similarity_workspace(n_variants, d_out, d_in);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "similarity needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    BD_NONNULL(signs);
+    BD_NONNULL(alpha);
+    BD_NONNULL(gram);
+    BD_NONNULL(cosine);
+    BD_ALIGNED(signs, 4);
+    BD_ALIGNED(alpha, 4);
+    BD_ALIGNED(gram, 8);
+    BD_ALIGNED(cosine, 8);
+    if (need) {
+        BD_NONNULL(workspace);
+        BD_ALIGNED(workspace, 4);
+    }
+    return device(bd::launch_similarity(signs, alpha, alpha_mode == BD_ALPHA_MATRIX, n_variants, d_out, d_in, gram,
+                                        cosine, static_cast<int32_t *>(workspace), (hipStream_t)stream),
+                  "bitdelta_similarity");
+}
+
 }  // extern "C"

@@ -52,4 +52,13 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
                           bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                           int32_t *workspace, hipStream_t s);
 
+// similarity.hip: Gram matrix and cosines of up to kSimilarityMaxVariants
+// variants' task vectors; `counts` holds similarity_workspace_bytes() bytes
+// (int32 per row and pair).
+constexpr int kSimilarityMaxVariants = 16;
+size_t similarity_workspace_bytes(int32_t n_variants, int64_t d_out);
+hipError_t launch_similarity(const uint8_t *signs, const float *alpha, bool per_matrix, int32_t n_variants,
+                             int64_t d_out, int64_t d_in, double *gram, double *cosine, int32_t *counts,
+                             hipStream_t s);
+
 }  // namespace bd

@@ -163,3 +163,35 @@ def test_launch_without_device_reports_edevice(bd):
     st = bd.lib.bitdelta_reconstruct(FAKE, FAKE, FAKE, 0, 4, 16, FAKE, None)
     assert st == bd.BD_EDEVICE, st
     assert "bitdelta_reconstruct" in err(bd)
+
+
+def test_similarity_validation(bd):
+    """Host-side checks of bitdelta_similarity: every failing call returns
+    before a launch (FAKE pointers are never dereferenced)."""
+    W = bd.lib.bitdelta_similarity_workspace
+    f = bd.lib.bitdelta_similarity
+    assert W(14, 8192, 8192) == 4 * 8192 * 91        # int32 per row and pair
+    assert W(2, 100, 64) == 4 * 100 * 1
+    assert W(1, 100, 64) == 0                        # one variant: no pairs
+    assert W(17, 100, 64) == 0 and W(0, 100, 64) == 0
+    need = W(4, 64, 256)
+    ok = (FAKE, FAKE, 0, 4, 64, 256, FAKE, FAKE, FAKE, need, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["signs", "alpha", "mode", "V", "d_out", "d_in", "gram", "cos", "ws", "nws", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(mode=2) == bd.BD_EINVAL
+    assert call(V=0) == bd.BD_EINVAL and call(V=17) == bd.BD_EINVAL
+    assert call(d_in=200) == bd.BD_ESHAPE              # multiple of 8, not of 32
+    assert call(d_in=12) == bd.BD_ESHAPE and call(d_out=0) == bd.BD_ESHAPE
+    assert call(V=16, d_out=1 << 20, d_in=1024) == bd.BD_ESHAPE  # signs of 2 GiB
+    assert call(nws=need - 1) == bd.BD_EWORKSPACE
+    assert call(signs=None) == bd.BD_EINVAL and call(gram=None) == bd.BD_EINVAL
+    assert call(ws=None) == bd.BD_EINVAL
+    assert call(signs=FAKE_ODD) == bd.BD_EALIGN
+    assert call(gram=ctypes.c_void_p(4100)) == bd.BD_EALIGN
+    assert call(ws=FAKE_ODD) == bd.BD_EALIGN
