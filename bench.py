@@ -24,6 +24,8 @@ The same line carries:
               PFLOP/s bf16 dense peak);
   grouped     14 variants over one shared 8192 x 8192 base, 4096 tokens in a
               Zipf(1.1) split (TFLOP/s);
+  similarity  K-Merge's cosine similarity of the 14 variants' task vectors
+              on the grouped layer's packed signs (GB/s);
   context     reference points from the vendor libraries through torch: a
               34 MiB copy, plain bf16 GEMMs on the prefill shapes, and the
               unfused path (reconstruct to HBM, then a plain GEMM) beside the
@@ -355,9 +357,51 @@ def run_grouped(torch, bd, synth, reps=10):
     tf = flop / us / 1e6
     log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s "
         f"(ids pre-sorted: {us_sorted:.1f} us)")
+    sim = run_similarity(torch, bd, signs, alpha)
     return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
             "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-            "us_ids_presorted": round(us_sorted, 1)}
+            "us_ids_presorted": round(us_sorted, 1)}, sim
+
+
+def run_similarity(torch, bd, signs, alpha, reps=20):
+    """K-Merge similarity (Gram matrix and cosines of the variants' task
+    vectors) over the grouped layer's 14 packed sign sets.  Algorithmic bytes:
+    the packed signs, alpha and the two V x V fp64 outputs; the int32 counts
+    it passes between its two kernels are scratch."""
+    V, N, G = signs.shape
+    K = 8 * G
+    dev = signs.device
+    gram = torch.empty((V, V), dtype=torch.float64, device=dev)
+    cos = torch.empty((V, V), dtype=torch.float64, device=dev)
+    nws = bd.lib.bitdelta_similarity_workspace(V, N, K)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bd.check(bd.lib.bitdelta_similarity(P(signs.data_ptr()), P(alpha.data_ptr()), bd.BD_ALPHA_ROW, V, N, K,
+                                            P(gram.data_ptr()), P(cos.data_ptr()), P(ws.data_ptr()), nws,
+                                            P(stream.cuda_stream)))
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    rep_us = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_us.append(e0.elapsed_time(e1) / reps * 1e3)
+    us = sum(rep_us) / 5
+    nbytes = V * N * G + V * N * 4 + 2 * V * V * 8
+    gbs = nbytes / us / 1e3
+    log(f"similarity {V} variants [{N},{K}]: {us:.1f} us, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
+    return {"variants": V, "d_out": N, "d_in": K, "us": round(us, 2), "us_median5": round(statistics.median(rep_us), 2),
+            "us_min5": round(min(rep_us), 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 # ----------------------------------------------------------------- context
@@ -835,7 +879,7 @@ def main():
     torch.cuda.empty_cache()
 
     prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
-    grouped = None if args.no_grouped else run_grouped(torch, bd, synth)
+    grouped, similarity = (None, None) if args.no_grouped else run_grouped(torch, bd, synth)
     context = None if args.no_context else run_context(torch)
     if context is not None and prefill is not None:
         context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill)
@@ -862,6 +906,7 @@ def main():
         "kernels": kernels,
         "prefill": prefill,
         "grouped": grouped,
+        "similarity": similarity,
         "context": context,
         "cpu_baseline": cpu,
     }

@@ -286,6 +286,9 @@ bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alph
     if ((int64_t)n_variants * d_out * (d_in / 8) >= ((int64_t)1 << 31))
         return fail(BD_ESHAPE, "similarity sign tensor [%d, %lld, %lld] must be below 2 GiB", n_variants,
                     (long long)d_out, (long long)(d_in / 8));
+    if ((int64_t)n_variants * (n_variants - 1) / 2 * d_out * 4 >= ((int64_t)1 << 31))
+        return fail(BD_ESHAPE, "similarity of %d variants over %lld rows needs pair counts of 2 GiB or more",
+                    n_variants, (long long)d_out);
     const size_t need = bitdelta_similarity_workspace(n_variants, d_out, d_in);
     if (workspace_bytes < need)
         return fail(BD_EWORKSPACE, "similarity needs %zu workspace bytes, got %zu", need, workspace_bytes);

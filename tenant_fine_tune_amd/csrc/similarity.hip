@@ -19,15 +19,16 @@
 //    keeps one disagreement count per pair (v_xor + v_bcnt per dword and
 //    pair).  The counts of the 4 lanes of a row are summed by lane shuffles,
 //    those of the 4 waves through LDS, and c_ab[r] is stored as int32
-//    [d_out][pairs].  The traffic is the packed signs (d_in / 8 bytes per row
-//    and variant): the kernel is bound by HBM.
+//    [pairs][d_out].  The traffic is the packed signs (d_in / 8 bytes per row
+//    and variant); at 14 variants the 91 pairs' v_bcnt work costs about as
+//    much as the reads.
 //  similarity_gram: the floating-point part, in the fixed order the oracle
 //    defines.  One workgroup per pair a <= b: thread t adds, for rows
 //    r = t, t + 256, ... in increasing order, the term
 //    (alpha_a[r] * alpha_b[r]) * c_ab[r] (the first product is exact in fp64,
 //    the second rounds once; no fused multiply-add) into its partial, then
-//    the halving tree p[k] += p[k + s], s = 128 .. 1.  The workgroup also
-//    forms the two diagonal sums the same way, so the cosine
+//    the halving tree p[k] += p[k + s], s = 128 .. 1.  The workgroup forms
+//    the two diagonal sums alongside, the same way, so the cosine
 //    g_ab / sqrt(g_aa g_bb) needs no second launch.
 #include <hip/hip_runtime.h>
 
@@ -71,13 +72,17 @@ __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_
 #pragma unroll
     for (int p = 0; p < P; ++p)
         d[p] = 0;
-    for (int k = wave; k < nk; k += kSimWaves) {
-        uint4 s[V];
+    // chunk k of this lane's row for every variant; chunks past the row
+    // (k >= nk) use an out-of-range offset and read zeros (no disagreement)
+    auto load = [&](uint4 (&s)[V], int k) {
+        const uint32_t b = k < nk ? base : kInvalidOffset;
         const uint32_t off = (uint32_t)k * 64u;
 #pragma unroll
         for (int v = 0; v < V; ++v)
             s[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, base, off + (uint32_t)v * vstride, kStream));
+                                                 rs, b, off + (uint32_t)v * vstride, kStream));
+    };
+    auto count = [&](uint4 (&s)[V], int k) {
         if constexpr (!EVEN) {
             // valid bytes of this lane's 16-byte piece (0..16); the rest is
             // masked to zero in every variant
@@ -108,6 +113,11 @@ __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_
                 c += __builtin_popcount(s[a].w ^ s[b].w);
                 d[pair_index(a, b, V)] = c;
             }
+    };
+    for (int k = wave; k < nk; k += kSimWaves) {
+        uint4 s[V];
+        load(s, k);
+        count(s, k);
     }
     // the 4 lanes of a row (q = 0..3: lanes j, j + 16, j + 32, j + 48)
 #pragma unroll
@@ -122,9 +132,10 @@ __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_
         if ((p & 3) == q)
             part[wave][j][p] = (int32_t)d[p];
     __syncthreads();
-    // c_ab[r] = d_in - 2 * (disagreements summed over the 4 waves)
+    // c_ab[r] = d_in - 2 * (disagreements summed over the 4 waves), stored
+    // pair-major [pairs][d_out] so the fixed-order sum reads it contiguously
     for (int i = threadIdx.x; i < kSimRows * P; i += 64 * kSimWaves) {
-        const int rr = i / P, p = i - rr * P;
+        const int p = i / kSimRows, rr = i - p * kSimRows;
         const int64_t r = (int64_t)blockIdx.x * kSimRows + rr;
         if (r >= R)
             continue;
@@ -132,41 +143,18 @@ __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_
 #pragma unroll
         for (int w = 0; w < kSimWaves; ++w)
             dis += part[w][rr][p];
-        counts[r * P + p] = (int32_t)(C - 2 * dis);
+        counts[(int64_t)p * R + r] = (int32_t)(C - 2 * dis);
     }
 }
 
-// Fixed-order fp64 sum over rows of (alpha_a[r] alpha_b[r]) c[r] (c = d_in
-// on the diagonal), 256 threads, the halving tree in LDS.  Uniform in the
-// workgroup; returns the sum in every thread.
-__device__ double gram_entry(const float *__restrict__ alpha, bool per_matrix, const int32_t *__restrict__ counts,
-                             int P, int a, int b, int V, int64_t R, int64_t C, double *tree)
-{
-    // every product and sum rounds on its own: no fused multiply-add (the
-    // compiler would otherwise contract acc + f * c into one fma)
-#pragma clang fp contract(off)
-    const int t = threadIdx.x;
-    const float *aa = per_matrix ? alpha + a : alpha + (int64_t)a * R;
-    const float *ab = per_matrix ? alpha + b : alpha + (int64_t)b * R;
-    const int p = a < b ? pair_index(a, b, V) : 0;
-    double acc = 0.0;
-    for (int64_t r = t; r < R; r += kTreeThreads) {
-        const double fa = (double)aa[per_matrix ? 0 : r];
-        const double fb = (double)ab[per_matrix ? 0 : r];
-        const double c = a == b ? (double)C : (double)counts[r * P + p];
-        acc = acc + (fa * fb) * c;
-    }
-    tree[t] = acc;
-    __syncthreads();
-    for (int s = kTreeThreads / 2; s >= 1; s >>= 1) {
-        if (t < s)
-            tree[t] = tree[t] + tree[t + s];
-        __syncthreads();
-    }
-    const double g = tree[0];
-    __syncthreads();
-    return g;
-}
+// The Gram kernel: workgroup (a, b), a <= b, forms g_ab, g_aa and g_bb
+// together.  Each is the fixed-order fp64 sum over rows of
+// (alpha_x[r] alpha_y[r]) c_xy[r] (c = d_in on the diagonal): thread t adds
+// rows t, t + 256, ... in increasing order (all of one batch's loads go out
+// before its dependent adds), then the halving tree over the 256 partials.
+// Every product and sum rounds on its own (no fused multiply-add: the
+// compiler would otherwise contract s + p * c into one fma).
+constexpr int kGramBatch = 32;
 
 __global__ __launch_bounds__(kTreeThreads) void similarity_gram(const float *__restrict__ alpha, bool per_matrix,
                                                                 const int32_t *__restrict__ counts, int V,
@@ -174,7 +162,7 @@ __global__ __launch_bounds__(kTreeThreads) void similarity_gram(const float *__r
                                                                 double *__restrict__ cosine)
 {
 #pragma clang fp contract(off)
-    __shared__ double tree[kTreeThreads];
+    __shared__ double tree[3][kTreeThreads];
     // workgroup -> pair a <= b, row by row of the upper triangle
     int a = 0, idx = (int)blockIdx.x;
     while (idx >= V - a) {
@@ -182,17 +170,62 @@ __global__ __launch_bounds__(kTreeThreads) void similarity_gram(const float *__r
         ++a;
     }
     const int b = a + idx;
+    const int t = threadIdx.x;
+    const float *aa = per_matrix ? alpha + a : alpha + (int64_t)a * R;
+    const float *ab = per_matrix ? alpha + b : alpha + (int64_t)b * R;
+    const bool diag = a == b;
+    // counts through a buffer resource: the diagonal (and one variant, no
+    // pairs at all) reads nothing (out-of-range offset)
     const int P = V * (V - 1) / 2;
-    const double gab = gram_entry(alpha, per_matrix, counts, P, a, b, V, R, C, tree);
-    const double gaa = a == b ? gab : gram_entry(alpha, per_matrix, counts, P, a, a, V, R, C, tree);
-    const double gbb = a == b ? gab : gram_entry(alpha, per_matrix, counts, P, b, b, V, R, C, tree);
-    if (threadIdx.x == 0) {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(counts, (int64_t)P * R * 4);
+    const uint32_t cbase = diag ? kInvalidOffset : (uint32_t)((int64_t)pair_index(a, b, V) * R * 4);
+    const double cd = (double)C;
+    double sab = 0.0, saa = 0.0, sbb = 0.0;
+    for (int64_t r0 = t; r0 < R; r0 += (int64_t)kGramBatch * kTreeThreads) {
+        // every load unconditional (rows past R read row R - 1 and are then
+        // zeroed), so they all go out before the adds
+        float fa[kGramBatch], fb[kGramBatch];
+        int32_t c[kGramBatch];
+#pragma unroll
+        for (int u = 0; u < kGramBatch; ++u) {
+            const int64_t r = r0 + (int64_t)u * kTreeThreads;
+            const bool ok = r < R;
+            const int64_t rr = ok ? r : R - 1;
+            const float va = aa[per_matrix ? 0 : rr], vb = ab[per_matrix ? 0 : rr];
+            const int32_t vc = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, cbase + (uint32_t)(rr * 4), 0, 0);
+            fa[u] = ok ? va : 0.0f;
+            fb[u] = ok ? vb : 0.0f;
+            c[u] = ok ? vc : 0;
+        }
+        // a zeroed row adds +0 (or -0) to a sum that starts at +0: no change
+#pragma unroll
+        for (int u = 0; u < kGramBatch; ++u) {
+            const double da = (double)fa[u], db = (double)fb[u];
+            sab = sab + (da * db) * (diag ? cd : (double)c[u]);
+            saa = saa + (da * da) * cd;
+            sbb = sbb + (db * db) * cd;
+        }
+    }
+    tree[0][t] = sab;
+    tree[1][t] = saa;
+    tree[2][t] = sbb;
+    __syncthreads();
+    for (int s = kTreeThreads / 2; s >= 1; s >>= 1) {
+        if (t < s) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                tree[i][t] = tree[i][t] + tree[i][t + s];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        const double gab = tree[0][0], gaa = tree[1][0], gbb = tree[2][0];
         const double n = sqrt(gaa * gbb);
-        const double c = n > 0.0 ? gab / n : 0.0;
+        const double cs = n > 0.0 ? gab / n : 0.0;
         gram[a * V + b] = gab;
         gram[b * V + a] = gab;
-        cosine[a * V + b] = c;
-        cosine[b * V + a] = c;
+        cosine[a * V + b] = cs;
+        cosine[b * V + a] = cs;
     }
 }
 
