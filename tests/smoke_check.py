@@ -1,6 +1,7 @@
 """One small pass of the hot path on cuda:0, checked against the oracle:
-compress -> reconstruct -> linear (decode and prefill) -> grouped, on a
-256 x 512 layer (the tiny single-layer workload) with 4 and 40 tokens."""
+compress -> reconstruct -> linear (decode and prefill) -> grouped ->
+similarity of the variants, on a 256 x 512 layer (the tiny single-layer
+workload) with 4 and 40 tokens."""
 import numpy as np
 import torch
 
@@ -36,8 +37,13 @@ def run() -> None:
     y = host_bits(bd.linear_grouped(bf16_dev(x), i32_dev(ids), wd, u8_dev(signs), f32_dev(alpha)))
     y64, sc = oracle.linear_grouped(x, ids, w_base, signs, alpha)
     check_linear(y, y64, sc, "smoke grouped")
+    g, c = bd.similarity(u8_dev(signs), f32_dev(alpha))
+    g64, c64 = oracle.similarity(signs, alpha)
+    assert np.array_equal(host(g), g64), "similarity Gram matrix differs from the oracle"
+    assert np.all(np.abs(host(c) - c64) <= np.spacing(np.abs(c64))), "similarity cosines differ from the oracle"
     torch.cuda.synchronize()
-    print("smoke: OK (compress, reconstruct, linear decode/prefill, grouped match the oracle)", flush=True)
+    print("smoke: OK (compress, reconstruct, linear decode/prefill, grouped, similarity match the oracle)",
+          flush=True)
 
 
 if __name__ == "__main__":
