@@ -57,7 +57,8 @@ typedef enum {
     BD_ESHAPE = 2,     /* d_in % 8 != 0, d_in <= 0, d_out <= 0, m < 0, or a size the grid cannot cover */
     BD_EALIGN = 3,     /* a pointer misses the alignment stated above */
     BD_EWORKSPACE = 4, /* workspace smaller than the matching *_workspace() query */
-    BD_EDEVICE = 5     /* the HIP runtime rejected a launch */
+    BD_EDEVICE = 5,    /* the HIP runtime rejected a launch (delta cache: the loader failed) */
+    BD_EBUSY = 6       /* delta cache: no slot can be freed (bitdelta_cache.h) */
 } bd_status;
 
 typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;

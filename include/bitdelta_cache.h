@@ -1,0 +1,82 @@
+/*
+ * bitdelta_cache.h -- host-side delta cache of the BitDelta serving path.
+ *
+ * "BitDelta: Serving 14 Zen Models from One GPU Cluster", section
+ * "Infrastructure Details": a variant whose deltas are not in the GPU-side
+ * delta cache pays a load on its first request (the post: about 200 ms for
+ * 8.75 GB); eviction is LRU weighted by request rate, the most requested
+ * variants (the top 6 of 14) stay pinned and the others share the remaining
+ * space under LRU.  Section "Serving Architecture": requests for a variant go
+ * through delta_load before the fused kernels run.
+ *
+ * The cache manages fixed-size slots in a device region the caller owns
+ * (n_slots * slot_bytes bytes); it allocates no device memory.  A variant is
+ * loaded by the caller's loader callback into its slot.  Policy (the
+ * readings where the post is silent):
+ *  - traffic volume of a variant = its requests among the last `window`
+ *    requests (the current one included); the pinned set at a request = the
+ *    n_pinned variants of largest volume, ties to the lower id, volume > 0;
+ *  - a miss takes the lowest free slot, else evicts the least recently
+ *    requested resident variant that is not pinned, not acquired and not
+ *    loading; if there is none the request fails with BD_EBUSY (its
+ *    bookkeeping still counts);
+ *  - single flight: concurrent acquires of a variant that is loading wait for
+ *    that one load instead of starting another.
+ * Every call is thread-safe.  Loads run outside the cache's lock, so loads
+ * of different variants proceed concurrently.
+ */
+#ifndef BITDELTA_CACHE_H
+#define BITDELTA_CACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bitdelta.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bd_delta_cache bd_delta_cache;
+
+/* Fill `dst` (device, slot_bytes) with variant `variant`'s packed deltas.
+ * Returns 0 on success; anything else fails the acquire (BD_EDEVICE) and
+ * leaves the slot free. */
+typedef int (*bd_delta_loader)(void *user, int32_t variant, void *dst, size_t slot_bytes);
+
+/* BD_EINVAL for n_variants < 1, n_slots < 1, n_pinned < 0, window < 1, a
+ * NULL slots, loader or out, or slot_bytes == 0.  slots: device region of
+ * n_slots * slot_bytes bytes, owned by the caller, which must outlive the
+ * cache. */
+bd_status bitdelta_cache_create(int32_t n_variants, int32_t n_slots, int32_t n_pinned, int64_t window,
+                                void *slots, size_t slot_bytes, bd_delta_loader loader, void *user,
+                                bd_delta_cache **out);
+/* Frees the cache's host state; NULL is a no-op.  No acquire may be in
+ * progress. */
+void bitdelta_cache_destroy(bd_delta_cache *cache);
+
+/* outcome of an acquire */
+enum { BD_CACHE_HIT = 0, BD_CACHE_MISS = 1, BD_CACHE_JOINED = 2 };
+
+/* Make variant `variant` resident and hold it: *slot_ptr = its device slot,
+ * *outcome = BD_CACHE_HIT, BD_CACHE_MISS (this call loaded it) or
+ * BD_CACHE_JOINED (it waited for another caller's load).  Blocks during a
+ * load.  Every successful acquire must be matched by one release.  Errors:
+ * BD_EINVAL (bad variant or NULL output), BD_EBUSY (no slot can be freed),
+ * BD_EDEVICE (the loader failed). */
+bd_status bitdelta_cache_acquire(bd_delta_cache *cache, int32_t variant, void **slot_ptr, int *outcome);
+/* BD_EINVAL when the variant is not held. */
+bd_status bitdelta_cache_release(bd_delta_cache *cache, int32_t variant);
+
+/* Slot index of a resident variant, -1 otherwise (also for a bad variant). */
+int32_t bitdelta_cache_slot_of(const bd_delta_cache *cache, int32_t variant);
+/* Counters since creation: hits, misses (loads started), joins, evictions,
+ * refused (BD_EBUSY) requests.  Any pointer may be NULL. */
+void bitdelta_cache_counters(const bd_delta_cache *cache, int64_t *hits, int64_t *misses, int64_t *joins,
+                             int64_t *evictions, int64_t *busy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITDELTA_CACHE_H */

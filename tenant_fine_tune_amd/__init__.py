@@ -19,10 +19,13 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
-           "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE",
+           "DeltaCache", "LOADER",
+           "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
+           "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
            "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
 
-BD_OK, BD_EINVAL, BD_ESHAPE, BD_EALIGN, BD_EWORKSPACE, BD_EDEVICE = range(6)
+BD_OK, BD_EINVAL, BD_ESHAPE, BD_EALIGN, BD_EWORKSPACE, BD_EDEVICE, BD_EBUSY = range(7)
+BD_CACHE_HIT, BD_CACHE_MISS, BD_CACHE_JOINED = 0, 1, 2
 BD_BF16, BD_F32 = 0, 1
 BD_ALPHA_ROW, BD_ALPHA_MATRIX = 0, 1
 
@@ -49,7 +52,17 @@ EXPORTS = {
     "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
     "bitdelta_similarity_workspace": (_SZ, [_I32, _I64, _I64]),
     "bitdelta_similarity": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    # include/bitdelta_cache.h
+    "bitdelta_cache_create": (_INT, [_I32, _I32, _I32, _I64, _P, _SZ, _P, _P, _P]),
+    "bitdelta_cache_destroy": (None, [_P]),
+    "bitdelta_cache_acquire": (_INT, [_P, _I32, _P, _P]),
+    "bitdelta_cache_release": (_INT, [_P, _I32]),
+    "bitdelta_cache_slot_of": (_I32, [_P, _I32]),
+    "bitdelta_cache_counters": (None, [_P, _P, _P, _P, _P, _P]),
 }
+
+# bd_delta_loader: int (*)(void *user, int32_t variant, void *dst, size_t slot_bytes)
+LOADER = ctypes.CFUNCTYPE(_INT, _P, _I32, _P, _SZ)
 
 
 class BitDeltaError(RuntimeError):
@@ -232,3 +245,48 @@ def similarity(signs, alpha, per_matrix: bool | None = None):
     check(lib.bitdelta_similarity(_ptr(signs), _ptr(alpha), mode, V, d_out, d_in, _ptr(gram), _ptr(cos), _ptr(ws),
                                   nws, _stream(signs.device)))
     return gram, cos
+
+
+class DeltaCache:
+    """Delta cache over `n_slots` slots of `slot_bytes` in a device region
+    (include/bitdelta_cache.h).  `loader(variant, dst_ptr, slot_bytes) -> int`
+    fills a slot (0 = success); `slots` is a device tensor of at least
+    n_slots * slot_bytes bytes that must outlive the cache."""
+
+    def __init__(self, n_variants, n_slots, n_pinned, window, slots, slot_bytes, loader):
+        torch = _torch()
+        if not isinstance(slots, torch.Tensor) or slots.device.type != "cuda":
+            raise TypeError("slots must be a device tensor")
+        if slots.numel() * slots.element_size() < n_slots * slot_bytes:
+            raise ValueError("slots region too small")
+        self._slots = slots
+        self._cb = LOADER(lambda user, v, dst, n: int(loader(v, dst, n)))
+        h = ctypes.c_void_p()
+        check(lib.bitdelta_cache_create(n_variants, n_slots, n_pinned, window, _ptr(slots), slot_bytes, self._cb,
+                                        None, ctypes.byref(h)))
+        self._h = h
+
+    def acquire(self, variant):
+        """(device pointer of the slot, outcome BD_CACHE_HIT / _MISS / _JOINED)."""
+        p, o = ctypes.c_void_p(), ctypes.c_int()
+        check(lib.bitdelta_cache_acquire(self._h, variant, ctypes.byref(p), ctypes.byref(o)))
+        return p.value, o.value
+
+    def release(self, variant):
+        check(lib.bitdelta_cache_release(self._h, variant))
+
+    def slot_of(self, variant):
+        return lib.bitdelta_cache_slot_of(self._h, variant)
+
+    def counters(self):
+        v = [ctypes.c_int64() for _ in range(5)]
+        lib.bitdelta_cache_counters(self._h, *[ctypes.byref(x) for x in v])
+        return dict(zip(("hits", "misses", "joins", "evictions", "busy"), (x.value for x in v)))
+
+    def close(self):
+        if self._h:
+            lib.bitdelta_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()

@@ -99,6 +99,7 @@ const char *bitdelta_status_string(int s)
     case BD_EALIGN: return "BD_EALIGN: misaligned pointer";
     case BD_EWORKSPACE: return "BD_EWORKSPACE: workspace too small";
     case BD_EDEVICE: return "BD_EDEVICE: HIP launch failed";
+    case BD_EBUSY: return "BD_EBUSY: no delta-cache slot can be freed";
     default: return "unknown bitdelta status";
     }
 }
