@@ -599,7 +599,38 @@ def run_stack(torch, bd, synth, n_layers):
         log(f"stack {label} m={m} through {n_layers * len(st.shapes)} linears: {ms:.2f} ms, "
             f"{flop / ms / 1e9:.1f} TFLOP/s, {nbytes / ms / 1e6:.1f} GB/s")
         del g, xs, ys
+    out["delta_upload"] = run_delta_upload(torch, bd, st)
     return out
+
+
+def run_delta_upload(torch, bd, st, reps=3):
+    """Cold start of a variant: its packed deltas for the whole stack (signs +
+    alpha of every matrix) copied from pinned host memory to HBM by the
+    library's delta-cache loader (bitdelta_cache_host_loader), timed on the
+    host around the call (the loader synchronises its stream)."""
+    nbytes = sum(d_out * d_in // 8 + 4 * d_out for _, _, d_out, d_in in st.matrices())
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    class HostLoader(ctypes.Structure):
+        _fields_ = [("host_ptrs", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+    table = (ctypes.c_void_p * 1)(host.data_ptr())
+    hl = HostLoader(ctypes.cast(table, ctypes.c_void_p), torch.cuda.current_stream().cuda_stream)
+    ms = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rc = bd.lib.bitdelta_cache_host_loader(ctypes.byref(hl), 0, ctypes.c_void_p(dst.data_ptr()), nbytes)
+        ms.append((time.perf_counter() - t0) * 1e3)
+        if rc != 0:
+            raise RuntimeError(f"host loader failed ({rc})")
+    best = min(ms)
+    log(f"stack delta upload (one variant, {nbytes / 1e9:.3f} GB, pinned host -> HBM): {best:.1f} ms, "
+        f"{nbytes / best / 1e6:.1f} GB/s (the post: about 200 ms for 8.75 GB from NVMe)")
+    del host, dst
+    return {"bytes": nbytes, "ms_best": round(best, 2), "ms_mean": round(sum(ms) / len(ms), 2),
+            "GB/s": round(nbytes / best / 1e6, 1)}
 
 
 # ----------------------------------------------------------------- cpu oracle

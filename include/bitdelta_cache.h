@@ -75,6 +75,18 @@ int32_t bitdelta_cache_slot_of(const bd_delta_cache *cache, int32_t variant);
 void bitdelta_cache_counters(const bd_delta_cache *cache, int64_t *hits, int64_t *misses, int64_t *joins,
                              int64_t *evictions, int64_t *busy);
 
+/* A loader the library provides: variant v's slot_bytes bytes are copied
+ * from host_ptrs[v] (host memory, best pinned) to the slot with
+ * hipMemcpyAsync on `stream`, which is then synchronised.  Pass
+ * bitdelta_cache_host_loader as the loader and a bd_host_loader as `user`;
+ * the struct and the table must outlive the cache.  Returns 0, or the HIP
+ * error code. */
+typedef struct {
+    const void *const *host_ptrs;
+    void *stream;
+} bd_host_loader;
+int bitdelta_cache_host_loader(void *user, int32_t variant, void *dst, size_t slot_bytes);
+
 #ifdef __cplusplus
 }
 #endif

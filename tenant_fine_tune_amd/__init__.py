@@ -59,6 +59,7 @@ EXPORTS = {
     "bitdelta_cache_release": (_INT, [_P, _I32]),
     "bitdelta_cache_slot_of": (_I32, [_P, _I32]),
     "bitdelta_cache_counters": (None, [_P, _P, _P, _P, _P, _P]),
+    "bitdelta_cache_host_loader": (_INT, [_P, _I32, _P, _SZ]),
 }
 
 # bd_delta_loader: int (*)(void *user, int32_t variant, void *dst, size_t slot_bytes)
@@ -253,17 +254,37 @@ class DeltaCache:
     fills a slot (0 = success); `slots` is a device tensor of at least
     n_slots * slot_bytes bytes that must outlive the cache."""
 
-    def __init__(self, n_variants, n_slots, n_pinned, window, slots, slot_bytes, loader):
+    def __init__(self, n_variants, n_slots, n_pinned, window, slots, slot_bytes, loader=None, host=None):
+        """Either `loader` (a Python callable) or `host`: a list of n_variants
+        host tensors (pinned, slot_bytes each), copied by the library's own
+        loader (bitdelta_cache_host_loader) on the current stream."""
         torch = _torch()
         if not isinstance(slots, torch.Tensor) or slots.device.type != "cuda":
             raise TypeError("slots must be a device tensor")
         if slots.numel() * slots.element_size() < n_slots * slot_bytes:
             raise ValueError("slots region too small")
+        if (loader is None) == (host is None):
+            raise ValueError("give exactly one of loader and host")
         self._slots = slots
-        self._cb = LOADER(lambda user, v, dst, n: int(loader(v, dst, n)))
+        if host is not None:
+            if len(host) != n_variants or any(h.numel() * h.element_size() < slot_bytes or h.device.type != "cpu"
+                                              for h in host):
+                raise ValueError("host must hold n_variants host tensors of slot_bytes each")
+            self._host = host
+            self._table = (ctypes.c_void_p * n_variants)(*[h.data_ptr() for h in host])
+
+            class _HostLoader(ctypes.Structure):
+                _fields_ = [("host_ptrs", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+            self._hl = _HostLoader(ctypes.cast(self._table, ctypes.c_void_p), _stream(slots.device))
+            self._cb = ctypes.cast(lib.bitdelta_cache_host_loader, LOADER)
+            user = ctypes.cast(ctypes.pointer(self._hl), ctypes.c_void_p)
+        else:
+            self._cb = LOADER(lambda user, v, dst, n: int(loader(v, dst, n)))
+            user = None
         h = ctypes.c_void_p()
         check(lib.bitdelta_cache_create(n_variants, n_slots, n_pinned, window, _ptr(slots), slot_bytes, self._cb,
-                                        None, ctypes.byref(h)))
+                                        user, ctypes.byref(h)))
         self._h = h
 
     def acquire(self, variant):

@@ -6,6 +6,7 @@
 // Fixed-size slots in a caller-owned device region; one mutex guards the
 // bookkeeping, loads run outside it, and a condition variable wakes the
 // callers that wait for a variant another caller is loading (single flight).
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -200,6 +201,18 @@ void bitdelta_cache_counters(const bd_delta_cache *c, int64_t *hits, int64_t *mi
     if (joins) *joins = c->joins;
     if (evictions) *evictions = c->evictions;
     if (busy) *busy = c->busy;
+}
+
+int bitdelta_cache_host_loader(void *user, int32_t variant, void *dst, size_t slot_bytes)
+{
+    const bd_host_loader *h = static_cast<const bd_host_loader *>(user);
+    if (!h || !h->host_ptrs || !h->host_ptrs[variant])
+        return (int)hipErrorInvalidValue;
+    hipStream_t s = static_cast<hipStream_t>(h->stream);
+    hipError_t e = hipMemcpyAsync(dst, h->host_ptrs[variant], slot_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    return (int)e;
 }
 
 }  // extern "C"
