@@ -49,6 +49,11 @@
 extern "C" {
 #endif
 
+/* Symbols of the library's C ABI; everything else in it is hidden. */
+#ifndef BD_API
+#define BD_API __attribute__((visibility("default")))
+#endif
+
 typedef uint16_t bd_bf16;
 
 typedef enum {
@@ -66,13 +71,13 @@ typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;
 typedef enum { BD_ALPHA_ROW = 0, BD_ALPHA_MATRIX = 1 } bd_alpha_mode;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
-int bitdelta_version(void);
+BD_API int bitdelta_version(void);
 
 /* Human-readable name of a status code (static string). */
-const char *bitdelta_status_string(int status);
+BD_API const char *bitdelta_status_string(int status);
 
 /* Detail of the last non-OK status on this thread (static per thread). */
-const char *bitdelta_last_error(void);
+BD_API const char *bitdelta_last_error(void);
 
 /* ---------------------------------------------------------------- compress
  * "Mathematical Foundation" (Delta, sign, alpha = mean |Delta|) and
@@ -92,8 +97,8 @@ const char *bitdelta_last_error(void);
  * workspace: device scratch of at least bitdelta_compress_workspace() bytes
  * (0 for BD_ALPHA_ROW; 8 * d_out for BD_ALPHA_MATRIX), 8-byte aligned;
  * may be NULL when the query returns 0. */
-size_t bitdelta_compress_workspace(int64_t d_out, int64_t d_in, int alpha_mode);
-bd_status bitdelta_compress(const bd_bf16 *w_base, const void *w_ft, int ft_dtype,
+BD_API size_t bitdelta_compress_workspace(int64_t d_out, int64_t d_in, int alpha_mode);
+BD_API bd_status bitdelta_compress(const bd_bf16 *w_base, const void *w_ft, int ft_dtype,
                             int64_t d_out, int64_t d_in, int alpha_mode,
                             uint8_t *signs, float *alpha,
                             void *workspace, size_t workspace_bytes, void *stream);
@@ -103,7 +108,7 @@ bd_status bitdelta_compress(const bd_bf16 *w_base, const void *w_ft, int ft_dtyp
  * W_eff = W_base + alpha * sign(Delta) as bf16 [d_out, d_in].  (The fused
  * linear below never does this; this call exists for callers that want the
  * dense weight and as the exact reference of the fused path.) */
-bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+BD_API bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
                                int alpha_mode, int64_t d_out, int64_t d_in,
                                bd_bf16 *w_eff, void *stream);
 
@@ -122,8 +127,8 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
  * its contents are scratch on entry and undefined after the call, and two
  * calls in flight at once must not share one.  Too small: BD_EWORKSPACE; a
  * requirement of 2 GiB or more: BD_ESHAPE. */
-size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in);
-bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
+BD_API size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in);
+BD_API bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
                           const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
                           int alpha_mode, int64_t d_out, int64_t d_in,
                           bd_bf16 *y, void *workspace, size_t workspace_bytes, void *stream);
@@ -140,8 +145,8 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m,
  * must be below 2 GiB (BD_ESHAPE otherwise).
  * workspace: at least bitdelta_linear_grouped_workspace() bytes, 16-byte
  * aligned. */
-size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t d_out, int64_t d_in);
-bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids,
+BD_API size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t d_out, int64_t d_in);
+BD_API bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids,
                                   int32_t n_variants, const bd_bf16 *w_base,
                                   const uint8_t *signs, const float *alpha, int alpha_mode,
                                   int64_t d_out, int64_t d_in, bd_bf16 *y,
@@ -172,8 +177,8 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
  * and pair of variants; 0 for one variant), 4-byte aligned; owned by the
  * caller, scratch on entry, undefined after; calls in flight at once must
  * not share one. */
-size_t bitdelta_similarity_workspace(int32_t n_variants, int64_t d_out, int64_t d_in);
-bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alpha_mode,
+BD_API size_t bitdelta_similarity_workspace(int32_t n_variants, int64_t d_out, int64_t d_in);
+BD_API bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alpha_mode,
                               int32_t n_variants, int64_t d_out, int64_t d_in,
                               double *gram, double *cosine,
                               void *workspace, size_t workspace_bytes, void *stream);

@@ -48,12 +48,12 @@ typedef int (*bd_delta_loader)(void *user, int32_t variant, void *dst, size_t sl
  * NULL slots, loader or out, or slot_bytes == 0.  slots: device region of
  * n_slots * slot_bytes bytes, owned by the caller, which must outlive the
  * cache. */
-bd_status bitdelta_cache_create(int32_t n_variants, int32_t n_slots, int32_t n_pinned, int64_t window,
+BD_API bd_status bitdelta_cache_create(int32_t n_variants, int32_t n_slots, int32_t n_pinned, int64_t window,
                                 void *slots, size_t slot_bytes, bd_delta_loader loader, void *user,
                                 bd_delta_cache **out);
 /* Frees the cache's host state; NULL is a no-op.  No acquire may be in
  * progress. */
-void bitdelta_cache_destroy(bd_delta_cache *cache);
+BD_API void bitdelta_cache_destroy(bd_delta_cache *cache);
 
 /* outcome of an acquire */
 enum { BD_CACHE_HIT = 0, BD_CACHE_MISS = 1, BD_CACHE_JOINED = 2 };
@@ -64,15 +64,15 @@ enum { BD_CACHE_HIT = 0, BD_CACHE_MISS = 1, BD_CACHE_JOINED = 2 };
  * load.  Every successful acquire must be matched by one release.  Errors:
  * BD_EINVAL (bad variant or NULL output), BD_EBUSY (no slot can be freed),
  * BD_EDEVICE (the loader failed). */
-bd_status bitdelta_cache_acquire(bd_delta_cache *cache, int32_t variant, void **slot_ptr, int *outcome);
+BD_API bd_status bitdelta_cache_acquire(bd_delta_cache *cache, int32_t variant, void **slot_ptr, int *outcome);
 /* BD_EINVAL when the variant is not held. */
-bd_status bitdelta_cache_release(bd_delta_cache *cache, int32_t variant);
+BD_API bd_status bitdelta_cache_release(bd_delta_cache *cache, int32_t variant);
 
 /* Slot index of a resident variant, -1 otherwise (also for a bad variant). */
-int32_t bitdelta_cache_slot_of(const bd_delta_cache *cache, int32_t variant);
+BD_API int32_t bitdelta_cache_slot_of(const bd_delta_cache *cache, int32_t variant);
 /* Counters since creation: hits, misses (loads started), joins, evictions,
  * refused (BD_EBUSY) requests.  Any pointer may be NULL. */
-void bitdelta_cache_counters(const bd_delta_cache *cache, int64_t *hits, int64_t *misses, int64_t *joins,
+BD_API void bitdelta_cache_counters(const bd_delta_cache *cache, int64_t *hits, int64_t *misses, int64_t *joins,
                              int64_t *evictions, int64_t *busy);
 
 /* A loader the library provides: variant v's slot_bytes bytes are copied
@@ -85,7 +85,7 @@ typedef struct {
     const void *const *host_ptrs;
     void *stream;
 } bd_host_loader;
-int bitdelta_cache_host_loader(void *user, int32_t variant, void *dst, size_t slot_bytes);
+BD_API int bitdelta_cache_host_loader(void *user, int32_t variant, void *dst, size_t slot_bytes);
 
 #ifdef __cplusplus
 }
