@@ -40,6 +40,8 @@ def _bind(lib):
     lib.oracle_linear_grouped_rows.restype = I
     lib.oracle_similarity.argtypes = [P, P, I, ctypes.c_int32, I64, I64, P, P]
     lib.oracle_similarity.restype = I
+    lib.oracle_monosoup.argtypes = [P, P, ctypes.c_int32, I64, I64, ctypes.c_int32, P, P]
+    lib.oracle_monosoup.restype = I
     lib.oracle_num_threads.restype = I
     lib.oracle_set_num_threads.argtypes = [I]
     return lib
@@ -188,6 +190,22 @@ class Oracle:
         return gram, cos
 
 
+    def monosoup(self, w_base, w_ft, rank: int):
+        """MonoSoup merge (R8): W_base + (1/k) sum_i tau_i, tau_i the rank-`rank`
+        truncated SVD of Delta_i = fl32(W_i - W_base).  w_base: uint16 [R, C];
+        w_ft: fp32 [k, R, C].  Returns (merged fp64 [R, C], sigma fp64 [k, min(R, C)])."""
+        lib = self.lib
+        w_base = _c(w_base, np.uint16)
+        w_ft = _c(w_ft, np.float32)
+        k, R, C = w_ft.shape
+        out = np.zeros((R, C), dtype=np.float64)
+        sig = np.zeros((k, min(R, C)), dtype=np.float64)
+        rc = lib.oracle_monosoup(_ptr(w_base), _ptr(w_ft), k, R, C, rank, _ptr(out), _ptr(sig))
+        if rc != 0:
+            raise ValueError(f"oracle_monosoup failed ({rc})")
+        return out, sig
+
+
 _default = None
 
 
@@ -232,3 +250,7 @@ def linear_grouped(*a, **k):
 
 def similarity(*a, **k):
     return default().similarity(*a, **k)
+
+
+def monosoup(*a, **k):
+    return default().monosoup(*a, **k)

@@ -20,6 +20,10 @@
  *   [KM]  "K-Merge: Online LoRA Adapter Management for the Edge": step 1 of
  *         its policy compares a new adapter with every pooled one by the
  *         cosine similarity of their task vectors.
+ *   [MS]  "MonoSoup" (a single-checkpoint complement by SVD): the task
+ *         vectors Delta_i = W_i - W_base of k checkpoints are each cut to
+ *         their rank-r truncated SVD tau_i, and W_merged = W_base +
+ *         (1/k) sum_i tau_i.
  *
  * Readings where the post is silent (each one is listed in the design notes):
  *   R1 sign(0): Delta >= 0 (including -0) is stored as bit 1 = +1; bit 0 = -1.
@@ -37,6 +41,10 @@
  *      server holds, tau[r][j] = alpha[r] * s[r][j] with s = +1 for bit 1 and
  *      -1 for bit 0; the similarity of two variants is the cosine of their
  *      task vectors over one matrix, from the dot products (Gram matrix).
+ *   R8 MonoSoup ([MS]): Delta_i = fl32(W_i - f32(W_base)) as in R3, then
+ *      fp64; tau_i = the exact rank-r truncated SVD (the r largest singular
+ *      values and their vectors), computed here by one-sided Jacobi in fp64;
+ *      W_merged returned in fp64.
  *
  * Fixed order for the Gram matrix (R7).  For variants a, b and row r,
  * c_ab[r] = sum_j s_a[r][j] s_b[r][j] is an integer (exact).  The row term is
@@ -313,6 +321,111 @@ int oracle_similarity(const uint8_t *signs, const float *alpha, int per_matrix, 
             double d = sqrt(na * nb);
             cosv[(int64_t)a * V + b] = d > 0.0 ? gram[(int64_t)a * V + b] / d : 0.0;
         }
+    return 0;
+}
+
+/* ---- MonoSoup merge ([MS], R8) ------------------------------------------ */
+
+/* One-sided Jacobi (Hestenes): rotate column pairs of A [R, C] (row-major,
+ * overwritten) until every pair is orthogonal to 1e-15 relative; V [C, C]
+ * accumulates the rotations.  Afterwards column j of A is sigma_j u_j and
+ * A = (A V^T) V, i.e. Delta = sum_j A[:, j] V[:, j]^T. */
+static void jacobi_columns(double *A, int64_t R, int64_t C, double *V)
+{
+    for (int64_t i = 0; i < C * C; ++i)
+        V[i] = 0.0;
+    for (int64_t i = 0; i < C; ++i)
+        V[i * C + i] = 1.0;
+    for (int sweep = 0; sweep < 80; ++sweep) {
+        int rotated = 0;
+        for (int64_t p = 0; p < C - 1; ++p)
+            for (int64_t q = p + 1; q < C; ++q) {
+                double alpha = 0.0, beta = 0.0, gamma = 0.0;
+                for (int64_t i = 0; i < R; ++i) {
+                    double ap = A[i * C + p], aq = A[i * C + q];
+                    alpha += ap * ap;
+                    beta += aq * aq;
+                    gamma += ap * aq;
+                }
+                if (gamma == 0.0 || fabs(gamma) <= 1e-15 * sqrt(alpha * beta))
+                    continue;
+                rotated = 1;
+                double zeta = (beta - alpha) / (2.0 * gamma);
+                double tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+                double c = 1.0 / sqrt(1.0 + tt * tt), s = c * tt;
+                for (int64_t i = 0; i < R; ++i) {
+                    double ap = A[i * C + p], aq = A[i * C + q];
+                    A[i * C + p] = c * ap - s * aq;
+                    A[i * C + q] = s * ap + c * aq;
+                }
+                for (int64_t i = 0; i < C; ++i) {
+                    double vp = V[i * C + p], vq = V[i * C + q];
+                    V[i * C + p] = c * vp - s * vq;
+                    V[i * C + q] = s * vp + c * vq;
+                }
+            }
+        if (!rotated)
+            break;
+    }
+}
+
+/* w_base: bf16 [R, C]; w_ft: fp32 [k, R, C] (the k checkpoints); rank r in
+ * [0, min(R, C)]; out: fp64 [R, C] = W_base + (1/k) sum_i tau_i.
+ * sigma (may be NULL): fp64 [k, min(R, C)], each checkpoint's singular
+ * values in decreasing order.  Returns 0, or -1 on a bad size or no memory. */
+int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_t R, int64_t C, int32_t r,
+                    double *out, double *sigma)
+{
+    const int64_t n = R < C ? R : C;
+    if (k < 1 || R < 1 || C < 1 || r < 0 || r > n)
+        return -1;
+    double *A = malloc(sizeof(double) * R * C), *V = malloc(sizeof(double) * C * C);
+    double *norm = malloc(sizeof(double) * C);
+    int64_t *order = malloc(sizeof(int64_t) * C);
+    if (!A || !V || !norm || !order) {
+        free(A); free(V); free(norm); free(order);
+        return -1;
+    }
+    for (int64_t i = 0; i < R * C; ++i)
+        out[i] = 0.0; /* sum of the tau_i until the end */
+    for (int32_t ck = 0; ck < k; ++ck) {
+        const float *wi = w_ft + (int64_t)ck * R * C;
+        for (int64_t i = 0; i < R * C; ++i)
+            A[i] = (double)(wi[i] - oracle_f32_from_bf16(w_base[i]));
+        jacobi_columns(A, R, C, V);
+        for (int64_t j = 0; j < C; ++j) {
+            double s = 0.0;
+            for (int64_t i = 0; i < R; ++i)
+                s += A[i * C + j] * A[i * C + j];
+            norm[j] = sqrt(s);
+            order[j] = j;
+        }
+        /* columns by decreasing singular value (insertion sort, ties by index) */
+        for (int64_t a = 1; a < C; ++a) {
+            int64_t v = order[a], b = a;
+            while (b > 0 && norm[order[b - 1]] < norm[v]) {
+                order[b] = order[b - 1];
+                --b;
+            }
+            order[b] = v;
+        }
+        if (sigma)
+            for (int64_t j = 0; j < n; ++j)
+                sigma[(int64_t)ck * n + j] = norm[order[j]];
+        /* tau_i = sum over the r largest of A[:, j] V[:, j]^T */
+        for (int64_t i = 0; i < R; ++i)
+            for (int64_t c = 0; c < C; ++c) {
+                double s = 0.0;
+                for (int32_t t = 0; t < r; ++t) {
+                    int64_t j = order[t];
+                    s += A[i * C + j] * V[c * C + j];
+                }
+                out[i * C + c] += s;
+            }
+    }
+    for (int64_t i = 0; i < R * C; ++i)
+        out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i] / (double)k;
+    free(A); free(V); free(norm); free(order);
     return 0;
 }
 

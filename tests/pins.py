@@ -417,8 +417,95 @@ def pin_similarity_invariants(o):
         assert abs(cos[a, b]) < 6.0 / math.sqrt(R * C)
 
 
+def _orthonormal(rng, n, k):
+    q, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    return q
+
+
+def _bf16_normal(rng, shape, std):
+    return _torch_bf16_bits((std * rng.standard_normal(shape)).astype(np.float32))
+
+
+def pin_monosoup_known_svd(o):
+    """MonoSoup's rank-r truncation on task vectors built with a known SVD
+    (orthonormal U, V from a QR, distinct singular values): the singular
+    values come back in decreasing order, the merge of k = 1 equals W_base +
+    U_r S_r V_r^T, and with two checkpoints the merge is W_base plus the mean
+    of the two closed-form truncations.  Tall and wide shapes; W_base nonzero,
+    so the task vector must be W_i - W_base.  Tolerances: fp32 rounding of W_i
+    (the task vector is the fp32 difference)."""
+    rng = np.random.default_rng(61)
+    for R, C in ((48, 20), (18, 40)):
+        n = min(R, C)
+        wb = _bf16_normal(rng, (R, C), 0.02)
+        base = _torch_widen(wb).astype(np.float64)
+        s = np.sort(rng.uniform(0.1, 1.0, n))[::-1] * np.geomspace(1.0, 0.05, n)
+        taus, wfs, sig_true = [], [], []
+        for _ in range(2):
+            U, V = _orthonormal(rng, R, n), _orthonormal(rng, C, n)
+            si = s * rng.uniform(0.9, 1.1)
+            wfs.append((base + (U * si) @ V.T).astype(np.float32))
+            taus.append(lambda r, U=U, V=V, si=si: (U[:, :r] * si[:r]) @ V[:, :r].T)
+            sig_true.append(si)
+        for r in (1, 3, n - 2):
+            m1, sig = o.monosoup(wb, wfs[0][None], r)
+            assert np.allclose(sig[0], sig_true[0], rtol=0, atol=2e-6), r
+            assert np.all(np.diff(sig[0]) <= 0)
+            assert np.abs(m1 - (base + taus[0](r))).max() <= 2e-6, r
+            m2, sig2 = o.monosoup(wb, np.stack(wfs), r)
+            assert np.allclose(sig2[1], sig_true[1], rtol=0, atol=2e-6), r
+            assert np.abs(m2 - (base + 0.5 * (taus[0](r) + taus[1](r)))).max() <= 2e-6, r
+
+
+def pin_monosoup_vs_numpy(o):
+    """Full-rank random task vectors, k = 3, rank 4: the merge equals
+    W_base + (1/3) sum_i U_i,4 S_i,4 Vh_i,4 from numpy's LAPACK SVD of the same
+    fp32 differences, to a relative 1e-10; the singular values match numpy's."""
+    rng = np.random.default_rng(62)
+    R, C, k, r = 30, 26, 3, 4
+    wb = _bf16_normal(rng, (R, C), 0.02)
+    base = _torch_widen(wb)
+    wf = (base[None] + 1e-3 * rng.standard_normal((k, R, C))).astype(np.float32)
+    m, sig = o.monosoup(wb, wf, r)
+    acc = np.zeros((R, C))
+    for i in range(k):
+        d = (wf[i] - base).astype(np.float64)     # fp32 subtraction, then widened
+        u, sv, vh = np.linalg.svd(d, full_matrices=False)
+        assert np.allclose(sig[i], sv, rtol=1e-12, atol=1e-18)
+        acc += (u[:, :r] * sv[:r]) @ vh[:r]
+    ref = base.astype(np.float64) + acc / k
+    scale = np.abs(acc / k).max()
+    assert np.abs(m - ref).max() <= 1e-10 * scale
+
+
+def pin_monosoup_special_cases(o):
+    """Rank 0 gives W_base exactly; full rank with k = 1 gives W_base plus the
+    whole fp32 difference (every component kept); k identical checkpoints merge as one; Eckart-Young: the
+    squared residual of the rank-r truncation equals the sum of the dropped
+    squared singular values; the frobenius norm of Delta equals the norm of
+    its singular values."""
+    rng = np.random.default_rng(63)
+    R, C = 21, 17
+    wb = _bf16_normal(rng, (R, C), 0.02)
+    base = _torch_widen(wb).astype(np.float64)
+    wf = (base + 1e-3 * rng.standard_normal((R, C))).astype(np.float32)
+    d = (wf - base.astype(np.float32)).astype(np.float64)    # the fp32 difference
+    m0, _ = o.monosoup(wb, wf[None], 0)
+    assert np.array_equal(m0, base)
+    mf, sig = o.monosoup(wb, wf[None], min(R, C))
+    assert np.abs(mf - (base + d)).max() <= 1e-15
+    assert abs(np.sqrt(np.sum(sig[0] ** 2)) - np.linalg.norm(d)) <= 1e-13 * np.linalg.norm(d)
+    for r in (2, 9):
+        m1, _ = o.monosoup(wb, wf[None], r)
+        m3, _ = o.monosoup(wb, np.stack([wf, wf, wf]), r)
+        assert np.abs(m3 - m1).max() <= 1e-16
+        resid = np.sum((d - (m1 - base)) ** 2)
+        assert abs(resid - np.sum(sig[0][r:] ** 2)) <= 1e-10 * np.sum(d ** 2)
+
+
 ALL = [pin_bf16_widen, pin_bf16_round, pin_bf16_hand_ties, pin_compress_handbuilt,
        pin_compress_packing_vs_numpy, pin_alpha_exact_mean, pin_alpha_laplace,
        pin_alpha_least_squares, pin_reconstruct_hand_cases, pin_reconstruct_vs_torch,
        pin_linear_exact_rational, pin_linear_vs_numpy, pin_linear_dyadic, pin_grouped,
-       pin_shape_4096, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants]
+       pin_shape_4096, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants,
+       pin_monosoup_known_svd, pin_monosoup_vs_numpy, pin_monosoup_special_cases]

@@ -42,6 +42,15 @@ MUTANTS = {
     "similarity_alpha_twice": ("double term = ((double)fa * (double)fb) * (double)c;",
                                "double term = ((double)fa * (double)fa) * (double)c;"),
     "similarity_no_sqrt": ("double d = sqrt(na * nb);", "double d = na * nb;"),
+    "monosoup_no_mean": ("out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i] / (double)k;",
+                         "out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i];"),
+    "monosoup_smallest_first": ("while (b > 0 && norm[order[b - 1]] < norm[v])",
+                                "while (b > 0 && norm[order[b - 1]] > norm[v])"),
+    "monosoup_no_base": ("A[i] = (double)(wi[i] - oracle_f32_from_bf16(w_base[i]));", "A[i] = (double)wi[i];"),
+    "monosoup_v_transposed": ("s += A[i * C + j] * V[c * C + j];", "s += A[i * C + j] * V[j * C + c];"),
+    "monosoup_rotation_sign": ("A[i * C + p] = c * ap - s * aq;", "A[i * C + p] = c * ap + s * aq;"),
+    "monosoup_first_checkpoint": ("const float *wi = w_ft + (int64_t)ck * R * C;", "const float *wi = w_ft;"),
+    "monosoup_rank_minus_one": ("for (int32_t t = 0; t < r; ++t)", "for (int32_t t = 1; t < r; ++t)"),
     "similarity_row_of_b": ("const uint8_t *rb = signs + ((int64_t)b * R + r) * G;",
                             "const uint8_t *rb = signs + ((int64_t)a * R + r) * G;"),
 }
