@@ -326,42 +326,48 @@ int oracle_similarity(const uint8_t *signs, const float *alpha, int per_matrix, 
 
 /* ---- MonoSoup merge ([MS], R8) ------------------------------------------ */
 
-/* One-sided Jacobi (Hestenes): rotate column pairs of A [R, C] (row-major,
- * overwritten) until every pair is orthogonal to 1e-15 relative; V [C, C]
- * accumulates the rotations.  Afterwards column j of A is sigma_j u_j and
- * A = (A V^T) V, i.e. Delta = sum_j A[:, j] V[:, j]^T. */
-static void jacobi_columns(double *A, int64_t R, int64_t C, double *V)
+/* One-sided Jacobi (Hestenes): rotate column pairs of A [m, n] (row-major,
+ * overwritten, m >= n) until every pair is orthogonal to 1e-15 relative; V
+ * [n, n] accumulates the rotations.  Afterwards column j of A is sigma_j u_j
+ * and A = (A V^T) V, i.e. the input equals sum_j A[:, j] V[:, j]^T.  Columns
+ * whose squared norm is below 1e-30 of the whole matrix's (singular values
+ * under 1e-15 of its norm) are left alone. */
+static void jacobi_columns(double *A, int64_t m, int64_t n, double *V)
 {
-    for (int64_t i = 0; i < C * C; ++i)
+    double frob2 = 0.0;
+    for (int64_t i = 0; i < m * n; ++i)
+        frob2 += A[i] * A[i];
+    const double tiny = 1e-30 * frob2;
+    for (int64_t i = 0; i < n * n; ++i)
         V[i] = 0.0;
-    for (int64_t i = 0; i < C; ++i)
-        V[i * C + i] = 1.0;
+    for (int64_t i = 0; i < n; ++i)
+        V[i * n + i] = 1.0;
     for (int sweep = 0; sweep < 80; ++sweep) {
         int rotated = 0;
-        for (int64_t p = 0; p < C - 1; ++p)
-            for (int64_t q = p + 1; q < C; ++q) {
+        for (int64_t p = 0; p < n - 1; ++p)
+            for (int64_t q = p + 1; q < n; ++q) {
                 double alpha = 0.0, beta = 0.0, gamma = 0.0;
-                for (int64_t i = 0; i < R; ++i) {
-                    double ap = A[i * C + p], aq = A[i * C + q];
+                for (int64_t i = 0; i < m; ++i) {
+                    double ap = A[i * n + p], aq = A[i * n + q];
                     alpha += ap * ap;
                     beta += aq * aq;
                     gamma += ap * aq;
                 }
-                if (gamma == 0.0 || fabs(gamma) <= 1e-15 * sqrt(alpha * beta))
+                if (gamma == 0.0 || alpha <= tiny || beta <= tiny || fabs(gamma) <= 1e-15 * sqrt(alpha * beta))
                     continue;
                 rotated = 1;
                 double zeta = (beta - alpha) / (2.0 * gamma);
                 double tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
                 double c = 1.0 / sqrt(1.0 + tt * tt), s = c * tt;
-                for (int64_t i = 0; i < R; ++i) {
-                    double ap = A[i * C + p], aq = A[i * C + q];
-                    A[i * C + p] = c * ap - s * aq;
-                    A[i * C + q] = s * ap + c * aq;
+                for (int64_t i = 0; i < m; ++i) {
+                    double ap = A[i * n + p], aq = A[i * n + q];
+                    A[i * n + p] = c * ap - s * aq;
+                    A[i * n + q] = s * ap + c * aq;
                 }
-                for (int64_t i = 0; i < C; ++i) {
-                    double vp = V[i * C + p], vq = V[i * C + q];
-                    V[i * C + p] = c * vp - s * vq;
-                    V[i * C + q] = s * vp + c * vq;
+                for (int64_t i = 0; i < n; ++i) {
+                    double vp = V[i * n + p], vq = V[i * n + q];
+                    V[i * n + p] = c * vp - s * vq;
+                    V[i * n + q] = s * vp + c * vq;
                 }
             }
         if (!rotated)
@@ -372,16 +378,20 @@ static void jacobi_columns(double *A, int64_t R, int64_t C, double *V)
 /* w_base: bf16 [R, C]; w_ft: fp32 [k, R, C] (the k checkpoints); rank r in
  * [0, min(R, C)]; out: fp64 [R, C] = W_base + (1/k) sum_i tau_i.
  * sigma (may be NULL): fp64 [k, min(R, C)], each checkpoint's singular
- * values in decreasing order.  Returns 0, or -1 on a bad size or no memory. */
+ * values in decreasing order.  A wide task vector (C > R) is decomposed as
+ * its transpose (the same singular values, the vectors swapped), so the
+ * Jacobi always works on min(R, C) columns.  Returns 0, or -1 on a bad size
+ * or no memory. */
 int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_t R, int64_t C, int32_t r,
                     double *out, double *sigma)
 {
-    const int64_t n = R < C ? R : C;
+    const int64_t n = R < C ? R : C, m = R < C ? C : R;
+    const int wide = C > R;
     if (k < 1 || R < 1 || C < 1 || r < 0 || r > n)
         return -1;
-    double *A = malloc(sizeof(double) * R * C), *V = malloc(sizeof(double) * C * C);
-    double *norm = malloc(sizeof(double) * C);
-    int64_t *order = malloc(sizeof(int64_t) * C);
+    double *A = malloc(sizeof(double) * m * n), *V = malloc(sizeof(double) * n * n);
+    double *norm = malloc(sizeof(double) * n);
+    int64_t *order = malloc(sizeof(int64_t) * n);
     if (!A || !V || !norm || !order) {
         free(A); free(V); free(norm); free(order);
         return -1;
@@ -390,18 +400,25 @@ int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_
         out[i] = 0.0; /* sum of the tau_i until the end */
     for (int32_t ck = 0; ck < k; ++ck) {
         const float *wi = w_ft + (int64_t)ck * R * C;
-        for (int64_t i = 0; i < R * C; ++i)
-            A[i] = (double)(wi[i] - oracle_f32_from_bf16(w_base[i]));
-        jacobi_columns(A, R, C, V);
-        for (int64_t j = 0; j < C; ++j) {
+        /* A = Delta_i [R, C], or its transpose [C, R] when wide */
+        for (int64_t i = 0; i < R; ++i)
+            for (int64_t c = 0; c < C; ++c) {
+                double d = (double)(wi[i * C + c] - oracle_f32_from_bf16(w_base[i * C + c]));
+                if (wide)
+                    A[c * n + i] = d;
+                else
+                    A[i * n + c] = d;
+            }
+        jacobi_columns(A, m, n, V);
+        for (int64_t j = 0; j < n; ++j) {
             double s = 0.0;
-            for (int64_t i = 0; i < R; ++i)
-                s += A[i * C + j] * A[i * C + j];
+            for (int64_t i = 0; i < m; ++i)
+                s += A[i * n + j] * A[i * n + j];
             norm[j] = sqrt(s);
             order[j] = j;
         }
         /* columns by decreasing singular value (insertion sort, ties by index) */
-        for (int64_t a = 1; a < C; ++a) {
+        for (int64_t a = 1; a < n; ++a) {
             int64_t v = order[a], b = a;
             while (b > 0 && norm[order[b - 1]] < norm[v]) {
                 order[b] = order[b - 1];
@@ -412,15 +429,16 @@ int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_
         if (sigma)
             for (int64_t j = 0; j < n; ++j)
                 sigma[(int64_t)ck * n + j] = norm[order[j]];
-        /* tau_i = sum over the r largest of A[:, j] V[:, j]^T */
-        for (int64_t i = 0; i < R; ++i)
-            for (int64_t c = 0; c < C; ++c) {
+        /* truncation of A = sum over the r largest of A[:, j] V[:, j]^T; tau_i
+         * is that, or its transpose when wide */
+        for (int64_t i = 0; i < m; ++i)
+            for (int64_t c = 0; c < n; ++c) {
                 double s = 0.0;
                 for (int32_t t = 0; t < r; ++t) {
                     int64_t j = order[t];
-                    s += A[i * C + j] * V[c * C + j];
+                    s += A[i * n + j] * V[c * n + j];
                 }
-                out[i * C + c] += s;
+                out[wide ? c * C + i : i * C + c] += s;
             }
     }
     for (int64_t i = 0; i < R * C; ++i)

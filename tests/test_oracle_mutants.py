@@ -46,9 +46,12 @@ MUTANTS = {
                          "out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i];"),
     "monosoup_smallest_first": ("while (b > 0 && norm[order[b - 1]] < norm[v])",
                                 "while (b > 0 && norm[order[b - 1]] > norm[v])"),
-    "monosoup_no_base": ("A[i] = (double)(wi[i] - oracle_f32_from_bf16(w_base[i]));", "A[i] = (double)wi[i];"),
-    "monosoup_v_transposed": ("s += A[i * C + j] * V[c * C + j];", "s += A[i * C + j] * V[j * C + c];"),
-    "monosoup_rotation_sign": ("A[i * C + p] = c * ap - s * aq;", "A[i * C + p] = c * ap + s * aq;"),
+    "monosoup_no_base": ("double d = (double)(wi[i * C + c] - oracle_f32_from_bf16(w_base[i * C + c]));",
+                         "double d = (double)wi[i * C + c];"),
+    "monosoup_v_transposed": ("s += A[i * n + j] * V[c * n + j];", "s += A[i * n + j] * V[j * n + c];"),
+    "monosoup_rotation_sign": ("A[i * n + p] = c * ap - s * aq;", "A[i * n + p] = c * ap + s * aq;"),
+    "monosoup_sigma_of_first_column": ("sigma[(int64_t)ck * n + j] = norm[order[j]];",
+                                       "sigma[(int64_t)ck * n + j] = norm[order[0]];"),
     "monosoup_first_checkpoint": ("const float *wi = w_ft + (int64_t)ck * R * C;", "const float *wi = w_ft;"),
     "monosoup_rank_minus_one": ("for (int32_t t = 0; t < r; ++t)", "for (int32_t t = 1; t < r; ++t)"),
     "similarity_row_of_b": ("const uint8_t *rb = signs + ((int64_t)b * R + r) * G;",
