@@ -80,6 +80,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
+    p.add_argument("--no-monosoup", action="store_true")
     p.add_argument("--no-context", action="store_true",
                    help="skip the vendor-library reference points (read stream, plain GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
@@ -402,6 +403,66 @@ def run_similarity(torch, bd, signs, alpha, reps=20):
     return {"variants": V, "d_out": N, "d_in": K, "us": round(us, 2), "us_median5": round(statistics.median(rep_us), 2),
             "us_min5": round(min(rep_us), 2), "bytes": nbytes, "GB/s": round(gbs, 1),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# ---------------------------------------------------------------- monosoup
+
+MS_SHAPE = (8192, 8192)
+MS_K, MS_RANK, MS_POWER = 2, 32, 1
+
+
+def run_monosoup(torch, bd, synth, reps=3):
+    """MonoSoup merge (section "MonoSoup"): the current and the best earlier
+    checkpoint (k = 2) of an 8192 x 8192 matrix merged through their rank-32
+    truncations, one power iteration, sketch of 64 columns; task vectors of
+    rank 32 (entry RMS 1e-3) plus N(0, 1e-5^2) noise.  Each Delta pass reads
+    both checkpoints (fp32) and the base (bf16): 6 bytes and 2 * 64 flops per
+    weight and checkpoint; 2 + 2 * power_iters passes, then the merge reads
+    the base and writes fp32 (6 bytes per weight, 2 * k * rp flops)."""
+    R, C = MS_SHAPE
+    k, r, q = MS_K, MS_RANK, MS_POWER
+    dev = torch.device("cuda")
+    wb, wf = synth.device_checkpoints(R, C, k, r, 1e-5, seed=5)
+    om = synth.device_normal((C, bd.MONOSOUP_SKETCH), 1.0, 5, synth.tag(synth.TAG_OMEGA), dev)
+    out = torch.empty((R, C), dtype=torch.float32, device=dev)
+    sig = torch.empty((k, r), dtype=torch.float64, device=dev)
+    nws = bd.lib.bitdelta_monosoup_workspace(R, C, k, r)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bd.check(bd.lib.bitdelta_monosoup(P(wb.data_ptr()), P(wf.data_ptr()), P(om.data_ptr()), k, R, C, r, q,
+                                          P(out.data_ptr()), P(sig.data_ptr()), P(ws.data_ptr()), nws,
+                                          P(stream.cuda_stream)))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    rep_us = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_us.append(e0.elapsed_time(e1) / reps * 1e3)
+    us = sum(rep_us) / 5
+    passes = 2 + 2 * q
+    rp = (r + 15) // 16 * 16
+    pass_flops = 2.0 * R * C * bd.MONOSOUP_SKETCH * k
+    flops = passes * pass_flops + 2.0 * R * C * k * rp
+    nbytes = passes * R * C * k * 6 + R * C * 6
+    log(f"monosoup k={k} [{R},{C}] rank {r}, {q} power iteration(s): {us / 1e3:.3f} ms per merge, "
+        f"{flops / us / 1e6:.1f} TFLOP/s, {nbytes / us / 1e3:.1f} GB/s over {passes} passes + merge")
+    res = {"k": k, "rows": R, "cols": C, "rank": r, "power_iters": q, "sketch": bd.MONOSOUP_SKETCH,
+           "us": round(us, 1), "us_median5": round(statistics.median(rep_us), 1), "us_min5": round(min(rep_us), 1),
+           "passes": passes, "flops": flops, "bytes": nbytes, "TFLOP/s": round(flops / us / 1e6, 1),
+           "GB/s": round(nbytes / us / 1e3, 1)}
+    del wb, wf, om, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 # ----------------------------------------------------------------- context
@@ -911,6 +972,7 @@ def main():
 
     prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
     grouped, similarity = (None, None) if args.no_grouped else run_grouped(torch, bd, synth)
+    monosoup = None if args.no_monosoup else run_monosoup(torch, bd, synth)
     context = None if args.no_context else run_context(torch)
     if context is not None and prefill is not None:
         context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill)
@@ -938,6 +1000,7 @@ def main():
         "prefill": prefill,
         "grouped": grouped,
         "similarity": similarity,
+        "monosoup": monosoup,
         "context": context,
         "cpu_baseline": cpu,
     }

@@ -183,6 +183,43 @@ BD_API bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, i
                               double *gram, double *cosine,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- MonoSoup
+ * "BitDelta: Serving 14 Zen Models from One GPU Cluster", section "MonoSoup":
+ * k fine-tuned checkpoints W_1..W_k of one matrix are merged through the
+ * rank-r truncated SVD tau_i of each task vector Delta_i = W_i - W_base:
+ *   W_merged = W_base + (1/k) sum_i tau_i.
+ * Delta_i is the fp32 difference fl32(W_i - f32(W_base)).  The truncation is
+ * computed by a randomized range finder with a sketch of
+ * BD_MONOSOUP_SKETCH (64) columns: Y = Delta Omega, then power_iters rounds
+ * of Y <- Delta (Delta^T Y) with the sketch re-orthonormalised between
+ * products, then the exact rank-r truncation of the projection of Delta onto
+ * range(Y).  It equals the exact truncated SVD when Delta has rank at most
+ * 64; otherwise its distance from it shrinks with the gap between the r-th
+ * and the 65th singular value and with power_iters.
+ *   w_base: bf16 [rows, cols], 8-byte aligned.
+ *   w_ft:   fp32 [k, rows, cols] (checkpoint i at offset i*rows*cols),
+ *           16-byte aligned.
+ *   omega:  fp32 [cols, 64], 16-byte aligned: the test matrix, normally
+ *           i.i.d. N(0, 1) drawn by the caller (unused, may be NULL, when
+ *           rank is 0).
+ *   rank:   r in [0, min(64, rows, cols)]; power_iters in [0, 4]
+ *           (BD_EINVAL otherwise); k in [1, 64] (BD_EINVAL).
+ *   rows >= 1, cols >= 4 a multiple of 4, both at most 2^21 (BD_ESHAPE).
+ *   w_merged: fp32 [rows, cols], 16-byte aligned: f32(W_base) + the fp32
+ *           contraction of the k rank-r factors.
+ *   sigma:  NULL, or fp64 [k, rank], 8-byte aligned: the estimated leading
+ *           singular values of each Delta_i, decreasing.
+ * workspace: at least bitdelta_monosoup_workspace() bytes (0 for rank 0),
+ * 256-byte aligned; owned by the caller, scratch on entry, undefined after;
+ * calls in flight at once must not share one.  The result is deterministic
+ * (every reduction runs in a fixed order). */
+#define BD_MONOSOUP_SKETCH 64
+BD_API size_t bitdelta_monosoup_workspace(int64_t rows, int64_t cols, int32_t k, int32_t rank);
+BD_API bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, const float *omega,
+                            int32_t k, int64_t rows, int64_t cols, int32_t rank, int32_t power_iters,
+                            float *w_merged, double *sigma,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ import os
 
 import numpy as np
 
-TAG_WBASE, TAG_DELTA, TAG_X, TAG_IDS, TAG_SCALE, TAG_VARIANT = 1, 2, 3, 4, 5, 16
+TAG_WBASE, TAG_DELTA, TAG_X, TAG_IDS, TAG_SCALE, TAG_FACTOR, TAG_NOISE, TAG_OMEGA, TAG_VARIANT = \
+    1, 2, 3, 4, 5, 6, 7, 8, 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
@@ -115,6 +116,44 @@ def variant_ft(w_base: np.ndarray, v: int, b: float, seed: int = 0, index: int =
     return bf16_bits_to_f32(w_base) + delta
 
 
+def lowrank_spectrum(rank: int, rms: float, d_out: int, d_in: int) -> np.ndarray:
+    """Singular values s_j = s_0 10^(-j/(rank-1)) (one decade), scaled so the
+    low-rank part has entry RMS `rms` over a [d_out, d_in] matrix."""
+    if rank == 0:
+        return np.zeros(0)
+    s = np.power(10.0, -np.arange(rank) / max(rank - 1, 1))
+    return s * (rms * math.sqrt(d_out * d_in) / math.sqrt(float(np.sum(s * s))))
+
+
+def checkpoints(d_out: int, d_in: int, k: int, rank: int, noise: float, rms: float = 1e-3, seed: int = 0,
+                index: int = 0, std: float = 0.02):
+    """k fine-tuned checkpoints of one matrix over a shared base whose task
+    vectors are low rank plus a noise floor: Delta_i = G_i diag(s) H_i^T + E_i,
+    G_i [d_out, rank] ~ N(0, 1/d_out), H_i [d_in, rank] ~ N(0, 1/d_in),
+    s = lowrank_spectrum(rank, rms, ...), E_i ~ N(0, noise^2) entries.
+    Returns W_base bf16 bits [d_out, d_in] and W_ft = fl32(W_base + fl32(Delta_i))
+    fp32 [k, d_out, d_in]."""
+    w_base = to_bf16_bits(normal_f32((d_out, d_in), std, seed, tag(TAG_WBASE, index)))
+    base = bf16_bits_to_f32(w_base)
+    s = lowrank_spectrum(rank, rms, d_out, d_in)
+    w_ft = np.empty((k, d_out, d_in), dtype=np.float32)
+    for i in range(k):
+        g = normal_f32((d_out, rank), 1.0 / math.sqrt(d_out), seed,
+                       tag(TAG_FACTOR, index + (1 << 20) * (2 * i))).astype(np.float64)
+        h = normal_f32((d_in, rank), 1.0 / math.sqrt(d_in), seed,
+                       tag(TAG_FACTOR, index + (1 << 20) * (2 * i + 1))).astype(np.float64)
+        delta = (g * s) @ h.T
+        if noise > 0:
+            delta += normal_f32((d_out, d_in), noise, seed, tag(TAG_NOISE, index + (1 << 20) * i))
+        w_ft[i] = base + delta.astype(np.float32)
+    return w_base, w_ft
+
+
+def omega(d_in: int, width: int = 64, seed: int = 0, index: int = 0) -> np.ndarray:
+    """Gaussian test matrix [d_in, width], i.i.d. N(0, 1) fp32."""
+    return normal_f32((d_in, width), 1.0, seed, tag(TAG_OMEGA, index))
+
+
 def activations(m: int, d_in: int, seed: int = 0, index: int = 0) -> np.ndarray:
     """x ~ N(0, 1), bf16 bits [m, d_in]."""
     return to_bf16_bits(normal_f32((m, d_in), 1.0, seed, tag(TAG_X, index)))
@@ -188,6 +227,28 @@ def device_layer(d_out: int, d_in: int, seed: int = 0, index: int = 0, b: float 
 
     w_base = device_normal((d_out, d_in), std, seed, tag(TAG_WBASE, index), device, torch.bfloat16)
     w_ft = w_base.float().add_(device_laplace((d_out, d_in), b, seed, tag(TAG_DELTA, index), device))
+    return w_base, w_ft
+
+
+def device_checkpoints(d_out: int, d_in: int, k: int, rank: int, noise: float, rms: float = 1e-3, seed: int = 0,
+                       index: int = 0, std: float = 0.02, device="cuda"):
+    """The checkpoints() recipe drawn on the device: (W_base bf16 [d_out, d_in],
+    W_ft fp32 [k, d_out, d_in])."""
+    import torch
+
+    w_base = device_normal((d_out, d_in), std, seed, tag(TAG_WBASE, index), device, torch.bfloat16)
+    s = torch.from_numpy(lowrank_spectrum(rank, rms, d_out, d_in)).to(device=device, dtype=torch.float32)
+    w_ft = torch.empty((k, d_out, d_in), dtype=torch.float32, device=device)
+    for i in range(k):
+        g = device_normal((d_out, rank), 1.0 / math.sqrt(d_out), seed, tag(TAG_FACTOR, index + (1 << 20) * (2 * i)),
+                          device)
+        h = device_normal((d_in, rank), 1.0 / math.sqrt(d_in), seed,
+                          tag(TAG_FACTOR, index + (1 << 20) * (2 * i + 1)), device)
+        delta = torch.mm(g * s, h.t().contiguous())
+        if noise > 0:
+            delta += device_normal((d_out, d_in), noise, seed, tag(TAG_NOISE, index + (1 << 20) * i), device)
+        w_ft[i] = w_base.float() + delta
+        del delta
     return w_base, w_ft
 
 

@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
-           "DeltaCache", "LOADER",
+           "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
            "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
            "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
@@ -28,6 +28,7 @@ BD_OK, BD_EINVAL, BD_ESHAPE, BD_EALIGN, BD_EWORKSPACE, BD_EDEVICE, BD_EBUSY = ra
 BD_CACHE_HIT, BD_CACHE_MISS, BD_CACHE_JOINED = 0, 1, 2
 BD_BF16, BD_F32 = 0, 1
 BD_ALPHA_ROW, BD_ALPHA_MATRIX = 0, 1
+MONOSOUP_SKETCH = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbitdelta.so")
@@ -52,6 +53,8 @@ EXPORTS = {
     "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
     "bitdelta_similarity_workspace": (_SZ, [_I32, _I64, _I64]),
     "bitdelta_similarity": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitdelta_monosoup_workspace": (_SZ, [_I64, _I64, _I32, _I32]),
+    "bitdelta_monosoup": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     # include/bitdelta_cache.h
     "bitdelta_cache_create": (_INT, [_I32, _I32, _I32, _I64, _P, _SZ, _P, _P, _P]),
     "bitdelta_cache_destroy": (None, [_P]),
@@ -246,6 +249,37 @@ def similarity(signs, alpha, per_matrix: bool | None = None):
     check(lib.bitdelta_similarity(_ptr(signs), _ptr(alpha), mode, V, d_out, d_in, _ptr(gram), _ptr(cos), _ptr(ws),
                                   nws, _stream(signs.device)))
     return gram, cos
+
+
+def monosoup(w_base, w_ft, omega, rank: int, power_iters: int = 1, out=None, sigma: bool = True):
+    """MonoSoup merge W_base + (1/k) sum_i tau_i of k checkpoints, tau_i the
+    rank-`rank` truncation of Delta_i = fl32(W_i - W_base) from a 64-column
+    randomized range finder.  w_base bf16 [R, C]; w_ft fp32 [k, R, C]; omega
+    fp32 [C, 64] (the caller's Gaussian test matrix).  Returns (merged fp32
+    [R, C], sigma fp64 [k, rank] or None)."""
+    torch = _torch()
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    _dev_tensor(w_ft, torch.float32, "w_ft")
+    if w_base.dim() != 2 or w_ft.dim() != 3 or tuple(w_ft.shape[1:]) != tuple(w_base.shape):
+        raise ValueError("w_base must be [R, C] and w_ft [k, R, C]")
+    k, R, C = w_ft.shape
+    if rank > 0:
+        _dev_tensor(omega, torch.float32, "omega")
+        if tuple(omega.shape) != (C, MONOSOUP_SKETCH):
+            raise ValueError(f"omega must be [{C}, {MONOSOUP_SKETCH}]")
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.float32, device=w_base.device)
+    else:
+        _dev_tensor(out, torch.float32, "out")
+        if tuple(out.shape) != (R, C):
+            raise ValueError("out must be [R, C]")
+    sig = torch.empty((k, rank), dtype=torch.float64, device=w_base.device) if sigma and rank > 0 else None
+    nws = lib.bitdelta_monosoup_workspace(R, C, k, rank)
+    ws = torch.empty((max(nws, 256),), dtype=torch.uint8, device=w_base.device)
+    check(lib.bitdelta_monosoup(_ptr(w_base), _ptr(w_ft), _ptr(omega) if rank > 0 else None, k, R, C, rank,
+                                power_iters, _ptr(out), _ptr(sig) if sig is not None else None, _ptr(ws), nws,
+                                _stream(w_base.device)))
+    return out, sig
 
 
 class DeltaCache:

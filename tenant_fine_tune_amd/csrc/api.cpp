@@ -310,4 +310,51 @@ bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alph
                   "bitdelta_similarity");
 }
 
+size_t bitdelta_monosoup_workspace(int64_t rows, int64_t cols, int32_t k, int32_t rank)
+{
+    const int64_t lim = (int64_t)1 << 21;
+    if (rows < 1 || cols < 4 || rows > lim || cols > lim || k < 1 || k > 64 || rank < 0 || rank > bd::kMsL)
+        return 0;
+    return bd::monosoup_workspace_bytes(rows, cols, k, rank);
+}
+
+bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, const float *omega, int32_t k, int64_t rows,
+                            int64_t cols, int32_t rank, int32_t power_iters, float *w_merged, double *sigma,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int64_t lim = (int64_t)1 << 21;
+    if (rows < 1 || cols < 4 || cols % 4 != 0 || rows > lim || cols > lim)
+        return fail(BD_ESHAPE, "monosoup needs rows in [1, 2^21] and cols a multiple of 4 in [4, 2^21] (got %lld, %lld)",
+                    (long long)rows, (long long)cols);
+    if (k < 1 || k > 64)
+        return fail(BD_EINVAL, "monosoup needs k in [1, 64] (got %d)", k);
+    const int64_t max_rank = rows < cols ? (rows < bd::kMsL ? rows : bd::kMsL) : (cols < bd::kMsL ? cols : bd::kMsL);
+    if (rank < 0 || rank > max_rank)
+        return fail(BD_EINVAL, "monosoup rank must be in [0, %lld] (got %d)", (long long)max_rank, rank);
+    if (power_iters < 0 || power_iters > 4)
+        return fail(BD_EINVAL, "monosoup power_iters must be in [0, 4] (got %d)", power_iters);
+    const size_t need = bitdelta_monosoup_workspace(rows, cols, k, rank);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "monosoup needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    BD_NONNULL(w_base);
+    BD_NONNULL(w_ft);
+    BD_NONNULL(w_merged);
+    BD_ALIGNED(w_base, 8);
+    BD_ALIGNED(w_ft, 16);
+    BD_ALIGNED(w_merged, 16);
+    if (rank > 0) {
+        BD_NONNULL(omega);
+        BD_ALIGNED(omega, 16);
+    }
+    if (sigma)
+        BD_ALIGNED(sigma, 8);
+    if (need) {
+        BD_NONNULL(workspace);
+        BD_ALIGNED(workspace, 256);
+    }
+    return device(bd::launch_monosoup(reinterpret_cast<const uint16_t *>(w_base), w_ft, omega, k, rows, cols, rank,
+                                      power_iters, w_merged, sigma, workspace, (hipStream_t)stream),
+                  "bitdelta_monosoup");
+}
+
 }  // extern "C"

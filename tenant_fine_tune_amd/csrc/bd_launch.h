@@ -61,4 +61,11 @@ hipError_t launch_similarity(const uint8_t *signs, const float *alpha, bool per_
                              int64_t d_out, int64_t d_in, double *gram, double *cosine, int32_t *counts,
                              hipStream_t s);
 
+// monosoup.hip: MonoSoup merge through a 64-column randomized range finder.
+constexpr int kMsL = 64;
+size_t monosoup_workspace_bytes(int64_t rows, int64_t cols, int32_t k, int32_t rank);
+hipError_t launch_monosoup(const uint16_t *w_base, const float *w_ft, const float *omega, int32_t k,
+                           int64_t rows, int64_t cols, int32_t rank, int32_t power_iters, float *out,
+                           double *sigma, void *workspace, hipStream_t s);
+
 }  // namespace bd

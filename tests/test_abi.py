@@ -166,6 +166,51 @@ def test_launch_without_device_reports_edevice(bd):
     assert "bitdelta_reconstruct" in err(bd)
 
 
+def test_monosoup_validation(bd):
+    """Host-side checks of bitdelta_monosoup (FAKE pointers never touched) and
+    the workspace formula: split partials, the two sketches, the whitened
+    copy, fp64 partial and summed Grams, the two 64 x 64 factors and the
+    merge factors."""
+    W = bd.lib.bitdelta_monosoup_workspace
+    f = bd.lib.bitdelta_monosoup
+    assert W(8192, 8192, 2, 0) == 0                      # rank 0: a copy of W_base, no scratch
+    assert W(0, 64, 1, 8) == 0 and W(64, 2, 1, 8) == 0 and W(64, 64, 0, 8) == 0 and W(64, 64, 1, 65) == 0
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    # 8192 x 8192, k = 2, r = 32: 256 blocks of 64 per pass -> 8 splits of 16 steps
+    R = C = 8192
+    expect = (a256(2 * 64 * 8 * R * 4) + a256(2 * R * 64 * 4) + a256(2 * C * 64 * 4) + a256(2 * R * 64 * 4)
+              + 2 * a256(2 * 64 * 64 * 64 * 8) + 4 * a256(2 * 64 * 64 * 8) + a256(R * 64 * 4) + a256(C * 64 * 4))
+    assert W(R, C, 2, 32) == expect
+    need = W(100, 96, 2, 8)
+    ok = (FAKE, FAKE, FAKE, 2, 100, 96, 8, 1, FAKE, FAKE, FAKE, need, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["wb", "wf", "om", "k", "R", "C", "r", "q", "out", "sig", "ws", "nws", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(C=98) == bd.BD_ESHAPE and call(C=0) == bd.BD_ESHAPE and call(R=0) == bd.BD_ESHAPE
+    assert call(R=(1 << 21) + 1) == bd.BD_ESHAPE
+    assert call(k=0) == bd.BD_EINVAL and call(k=65) == bd.BD_EINVAL
+    assert call(r=-1) == bd.BD_EINVAL and call(r=65) == bd.BD_EINVAL
+    assert call(R=20, r=21) == bd.BD_EINVAL                # rank above min(rows, cols)
+    assert call(q=-1) == bd.BD_EINVAL and call(q=5) == bd.BD_EINVAL
+    assert call(nws=need - 1) == bd.BD_EWORKSPACE
+    assert call(wb=None) == bd.BD_EINVAL and call(out=None) == bd.BD_EINVAL and call(om=None) == bd.BD_EINVAL
+    assert call(ws=None) == bd.BD_EINVAL
+    assert call(wf=ctypes.c_void_p(4104)) == bd.BD_EALIGN
+    assert call(om=ctypes.c_void_p(4104)) == bd.BD_EALIGN
+    assert call(wb=ctypes.c_void_p(4100)) == bd.BD_EALIGN
+    assert call(sig=ctypes.c_void_p(4100)) == bd.BD_EALIGN
+    assert call(out=ctypes.c_void_p(4100)) == bd.BD_EALIGN
+    assert call(ws=ctypes.c_void_p(4096 + 128)) == bd.BD_EALIGN
+
+
 def test_similarity_validation(bd):
     """Host-side checks of bitdelta_similarity: every failing call returns
     before a launch (FAKE pointers are never dereferenced)."""
