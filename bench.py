@@ -81,6 +81,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
     p.add_argument("--no-monosoup", action="store_true")
+    p.add_argument("--summarize-kernels", nargs=3, metavar=("TRACE_CSV", "PATTERN", "ANCHOR"),
+                   help="per-kernel totals of the kernels matching PATTERN, per dispatch of ANCHOR")
     p.add_argument("--no-context", action="store_true",
                    help="skip the vendor-library reference points (read stream, plain GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
@@ -869,6 +871,33 @@ def summarize_trace(trace_csv, gap=12):
               f"{statistics.median(v):9.2f} {min(v):9.2f}")
 
 
+def summarize_kernels(trace_csv, pattern, anchor):
+    """Per-kernel totals for the library kernels whose name contains
+    `pattern` (e.g. the MonoSoup kernels, "ms_"): dispatches, average /
+    median / min duration, and the time per call of the entry point, taking
+    the number of `anchor` dispatches as the number of calls."""
+    import csv
+    import re
+
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if "bd::" not in name or pattern not in name:
+            continue
+        m = re.search(r"(\w+(<[^>]*>)?)\(", name.replace("(anonymous namespace)::", ""))
+        key = m.group(1) if m else _short(name)
+        per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    calls = len(per.get(anchor, [])) or 1
+    print(f"{calls} calls (dispatches of {anchor})")
+    print(f"{'kernel':28s} {'n':>6s} {'avg us':>9s} {'median':>9s} {'min':>9s} {'us/call':>9s}")
+    total = 0.0
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        total += sum(v) / calls
+        print(f"{k[:28]:28s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} {min(v):9.2f} "
+              f"{sum(v) / calls:9.1f}")
+    print(f"{'total':28s} {'':6s} {'':9s} {'':9s} {'':9s} {total:9.1f}")
+
+
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
                  "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU",
                  "GRBM_GUI_ACTIVE")
@@ -928,6 +957,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "

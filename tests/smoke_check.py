@@ -1,7 +1,8 @@
 """One small pass of the hot path on cuda:0, checked against the oracle:
 compress -> reconstruct -> linear (decode and prefill) -> grouped ->
 similarity of the variants, on a 256 x 512 layer (the tiny single-layer
-workload) with 4 and 40 tokens."""
+workload) with 4 and 40 tokens; then a MonoSoup merge of two 130 x 68
+checkpoints."""
 import numpy as np
 import torch
 
@@ -42,7 +43,18 @@ def run() -> None:
     assert np.array_equal(host(g), g64), "similarity Gram matrix differs from the oracle"
     assert np.all(np.abs(host(c) - c64) <= np.spacing(np.abs(c64))), "similarity cosines differ from the oracle"
     torch.cuda.synchronize()
-    print("smoke: OK (compress, reconstruct, linear decode/prefill, grouped, similarity match the oracle)",
+    # MonoSoup merge of two checkpoints with rank-6 task vectors plus noise, one power iteration:
+    # the fp32 bar of the parity tests against the oracle's exact truncated SVD
+    mb, mf = synth.checkpoints(130, 68, 2, 6, 1e-5, seed=0)
+    om = synth.omega(68, seed=0)
+    ref, _ = oracle.monosoup(mb, mf, 6)
+    got, _ = bd.monosoup(bf16_dev(mb), f32_dev(mf), f32_dev(om), 6, power_iters=1)
+    base = synth.bf16_bits_to_f32(mb).astype(np.float64)
+    d_ref = ref - base
+    rel = np.linalg.norm(host(got).astype(np.float64) - ref) / np.linalg.norm(d_ref)
+    assert rel <= 2e-5, f"monosoup differs from the oracle's truncated SVD merge (rel {rel:.2e})"
+    print(f"smoke: monosoup relative error {rel:.2e}", flush=True)
+    print("smoke: OK (compress, reconstruct, linear decode/prefill, grouped, similarity, monosoup match the oracle)",
           flush=True)
 
 
