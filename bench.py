@@ -833,6 +833,23 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
         lines.append(f"grouped GEMM (14 variants, 4096 tokens): fetched {tf_:.0f} B, written {tw_:.0f} B per launch; "
                      f"W_base {w_bytes} B, all 14 sign sets {s_bytes} B, x {x_bytes} B; fetched / W_base = "
                      f"{tf_ / w_bytes:.3f} (a launch per variant would fetch W_base 14 times)")
+    # MonoSoup (k = 2 checkpoints of 8192 x 8192, rank 32), if in the runs: the Delta passes read
+    # 6 B per weight and checkpoint (fp32 W_i + bf16 W_base); the merge reads W_base and writes fp32
+    R_, C_ = MS_SHAPE
+    ms = {"ms_pass<false>": MS_K * R_ * C_ * 6, "ms_pass<true>": MS_K * R_ * C_ * 6, "ms_merge": R_ * C_ * 6}
+    for kern, algo_b in ms.items():
+        rx = re.compile(re.escape(kern))
+        fv = [v for nm, _, v in fetch if rx.search(nm)]
+        wv = [v for nm, _, v in write if rx.search(nm)]
+        if not fv or not wv:
+            continue
+        tf_, tw_ = statistics.median(fv) * f_fetch, statistics.median(wv) * f_write
+        out.setdefault("monosoup", {})[kern] = {"fetch_bytes": round(tf_), "write_bytes": round(tw_),
+                                                "algorithmic_bytes": algo_b,
+                                                "ratio": round((tf_ + tw_) / algo_b, 4)}
+        lines.append(f"monosoup {kern:16s} fetched {tf_:.0f} B, written {tw_:.0f} B per launch; algorithmic "
+                     f"{algo_b} B (6 B per weight{' and checkpoint' if 'pass' in kern else ''}); ratio "
+                     f"{(tf_ + tw_) / algo_b:.3f}")
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:

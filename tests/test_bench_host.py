@@ -53,6 +53,35 @@ def test_summarize_trace_splits_runs(tmp_path, capsys):
     assert got == [("bd::kern_a", 1024, 3, 5.0), ("bd::kern_b", 2048, 13, 7.0), ("bd::kern_a", 1024, 2, 9.0)]
 
 
+def test_summarize_kernels_totals_per_call(tmp_path, capsys):
+    """Per-kernel totals over the kernels matching a pattern, divided by the
+    number of anchor dispatches (one per entry-point call); template
+    arguments stay in the name, other kernels are ignored."""
+    rows, i = [], 0
+
+    def add(name, us, n):
+        nonlocal i
+        for _ in range(n):
+            i += 1
+            rows.append({"Dispatch_Id": i, "Kernel_Name": f"void bd::(anonymous namespace)::{name}(int, float*)",
+                         "Grid_Size_X": 256, "Grid_Size_Y": 1, "Workgroup_Size_X": 256,
+                         "Start_Timestamp": 1000 * i, "End_Timestamp": 1000 * i + int(us * 1000)})
+
+    for _ in range(2):
+        add("ms_pass<true>", 10.0, 2)
+        add("ms_solve", 30.0, 1)
+        add("gemv_stream<1>", 99.0, 1)
+    path = tmp_path / "trace.csv"
+    _write_csv(path, list(rows[0]), rows)
+    bench.summarize_kernels(str(path), "ms_", "ms_solve")
+    out = capsys.readouterr().out.splitlines()
+    assert out[0].startswith("2 calls")
+    body = {ln.split()[0]: ln.split() for ln in out[2:]}
+    assert set(body) == {"ms_solve", "ms_pass<true>", "total"}
+    assert int(body["ms_pass<true>"][1]) == 4 and float(body["ms_pass<true>"][5]) == 20.0
+    assert float(body["ms_solve"][5]) == 30.0 and float(body["total"][1]) == 50.0
+
+
 def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
     """A copy of 256 MiB that FETCH_SIZE reads as half its bytes gives the
     factor 2; each entry's bytes are the median of its dispatches on the
