@@ -925,14 +925,14 @@ def summarize_mfma(counter_csv, gap=12):
     MFMA_COUNTERS (its CSV carries each dispatch's start and end).  Per run of
     dispatches of one (kernel, grid): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
     over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs, the average graphics clock =
-    GRBM_GUI_ACTIVE / 8 over the dispatch's duration, and the MFMA rate these
-    two imply (1024 bf16 flop per SIMD per clock)."""
+    GRBM_GUI_ACTIVE / 8 over the dispatch's duration, and the MFMA rate
+    (SQ_INSTS_MFMA x flop per instruction over the duration)."""
     import csv
 
     disp = {}
     for r in csv.DictReader(open(counter_csv)):
         name = _short(r["Kernel_Name"])
-        if not ("gemm_tiles" in name or "splitk_reduce" in name):
+        if not ("gemm_tiles" in name or "splitk_reduce" in name or "ms_pass" in name or "ms_merge" in name):
             continue
         d = disp.setdefault(int(r["Dispatch_Id"]), {"name": name, "grid": int(r["Grid_Size"]),
                                                     "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
@@ -942,7 +942,8 @@ def summarize_mfma(counter_csv, gap=12):
     for i in sorted(disp):
         d = disp[i]
         k = (d["name"], d["grid"])
-        if k in open_run and i - open_run[k][0] <= gap:
+        # the MonoSoup kernels interleave with many small ones: one run per kernel
+        if k in open_run and (i - open_run[k][0] <= gap or "ms_" in d["name"]):
             j = open_run[k][1]
         else:
             runs.append([k, i, []])
@@ -957,8 +958,9 @@ def summarize_mfma(counter_csv, gap=12):
         xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8
         busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024) if xcd_cycles else 0.0
         clock = xcd_cycles / us / 1e3 if us else 0.0
-        tf = busy * 1024 * 1024 * clock / 1e3
         mf = c["SQ_INSTS_MFMA"]
+        # flop per MFMA instruction: v_mfma_f32_32x32x16_bf16 (prefill) or v_mfma_f32_32x32x2_f32 (MonoSoup)
+        tf = mf * (4096 if "ms_" in name else 32768) / us / 1e6 if us else 0.0
         per = (f"{c['SQ_INSTS_VALU'] / mf:9.2f} {c['SQ_INSTS_LDS'] / mf:8.2f}" if mf else f"{'-':>9s} {'-':>8s}")
         print(f"{name[:40]:40s} {threads:9d} {first:6d} {len(v):3d} {us:8.1f} {mf:10.0f} "
               f"{100 * busy:6.1f} {clock:9.2f} {tf:9.0f} {per} {c['SQ_LDS_BANK_CONFLICT']:7.0f}")

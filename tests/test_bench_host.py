@@ -129,11 +129,14 @@ def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
 
 def test_summarize_mfma_busy_and_clock(tmp_path, capsys):
     """busy = MFMA busy cycles over (GRBM_GUI_ACTIVE / 8) x 1024 SIMDs; clock =
-    (GRBM_GUI_ACTIVE / 8) over the dispatch's duration."""
+    (GRBM_GUI_ACTIVE / 8) over the dispatch's duration; rate = MFMA
+    instructions x 32768 flop (bf16 32x32x16) over the duration."""
     us, ghz, busy = 100.0, 1.8, 0.5
     xcd_cycles = ghz * 1e3 * us
+    n_mfma = 2880000
     vals = {"GRBM_GUI_ACTIVE": 8 * xcd_cycles, "SQ_VALU_MFMA_BUSY_CYCLES": busy * xcd_cycles * 1024,
-            "SQ_INSTS_MFMA": 1000, "SQ_INSTS_VALU": 4000, "SQ_INSTS_LDS": 1500, "SQ_LDS_BANK_CONFLICT": 0,
+            "SQ_INSTS_MFMA": n_mfma, "SQ_INSTS_VALU": 4 * n_mfma, "SQ_INSTS_LDS": 1.5 * n_mfma,
+            "SQ_LDS_BANK_CONFLICT": 0,
             "SQ_BUSY_CYCLES": 1, "SQ_WAVE_CYCLES": 1, "SQ_ACTIVE_INST_VALU": 1}
     assert set(vals) == set(bench.MFMA_COUNTERS)
     rows = []
@@ -149,7 +152,7 @@ def test_summarize_mfma_busy_and_clock(tmp_path, capsys):
     n, avg_us, mf, b, clk, tf, valu, lds, cf = line[-9:]
     assert int(n) == 2 and float(avg_us) == pytest.approx(us)
     assert float(b) == pytest.approx(100 * busy) and float(clk) == pytest.approx(ghz)
-    assert float(tf) == pytest.approx(busy * 1024 * 1024 * ghz / 1e3, abs=1)
+    assert float(mf) == n_mfma and float(tf) == pytest.approx(n_mfma * 32768 / us / 1e6, abs=1)
     assert float(valu) == pytest.approx(4.0) and float(lds) == pytest.approx(1.5)
 
 
