@@ -135,6 +135,23 @@ def test_monosoup_degenerate_cases(bd):
     assert rel <= TIGHT_REL and elem <= TIGHT_ELEM, (rel, elem)
 
 
+@pytest.mark.parametrize("R,C", [(1, 260), (300, 4), (5, 8)])
+def test_monosoup_full_rank_thin_shapes(bd, R, C):
+    """A single row, four columns, a 5 x 8 matrix: at rank min(R, C) every
+    task vector is kept whole, so the merge is the mean of the checkpoints
+    (the sketch is wider than the matrix's rank: the solver must drop the
+    empty directions)."""
+    r = min(R, C)
+    wb = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, 75, synth.tag(synth.TAG_WBASE, C)))
+    base = synth.bf16_bits_to_f32(wb)
+    wf = base[None] + synth.normal_f32((3, R, C), 1e-3, 75, synth.tag(synth.TAG_NOISE, C))
+    om = synth.omega(C, seed=75)
+    got, _ = _run(bd, wb, wf, om, r, 1)
+    ref = base.astype(np.float64) + (wf.astype(np.float64) - base[None]).mean(axis=0)
+    rel, elem = _errors(got, ref, base.astype(np.float64))
+    assert rel <= TIGHT_REL and elem <= TIGHT_ELEM, (rel, elem)
+
+
 def test_monosoup_identical_checkpoints_merge_as_one(bd):
     wb, wf, om, r, _, _ = _case("ragged_tall")
     one, _ = _run(bd, wb, wf[:1], om, r, 1)
