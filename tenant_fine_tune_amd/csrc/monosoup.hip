@@ -26,8 +26,9 @@
 //                   the contraction into partials; 64x64 output tile per
 //                   workgroup, four waves of v_mfma_f32_32x32x2_f32, the Delta
 //                   and right tiles staged through LDS, next tile's global
-//                   loads in flight during the MFMAs.  HBM-bound on the
-//                   checkpoint and base reads (6 bytes per weight).
+//                   loads in flight during the MFMAs.  6 bytes (fp32 W_i,
+//                   bf16 W_base) and 2 * 64 flop per weight: 21 flop/B, at
+//                   the fp32-MFMA ridge (157.3 TFLOP/s over 8 TB/s).
 //   ms_reduce       sums the partials in split order (deterministic).
 //   ms_gram         fp64 X^T X of a [n, 64] fp32 matrix, partial per 128 rows
 //                   (fp32 products are exact in fp64); ms_gram_reduce sums
