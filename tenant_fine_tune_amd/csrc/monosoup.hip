@@ -30,9 +30,9 @@
 //                   bf16 W_base) and 2 * 64 flop per weight: 21 flop/B, at
 //                   the fp32-MFMA ridge (157.3 TFLOP/s over 8 TB/s).
 //   ms_reduce       sums the partials in split order (deterministic).
-//   ms_gram         fp64 X^T X of a [n, 64] fp32 matrix, partial per 128 rows
-//                   (fp32 products are exact in fp64); ms_gram_reduce sums
-//                   the partials in chunk order.
+//   ms_gram         fp64 X^T X of a [n, 64] fp32 matrix, at most 256 partials
+//                   of consecutive rows (fp32 products are exact in fp64);
+//                   ms_gram_reduce sums the partials in a fixed order.
 //   ms_whiten       one workgroup of 1024: the pivoted-Cholesky whitening
 //                   factor T of a 64 x 64 Gram matrix (fp64).
 //   ms_solve        one workgroup of 1024: T of Y's Gram, then a cyclic Jacobi
@@ -54,7 +54,8 @@ namespace {
 
 constexpr int kL = kMsL;          // sketch width
 constexpr int kTile = 64;         // rows / columns of a Delta tile
-constexpr int kGramRows = 128;    // rows per partial Gram
+constexpr int kGramRows = 128;    // rows per LDS batch of the Gram kernel
+constexpr int kGramMaxChunks = 256;   // partial Grams per matrix at most
 constexpr int kPitch = 65;        // padded LDS row (floats or doubles)
 constexpr int kTargetGroups = 2048;
 constexpr int kMaxSplits = 32;
@@ -168,33 +169,39 @@ __global__ __launch_bounds__(256) void ms_reduce(const float *__restrict__ part,
     reinterpret_cast<f32x4 *>(out)[ck * n4 + e] = s;
 }
 
-// Partial Gram X^T X over rows [blockIdx.x * 128, +128) of checkpoint
-// blockIdx.y; gpart layout [ck][chunk][64][64] fp64.
-__global__ __launch_bounds__(256) void ms_gram(const float *__restrict__ X, int64_t n, double *__restrict__ gpart)
+// Partial Gram X^T X over rows [blockIdx.x * span, +span) of checkpoint
+// blockIdx.y (span a multiple of 128, rows in increasing order, 128 at a time
+// through LDS); gpart layout [ck][chunk][64][64] fp64.
+__global__ __launch_bounds__(256) void ms_gram(const float *__restrict__ X, int64_t n, int64_t span,
+                                               double *__restrict__ gpart)
 {
     __shared__ __attribute__((aligned(16))) float xs[kGramRows][kL];
     const int tid = threadIdx.x;
-    const int64_t ck = blockIdx.y, r0 = (int64_t)blockIdx.x * kGramRows;
+    const int64_t ck = blockIdx.y, c0 = (int64_t)blockIdx.x * span;
+    const int64_t c1 = c0 + span < n ? c0 + span : n;
     const float *x = X + ck * n * kL;
-#pragma unroll
-    for (int it = 0; it < kGramRows * kL / 4 / 256; ++it) {
-        const int idx = it * 256 + tid, row = idx >> 4, c4 = (idx & 15) * 4;
-        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (r0 + row < n)
-            v = *reinterpret_cast<const f32x4 *>(x + (r0 + row) * kL + c4);
-        *reinterpret_cast<f32x4 *>(&xs[row][c4]) = v;
-    }
-    __syncthreads();
     const int a0 = (tid >> 4) * 4, b0 = (tid & 15) * 4;
     double acc[4][4] = {};
-    for (int r = 0; r < kGramRows; ++r) {
-        const f32x4 xa = *reinterpret_cast<const f32x4 *>(&xs[r][a0]);
-        const f32x4 xb = *reinterpret_cast<const f32x4 *>(&xs[r][b0]);
+    for (int64_t r0 = c0; r0 < c1; r0 += kGramRows) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int it = 0; it < kGramRows * kL / 4 / 256; ++it) {
+            const int idx = it * 256 + tid, row = idx >> 4, c4 = (idx & 15) * 4;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (r0 + row < c1)
+                v = *reinterpret_cast<const f32x4 *>(x + (r0 + row) * kL + c4);
+            *reinterpret_cast<f32x4 *>(&xs[row][c4]) = v;
+        }
+        __syncthreads();
+        for (int r = 0; r < kGramRows; ++r) {
+            const f32x4 xa = *reinterpret_cast<const f32x4 *>(&xs[r][a0]);
+            const f32x4 xb = *reinterpret_cast<const f32x4 *>(&xs[r][b0]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] += (double)xa[i] * (double)xb[j];
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] += (double)xa[i] * (double)xb[j];
+        }
+        __syncthreads();
     }
     double *g = gpart + ((ck * gridDim.x + blockIdx.x) * kL) * kL;
 #pragma unroll
@@ -640,6 +647,10 @@ PassPlan pass_plan(int64_t n_out, int64_t n_k, int32_t k)
     return PassPlan{sps, (int)cdiv(steps, sps)};
 }
 
+// Rows per partial Gram: a multiple of 128, so that at most 256 partials cover n rows.
+int64_t gram_span(int64_t n) { return kGramRows * cdiv(cdiv(n, kGramRows), kGramMaxChunks); }
+int gram_chunks(int64_t n) { return (int)cdiv(n, gram_span(n)); }
+
 struct MsLayout {
     size_t part, y, z, x2, gy, gz, g2y, g2z, t, p, u, w, total;
     int nch_y, nch_z, rp, K;
@@ -652,8 +663,8 @@ MsLayout ms_layout(int64_t R, int64_t C, int32_t k, int32_t rank)
     MsLayout L{};
     const PassPlan pn = pass_plan(R, C, k), pt = pass_plan(C, R, k);
     const int64_t part_f = (int64_t)k * kL * (pn.S * R > pt.S * C ? pn.S * R : pt.S * C);
-    L.nch_y = (int)cdiv(R, kGramRows);
-    L.nch_z = (int)cdiv(C, kGramRows);
+    L.nch_y = gram_chunks(R);
+    L.nch_z = gram_chunks(C);
     L.rp = (int)cdiv(rank, 16) * 16;
     L.K = k * L.rp;
     size_t off = 0;
@@ -729,8 +740,8 @@ hipError_t launch_monosoup(const uint16_t *w_base, const float *w_ft, const floa
     };
     // G2 <- X^T X (fp64, per checkpoint)
     auto gram = [&](const float *X, int64_t n, double *g, double *G2) {
-        const int nch = (int)cdiv(n, kGramRows);
-        hipLaunchKernelGGL(ms_gram, dim3((unsigned)nch, (unsigned)k), dim3(256), 0, s, X, n, g);
+        const int nch = gram_chunks(n);
+        hipLaunchKernelGGL(ms_gram, dim3((unsigned)nch, (unsigned)k), dim3(256), 0, s, X, n, gram_span(n), g);
         hipLaunchKernelGGL(ms_gram_reduce, dim3(kL * kL / 64, (unsigned)k), dim3(256), 0, s, (const double *)g, nch,
                            G2);
     };

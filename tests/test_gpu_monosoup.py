@@ -152,6 +152,21 @@ def test_monosoup_full_rank_thin_shapes(bd, R, C):
     assert rel <= TIGHT_REL and elem <= TIGHT_ELEM, (rel, elem)
 
 
+def test_monosoup_maximum_rows_and_power_iterations(bd):
+    """The largest row count the entry point takes (2^21) on four columns,
+    rank 4 (the whole task vector), with the largest power_iters (4): the
+    merge is the mean of the checkpoints."""
+    R, C, r = 1 << 21, 4, 4
+    wb = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, 76, synth.tag(synth.TAG_WBASE, 1)))
+    base = synth.bf16_bits_to_f32(wb)
+    wf = base[None] + synth.normal_f32((2, R, C), 1e-3, 76, synth.tag(synth.TAG_NOISE, 1))
+    om = synth.omega(C, seed=76)
+    got, _ = _run(bd, wb, wf, om, r, 4)
+    ref = base.astype(np.float64) + (wf.astype(np.float64) - base[None]).mean(axis=0)
+    rel, elem = _errors(got, ref, base.astype(np.float64))
+    assert rel <= TIGHT_REL and elem <= TIGHT_ELEM, (rel, elem)
+
+
 def test_monosoup_identical_checkpoints_merge_as_one(bd):
     wb, wf, om, r, _, _ = _case("ragged_tall")
     one, _ = _run(bd, wb, wf[:1], om, r, 1)
