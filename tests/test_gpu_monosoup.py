@@ -64,6 +64,7 @@ _CASES = {
     "ragged_small": (130, 68, 2, 6, 6, 1e-5),
     "wide": (70, 260, 1, 10, 10, 1e-5),
     "rank_40_of_64": (300, 256, 2, 64, 40, 0.0),
+    "many_checkpoints": (96, 72, 64, 8, 8, 1e-5),   # the largest k the entry point takes
 }
 _ORACLE = {}
 
