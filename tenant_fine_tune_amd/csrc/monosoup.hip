@@ -551,20 +551,32 @@ __global__ __launch_bounds__(256) void ms_apply(const float *__restrict__ X, int
         Xs[row][a] = r0 + row < n ? x[(r0 + row) * kL + a] : 0.0f;
     }
     __syncthreads();
-    const int row = tid >> 2, c0 = (tid & 3) * 16;
-    double acc[16] = {};
+    // thread (rg, cg): rows 4 rg .. 4 rg + 3, columns 4 cg .. 4 cg + 3 (4 x 4 register block)
+    const int rg = tid >> 4, cg = tid & 15;
+    double acc[4][4] = {};
     for (int a = 0; a < kL; ++a) {
-        const double xv = Xs[row][a];
+        double xv[4], fv[4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            acc[c] += xv * Fs[a][c0 + c];
+        for (int i = 0; i < 4; ++i) {
+            xv[i] = Xs[4 * rg + i][a];
+            fv[i] = Fs[a][4 * cg + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] += xv[i] * fv[j];
     }
-    if (r0 + row < n) {
-        float *d = dst + ck * dst_ck + (r0 + row) * dst_row;
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            if (c0 + c < ncols)
-                d[c0 + c] = (float)(acc[c] * scale);
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = r0 + 4 * rg + i;
+        if (row < n) {
+            float *d = dst + ck * dst_ck + row * dst_row;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * cg + j < ncols)
+                    d[4 * cg + j] = (float)(acc[i][j] * scale);
+        }
     }
 }
 
