@@ -595,6 +595,15 @@ __global__ __launch_bounds__(256) void ms_merge(const uint16_t *__restrict__ wb,
     const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
     const int rr0 = tid >> 4, kq = (tid & 15) * 4;
 
+    // the W_base groups of the epilogue, loaded before the MFMAs so they arrive meanwhile
+    const int64_t row = r0 + 32 * wj + li;
+    uint2 bb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t c = c0 + 32 * wi + 8 * g + 4 * lk;
+        bb[g] = (row < R && c < C) ? *reinterpret_cast<const uint2 *>(wb + row * C + c) : make_uint2(0u, 0u);
+    }
+
     f32x16_t acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v)
@@ -624,13 +633,12 @@ __global__ __launch_bounds__(256) void ms_merge(const uint16_t *__restrict__ wb,
         __syncthreads();
     }
     // acc[v]: column c0 + 32 wi + 8 (v / 4) + 4 lk + v % 4, row r0 + 32 wj + li
-    const int64_t row = r0 + 32 * wj + li;
     if (row < R) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int64_t c = c0 + 32 * wi + 8 * g + 4 * lk;
             if (c < C) {   // C % 4 == 0: the group of four is whole
-                const uint2 b = *reinterpret_cast<const uint2 *>(wb + row * C + c);
+                const uint2 b = bb[g];
                 f32x4 o;
                 o[0] = lo_f32(b.x) + acc[4 * g + 0];
                 o[1] = hi_f32(b.x) + acc[4 * g + 1];
