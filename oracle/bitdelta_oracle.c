@@ -65,8 +65,10 @@
  *
  * Parity pins for every function here live in the CPU test tier: hand-built
  * bytes and ties, closed-form means, an exact rational (math.fsum) mean,
- * Laplace statistics, least-squares optimality of alpha, and brute-force
- * exact-rational matrix products on tiny inputs.
+ * Laplace statistics, least-squares optimality of alpha, brute-force
+ * exact-rational matrix products on tiny inputs, exact rational Gram
+ * matrices, and for the MonoSoup merge task vectors with a known SVD,
+ * LAPACK's SVD and the Eckart-Young residual.
  */
 #include <math.h>
 #include <stdint.h>
