@@ -88,6 +88,40 @@ __device__ __forceinline__ uint4 weff8(const float *sgn, uint32_t b, uint4 w, fl
     return e;
 }
 
+// fp16 form of the sign table, in the same 256 bytes: entry e sits at byte
+// 16e and holds (bit b of e) ? +1 : -1 as fp16 for b = 0..3 in its first 8
+// bytes (the other 8 are unused).  A lookup is then an 8-byte LDS read
+// instead of 16, at the same address as in the fp32 table.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void fill_sign_table_h(float *sgn)
+{
+    if (threadIdx.x < 64) {
+        const int e = threadIdx.x >> 2, b = threadIdx.x & 3;
+        if (b < 2) {
+            // two fp16 entries per thread-pair's dword: bits 2b, 2b+1 of e
+            const uint32_t lo = ((e >> (2 * b)) & 1) ? 0x3C00u : 0xBC00u;
+            const uint32_t hi = ((e >> (2 * b + 1)) & 1) ? 0x3C00u : 0xBC00u;
+            reinterpret_cast<uint32_t *>(sgn)[4 * e + b] = lo | (hi << 16);
+        }
+    }
+}
+
+// weff8 with the fp16 table: the fp16 +-1 feeds the fma directly (one
+// v_fma_mix_f32 per weight, the conversion of +-1 exact), so the result is the
+// same single rounding of f32(W) + s alpha.
+__device__ __forceinline__ uint4 weff8h(const float *sgn, uint32_t b, uint4 w, float a)
+{
+    const uint8_t *t = reinterpret_cast<const uint8_t *>(sgn);
+    const f16x4 lo = *reinterpret_cast<const f16x4 *>(t + (b & 15u) * 16);
+    const f16x4 hi = *reinterpret_cast<const f16x4 *>(t + (b & 0xF0u));
+    uint4 e;
+    e.x = pack_bf16x2(fmaf((float)lo[0], a, lo_f32(w.x)), fmaf((float)lo[1], a, hi_f32(w.x)));
+    e.y = pack_bf16x2(fmaf((float)lo[2], a, lo_f32(w.y)), fmaf((float)lo[3], a, hi_f32(w.y)));
+    e.z = pack_bf16x2(fmaf((float)hi[0], a, lo_f32(w.z)), fmaf((float)hi[1], a, hi_f32(w.z)));
+    e.w = pack_bf16x2(fmaf((float)hi[2], a, lo_f32(w.w)), fmaf((float)hi[3], a, hi_f32(w.w)));
+    return e;
+}
+
 // Streaming (nontemporal) 16-byte global load / store and byte load: data
 // touched once, kept out of the way of the caches.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

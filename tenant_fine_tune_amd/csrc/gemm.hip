@@ -331,7 +331,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     __shared__ int32_t rows_s[GATHER ? BM : 1];
     uint8_t *const XSb[2] = {XS0, XS1};
     uint8_t *const WEb[2] = {WE0, WE1};
-    fill_sign_table(sgn);
+    fill_sign_table_h(sgn);
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
@@ -445,7 +445,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     auto build_store = [&](const WRaw8 &r, int i, int buf) {
         const int nl = wave * 32 + i * 8 + (lane >> 3);
         const int sw = ((i & 1) * 4 + (lane >> 4)) & 7;  // (nl >> 1) & 7
-        const uint4 e = weff8(sgn, r.s[i], r.w[i], a[i]);
+        const uint4 e = weff8h(sgn, r.s[i], r.w[i], a[i]);
         *reinterpret_cast<uint4 *>(WEb[buf] + nl * 128 + ((p ^ sw) * 16)) = e;
     };
 
