@@ -85,8 +85,12 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[N])
 
 // ------------------------------------------------------------------ m <= 4
 // EVEN: d_in / 8 is a multiple of 64 (no ragged last step).  S = the number of
-// 512-column steps is a multiple of D (the host picks D).
-template <int MT, int RW, int D, bool PER_MATRIX, bool EVEN>
+// 512-column steps is a multiple of D (the host picks D).  XL (EVEN only): x
+// is copied once into the workgroup's LDS (dynamic, m * d_in * 2 bytes) by
+// direct-to-LDS loads issued ahead of the first weight stages, and every wave
+// reads its token columns from there instead of from L2 (at m = 4 the L2 reads
+// of x are otherwise twice those of W_base).
+template <int MT, int RW, int D, bool PER_MATRIX, bool EVEN, bool XL>
 __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ x, int m,
                                                    const uint16_t *__restrict__ w_base,
                                                    const uint8_t *__restrict__ signs,
@@ -94,7 +98,9 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
                                                    uint16_t *__restrict__ y, int64_t ldy)
 {
     constexpr int kWaves = 8;
+    static_assert(!XL || EVEN, "x in LDS needs whole 512-column steps");
     __shared__ __attribute__((aligned(16))) float sgn[64];
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // XL: x [m, K] bf16
     fill_sign_table(sgn);
     __syncthreads();
     const int lane = threadIdx.x & 63;
@@ -105,6 +111,17 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);
+    if constexpr (XL) {
+        // 1 KB chunk c of x (flat [m, K], a whole number of chunks since K is
+        // a multiple of 512) -> LDS bytes [1024 c, +1024): wave w copies
+        // chunks w, w + 8, ...  The host bounds m * K * 2 by 56 KB, so a
+        // wave has at most 7 of these in flight.
+        const int chunks = (int)(((int64_t)m * K * 2) >> 10);
+        for (int c = wave; c < chunks; c += kWaves)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xs + c * 1024), 16, (uint32_t)(16 * lane),
+                                                     (uint32_t)(c * 1024), 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // the copies stay ahead of the weight loads
+    }
     // Rows past R use an out-of-range offset (zeros, never stored).  In a
     // ragged last step the lanes past the row read the next row's W_base and
     // sign byte (finite) and x = 0, so they add nothing.
@@ -134,16 +151,25 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wrow[r], (uint32_t)s * 1024u, kStream));
             sq[d][r] = __builtin_amdgcn_raw_buffer_load_b8(rs, srow[r], (uint32_t)s * 64u, kStream);
         }
+        if constexpr (!XL) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-            xq[d][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rx, live ? xrow[t] : kInvalidOffset, (uint32_t)s * 1024u, 0));
+            for (int t = 0; t < MT; ++t)
+                xq[d][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rx, live ? xrow[t] : kInvalidOffset, (uint32_t)s * 1024u, 0));
+        }
     };
     float acc[RW * MT];
 #pragma unroll
     for (int i = 0; i < RW * MT; ++i)
         acc[i] = 0.0f;
-    auto compute = [&](int d) {
+    auto compute = [&](int d, int s) {
+        if constexpr (XL) {
+            // tokens past m read LDS rows that hold nothing useful; their sums
+            // are never stored
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                xq[d][t] = *reinterpret_cast<const uint4 *>(xs + ((int64_t)(t < m ? t : 0) * K * 2 + s * 1024 + 16 * lane));
+        }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
             const uint4 e = weff8(sgn, sq[d][r], wq[d][r], a[r]);
@@ -163,10 +189,18 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
         load(d, d);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (XL) {
+        // the x copies were issued before the 2 * RW * D loads of the first
+        // stages: once at most that many are outstanding, this wave's copies
+        // have landed; the barrier makes every wave's visible
+        wait_vmcnt<2 * RW * D>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s0 = 0; s0 < S - D; s0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            compute(d);
+            compute(d, s0 + d);
             __builtin_amdgcn_sched_barrier(0);
             load(d, s0 + d + D);
             __builtin_amdgcn_sched_barrier(0);
@@ -174,7 +208,7 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-        compute(d);
+        compute(d, S - D + d);
 
     constexpr int N = RW * MT;
     constexpr int kbits = log2i<N>();
@@ -329,20 +363,33 @@ struct Args {
     hipStream_t s;
 };
 
+// x goes through LDS for MT >= kXLdsMinM tokens and at most kXLdsMax bytes.
+constexpr int kXLdsMinM = 2;
+// Largest x (m * d_in bf16) the m <= 4 kernels keep in LDS.
+constexpr int64_t kXLdsMax = 56 * 1024;
+
 template <int MT, int RW, int D>
 hipError_t launch_stream(const Args &g)
 {
     const bool even = (g.d_in >> 3) % 64 == 0;
+    const int64_t xbytes = (int64_t)g.m * g.d_in * 2;
     const dim3 grid((unsigned)((g.rows + 8 * RW - 1) / (8 * RW))), block(512);
-#define BD_STREAM(PM, EV)                                                                                   \
-    hipLaunchKernelGGL((gemv_stream<MT, RW, D, PM, EV>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, \
-                       g.d_in, g.y, g.ldy)
+#define BD_STREAM(PM, EV, XL, LDS)                                                                          \
+    hipLaunchKernelGGL((gemv_stream<MT, RW, D, PM, EV, XL>), grid, block, LDS, g.s, g.x, g.m, g.w, g.sg, g.a, \
+                       g.rows, g.d_in, g.y, g.ldy)
+    if constexpr (MT >= kXLdsMinM) {
+        if (even && xbytes <= kXLdsMax) {
+            if (g.pm) BD_STREAM(true, true, true, (unsigned)xbytes);
+            else BD_STREAM(false, true, true, (unsigned)xbytes);
+            return hipGetLastError();
+        }
+    }
     if (g.pm) {
-        if (even) BD_STREAM(true, true);
-        else BD_STREAM(true, false);
+        if (even) BD_STREAM(true, true, false, 0);
+        else BD_STREAM(true, false, false, 0);
     } else {
-        if (even) BD_STREAM(false, true);
-        else BD_STREAM(false, false);
+        if (even) BD_STREAM(false, true, false, 0);
+        else BD_STREAM(false, false, false, 0);
     }
 #undef BD_STREAM
     return hipGetLastError();

@@ -159,10 +159,13 @@ def test_linear_3d_input_and_determinism(bd):
     check_linear(host_bits(y1.view(300, R)), y64, sc, "3d input")
 
 
-@pytest.mark.parametrize("M", [1, 16], ids=["m1", "m16"])
-def test_identity_decode(bd, M):
+# (m, d_in): d_in = 1032 takes the ragged-step kernels; the others, whole
+# 512-column steps with x small enough to sit in LDS (m = 2..4)
+@pytest.mark.parametrize("M,C", [(1, 1032), (16, 1032), (4, 4096), (2, 512), (3, 8704)],
+                         ids=lambda v: str(v))
+def test_identity_decode(bd, M, C):
     """One-hot x: y[t, r] must equal W_eff[r, j_t] bit for bit."""
-    R, C = 1000, 1032
+    R = 1000
     w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=6)
     weff = oracle.reconstruct(w_base, so, ao)
     cols = np.linspace(0, C - 1, M).astype(int)
@@ -183,10 +186,11 @@ def test_identity_prefill(bd, shape):
     assert same_bits_pm0(y, weff.T)
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 40, 300], ids=lambda m: f"m{m}")
-def test_dyadic_exact(bd, M):
+@pytest.mark.parametrize("M,C", [(1, 256), (5, 256), (16, 256), (40, 256), (300, 256), (4, 2048), (2, 512),
+                                 (3, 4096)], ids=lambda v: str(v))
+def test_dyadic_exact(bd, M, C):
     """Exact-arithmetic inputs: every sign bit and alpha shows in y, bit for bit."""
-    R, C = 200, 256
+    R = 200
     x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=40 + M)
     y = host_bits(bd.linear(bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])))
     y64, _ = oracle.linear(x, w_base, sb[0], alpha[0])
