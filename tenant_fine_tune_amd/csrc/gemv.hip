@@ -27,7 +27,7 @@
 //    per-lane sums are reduced across the wave by a reduce-scatter.
 //
 //  gemv_mfma (m in 5..16, matrix cores): one workgroup of 8 waves per block of
-//    16 rows; the columns are cut into super-blocks of 256 and wave w takes
+//    16 rows; the columns are cut into super-blocks of 128 and wave w takes
 //    super-blocks w, w + 8, ...  Lane l (j = l % 16, q = l / 16) loads, for
 //    MFMA jj, the 16 bytes of chunk 4jj + q of row n0 + j (so the 4 lanes of a
 //    row read 64 contiguous bytes per instruction) and the same columns of
@@ -223,11 +223,13 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
 
 // ------------------------------------------------------------- m in 5..16
 constexpr int kMfmaWaves = 8;
-constexpr int kSuperK = 256;  // columns per super-block (32 chunks of 8)
 
-// EVEN: d_in is a multiple of 256 (whole super-blocks; sign rows 16-byte
-// aligned, so each lane fetches its super-block's 32 sign bytes in two
-// 16-byte loads).  Otherwise the lane loads its 8 sign bytes one by one and
+
+constexpr int kSuperK = 128;  // columns per super-block (4 MFMA chunks of 32)
+
+// EVEN: d_in is a multiple of 128 (whole super-blocks; sign rows 16-byte
+// aligned, so each lane fetches its super-block's 16 sign bytes in one
+// 16-byte load).  Otherwise the lane loads its 4 sign bytes one by one and
 // x is zero past the row.
 template <bool PER_MATRIX, bool EVEN>
 __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__restrict__ x, int m,
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
                                                              int64_t K, uint16_t *__restrict__ y, int64_t ldy)
 {
     constexpr int KW = kMfmaWaves;
+    constexpr int JJ = kSuperK / 32;  // MFMAs per super-block
     __shared__ __attribute__((aligned(16))) float sgn[64];
     __shared__ f32x4 red[KW][64];
     fill_sign_table(sgn);
@@ -258,8 +261,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
     const uint32_t xrow = j < m ? (uint32_t)(j * K * 2 + 16 * q) : kInvalidOffset;
 
     struct Stage {
-        uint4 w[8], x[8];
-        uint32_t s[8];  // EVEN: the 32 sign bytes (dword jj holds chunk 4jj + q in byte q); else byte jj
+        uint4 w[JJ], x[JJ];
+        uint32_t s[JJ];  // EVEN: the 16 sign bytes (dword jj holds chunk 4jj + q in byte q); else byte jj
     };
     Stage st[2];
     // Stages past the wave's last super-block are issued with out-of-range
@@ -271,25 +274,22 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
         const uint32_t wv = live ? wrow : kInvalidOffset;
         const uint32_t sv = live ? srow : kInvalidOffset;
         if constexpr (EVEN) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint4 v = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, sv + 16 * i, (uint32_t)sb * 32u, 0));
-                st[b].s[4 * i] = v.x;
-                st[b].s[4 * i + 1] = v.y;
-                st[b].s[4 * i + 2] = v.z;
-                st[b].s[4 * i + 3] = v.w;
-            }
+            const uint4 v = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, sv, (uint32_t)sb * (kSuperK / 8), 0));
+            st[b].s[0] = v.x;
+            st[b].s[1] = v.y;
+            st[b].s[2] = v.z;
+            st[b].s[3] = v.w;
         } else {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                st[b].s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, sv + 4 * jj + q, (uint32_t)sb * 32u, 0);
+            for (int jj = 0; jj < JJ; ++jj)
+                st[b].s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, sv + 4 * jj + q, (uint32_t)sb * (kSuperK / 8), 0);
         }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             bool ok = live;
             if constexpr (!EVEN)
-                ok = ok && (int64_t)sb * 32 + 4 * jj + q < G;
+                ok = ok && (int64_t)sb * (kSuperK / 8) + 4 * jj + q < G;
             st[b].w[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv + 64 * jj, so, 0));
             st[b].x[jj] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xrow + 64 * jj : kInvalidOffset, so, 0));
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     auto compute = [&](int b) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             const uint32_t byte = EVEN ? (st[b].s[jj] >> (8 * q)) & 0xFFu : st[b].s[jj];
             const uint4 e = weff8(sgn, byte, st[b].w[jj], a);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st[b].x[jj]),
@@ -420,8 +420,8 @@ hipError_t launch_mfma(const Args &g)
     const bool even = g.d_in % kSuperK == 0;
     const dim3 grid((unsigned)((g.rows + 15) / 16)), block(64 * kMfmaWaves);
 #define BD_MFMA(PM, EV)                                                                                     \
-    hipLaunchKernelGGL((gemv_mfma<PM, EV>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, g.d_in, g.y, \
-                       g.ldy)
+    hipLaunchKernelGGL((gemv_mfma<PM, EV>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, \
+                       g.d_in, g.y, g.ldy)
     if (g.pm) {
         if (even) BD_MFMA(true, true);
         else BD_MFMA(true, false);
