@@ -63,10 +63,10 @@ STEP_KERNELS = {
     "compress_row": ("compress.hip", [r"compress_rows<true, false>"]),
     "compress_matrix": ("compress.hip", [r"compress_rows<true, true>", r"alpha_matrix_finish"]),
     "reconstruct": ("reconstruct.hip", [r"reconstruct_rows<false>"]),
-    "linear_m1_row": ("gemv.hip", [r"gemv_stream<1, 1, \d+, false, true>"]),
-    "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true>"]),
-    "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 2, \d+, false, true>"]),
-    "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 2, \d+, true, true>"]),
+    "linear_m1_row": ("gemv.hip", [r"gemv_stream<1, 1, \d+, false, true, false>"]),
+    "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true, false>"]),
+    "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 2, \d+, false, true, true>"]),
+    "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 2, \d+, true, true, true>"]),
     "linear_m16_row": ("gemv.hip", [r"gemv_mfma<false, true>"]),
     "linear_m16_matrix": ("gemv.hip", [r"gemv_mfma<true, true>"]),
 }
