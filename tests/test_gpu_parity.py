@@ -40,7 +40,10 @@ def _bits32(a):
 
 # ------------------------------------------------------------------ compress
 
-COMPRESS_SHAPES = [(256, 512), (5, 24), (1, 8), (3, 2056), (64, 28672), (300, 4096), (4096, 4096)]
+# includes rows of 2048..8192 columns (1..4 whole groups per thread) and row counts that are
+# not a multiple of 4
+COMPRESS_SHAPES = [(256, 512), (5, 24), (1, 8), (3, 2056), (64, 28672), (300, 4096), (4096, 4096),
+                   (7, 2048), (13, 6144), (10, 8192), (301, 4096)]
 
 
 @pytest.mark.parametrize("ft_bf16", [False, True], ids=["ft_f32", "ft_bf16"])
