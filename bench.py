@@ -65,8 +65,8 @@ STEP_KERNELS = {
     "reconstruct": ("reconstruct.hip", [r"reconstruct_rows<false>"]),
     "linear_m1_row": ("gemv.hip", [r"gemv_stream<1, 1, \d+, false, true, false>"]),
     "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true, false>"]),
-    "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 2, \d+, false, true, true>"]),
-    "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 2, \d+, true, true, true>"]),
+    "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 1, \d+, false, true, true>"]),
+    "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 1, \d+, true, true, true>"]),
     "linear_m16_row": ("gemv.hip", [r"gemv_mfma<false, true>"]),
     "linear_m16_matrix": ("gemv.hip", [r"gemv_mfma<true, true>"]),
 }

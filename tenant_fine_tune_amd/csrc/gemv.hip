@@ -461,7 +461,7 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
         else if (m <= 2)
             e = dispatch_stream<2, 2>(g, 4);
         else if (m <= 4)
-            e = dispatch_stream<4, 2>(g, 4);
+            e = dispatch_stream<4, 1>(g, 4);
         else
             e = launch_mfma(g);
         if (e != hipSuccess)
