@@ -61,17 +61,35 @@ enum { BD_CACHE_HIT = 0, BD_CACHE_MISS = 1, BD_CACHE_JOINED = 2 };
 /* Make variant `variant` resident and hold it: *slot_ptr = its device slot,
  * *outcome = BD_CACHE_HIT, BD_CACHE_MISS (this call loaded it) or
  * BD_CACHE_JOINED (it waited for another caller's load).  Blocks during a
- * load.  Every successful acquire must be matched by one release.  Errors:
- * BD_EINVAL (bad variant or NULL output), BD_EBUSY (no slot can be freed),
- * BD_EDEVICE (the loader failed). */
+ * load.  A caller that waited for a load that succeeded but found the
+ * variant evicted again when it woke starts over (it may then load the
+ * variant itself: BD_CACHE_MISS).  Before a load writes into a slot it waits
+ * on the host for the events that bitdelta_cache_release_on_stream recorded
+ * for that slot.  Every successful acquire must be matched by one release.
+ * Errors: BD_EINVAL (bad variant or NULL output), BD_EBUSY (no slot can be
+ * freed), BD_EDEVICE (the loader this call ran or waited for failed, or a
+ * wait on a release event failed). */
 BD_API bd_status bitdelta_cache_acquire(bd_delta_cache *cache, int32_t variant, void **slot_ptr, int *outcome);
-/* BD_EINVAL when the variant is not held. */
+/* Give up one hold of a variant.  Once no hold is left its slot may be
+ * evicted and overwritten by the next miss at any time, so every GPU read of
+ * the slot must be complete (the streams that used it synchronised) before
+ * this call; with reads still queued, use bitdelta_cache_release_on_stream.
+ * BD_EINVAL when the variant is not held. */
 BD_API bd_status bitdelta_cache_release(bd_delta_cache *cache, int32_t variant);
+/* Give up one hold once the work queued so far on `stream` (a hipStream_t,
+ * NULL = the null stream) is done: an event is recorded on `stream` now, and
+ * the next load into this variant's slot waits for it first.  Release with
+ * this call after enqueueing the kernels that read the slot, on the stream
+ * they run on (one call per stream if several read it).  BD_EINVAL when the
+ * variant is not held; BD_EDEVICE when the event cannot be created or
+ * recorded (the hold is then kept). */
+BD_API bd_status bitdelta_cache_release_on_stream(bd_delta_cache *cache, int32_t variant, void *stream);
 
 /* Slot index of a resident variant, -1 otherwise (also for a bad variant). */
 BD_API int32_t bitdelta_cache_slot_of(const bd_delta_cache *cache, int32_t variant);
-/* Counters since creation: hits, misses (loads started), joins, evictions,
- * refused (BD_EBUSY) requests.  Any pointer may be NULL. */
+/* Counters since creation: hits, misses (loads started), joins (requests
+ * that waited for another caller's load at least once), evictions, refused
+ * (BD_EBUSY) requests.  Any pointer may be NULL. */
 BD_API void bitdelta_cache_counters(const bd_delta_cache *cache, int64_t *hits, int64_t *misses, int64_t *joins,
                              int64_t *evictions, int64_t *busy);
 

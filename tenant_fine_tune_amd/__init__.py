@@ -60,6 +60,7 @@ EXPORTS = {
     "bitdelta_cache_destroy": (None, [_P]),
     "bitdelta_cache_acquire": (_INT, [_P, _I32, _P, _P]),
     "bitdelta_cache_release": (_INT, [_P, _I32]),
+    "bitdelta_cache_release_on_stream": (_INT, [_P, _I32, _P]),
     "bitdelta_cache_slot_of": (_I32, [_P, _I32]),
     "bitdelta_cache_counters": (None, [_P, _P, _P, _P, _P, _P]),
     "bitdelta_cache_host_loader": (_INT, [_P, _I32, _P, _SZ]),
@@ -328,7 +329,15 @@ class DeltaCache:
         return p.value, o.value
 
     def release(self, variant):
+        """Give up a hold; every GPU read of the slot must be complete."""
         check(lib.bitdelta_cache_release(self._h, variant))
+
+    def release_on_stream(self, variant, stream=None):
+        """Give up a hold once the work queued so far on `stream` (torch's
+        current stream by default) is done."""
+        torch = _torch()
+        st = (stream or torch.cuda.current_stream(self._slots.device)).cuda_stream
+        check(lib.bitdelta_cache_release_on_stream(self._h, variant, ctypes.c_void_p(st)))
 
     def slot_of(self, variant):
         return lib.bitdelta_cache_slot_of(self._h, variant)

@@ -198,9 +198,14 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, co
     }
     const bool per_matrix = alpha_mode == BD_ALPHA_MATRIX;
     hipStream_t s = (hipStream_t)stream;
-    if (m <= bd::kGemvMaxM)
+    if (m <= bd::kGemvMaxM) {
+        // The decode kernels address x and each launched chunk of W_base (at
+        // least 16 rows) through 32-bit buffer offsets.
+        if ((int64_t)bd::kGemvMaxM * d_in * 2 >= ((int64_t)1 << 31))
+            return fail(BD_ESHAPE, "decode linear needs 16 rows of W_base below 2 GiB (d_in=%lld)", (long long)d_in);
         return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
                       "bitdelta_linear (decode)");
+    }
     const int64_t tiles = ((m + bd::kGemmBM - 1) / bd::kGemmBM) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
     if (!operands_fit(m, d_out, d_in))
         return fail(BD_ESHAPE, "prefill operands must each be below 2 GiB (m=%lld, d_out=%lld, d_in=%lld)",

@@ -138,10 +138,16 @@ __device__ __forceinline__ void st_stream16(void *p, uint4 v)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Buffer offset of a row that does not exist: beyond every tensor (all
+// Lane (VGPR) offset of a row that does not exist: beyond every tensor (all
 // tensors a kernel addresses through a buffer resource are below 2 GiB,
-// checked on the host) without wrapping when a column offset is added, so
-// loads return zero and stores are dropped.
+// checked on the host), so loads return zero and stores are dropped.
+//
+// The hardware range check of a raw buffer access covers the lane offset
+// (plus the instruction's immediate offset) only; the scalar (SGPR) offset
+// is added to the address after the check.  Every kernel here therefore puts
+// in the scalar offset only a displacement that stays inside memory the lane
+// offset has already validated (a column position inside a valid row), and
+// gives each row, chunk or token that may not exist its own lane offset.
 constexpr uint32_t kInvalidOffset = 0x80000000u;
 
 // Cache policy of a buffer load that streams data read once (nt).

@@ -33,6 +33,13 @@ struct bd_delta_cache {
     std::vector<State> state;
     std::vector<int32_t> slot_of, in_slot, refs, volume;
     std::vector<int64_t> last_use;
+    // load_seq[v]: loads of v started so far; failed_seq[v]: the number of
+    // the last load of v that failed (-1: none), so a caller that waited for
+    // load n can tell its failure from a later eviction
+    std::vector<int64_t> load_seq, failed_seq;
+    // per slot: events recorded by bitdelta_cache_release_on_stream that
+    // a later load into the slot must wait for
+    std::vector<std::vector<hipEvent_t>> slot_events;
     std::deque<int32_t> history;
     int64_t t = 0;
     int64_t hits = 0, misses = 0, joins = 0, evictions = 0, busy = 0;
@@ -113,12 +120,23 @@ bd_status bitdelta_cache_create(int32_t n_variants, int32_t n_slots, int32_t n_p
     c->refs.assign(n_variants, 0);
     c->volume.assign(n_variants, 0);
     c->last_use.assign(n_variants, -1);
+    c->load_seq.assign(n_variants, 0);
+    c->failed_seq.assign(n_variants, -1);
     c->in_slot.assign(n_slots, -1);
+    c->slot_events.resize(n_slots);
     *out = c;
     return BD_OK;
 }
 
-void bitdelta_cache_destroy(bd_delta_cache *cache) { delete cache; }
+void bitdelta_cache_destroy(bd_delta_cache *cache)
+{
+    if (!cache)
+        return;
+    for (auto &evs : cache->slot_events)
+        for (hipEvent_t e : evs)
+            (void)hipEventDestroy(e);
+    delete cache;
+}
 
 bd_status bitdelta_cache_acquire(bd_delta_cache *c, int32_t v, void **slot_ptr, int *outcome)
 {
@@ -126,22 +144,30 @@ bd_status bitdelta_cache_acquire(bd_delta_cache *c, int32_t v, void **slot_ptr, 
         return BD_EINVAL;
     std::unique_lock<std::mutex> lk(c->mu);
     c->note_request(v);
-    if (c->state[v] == bd_delta_cache::kLoading) {
-        ++c->joins;
-        c->cv.wait(lk, [&] { return c->state[v] != bd_delta_cache::kLoading; });
-        if (c->state[v] != bd_delta_cache::kResident)
-            return BD_EDEVICE;  // the load this call waited for failed
-        ++c->refs[v];
-        *slot_ptr = c->slots + (size_t)c->slot_of[v] * c->slot_bytes;
-        *outcome = BD_CACHE_JOINED;
-        return BD_OK;
-    }
-    if (c->state[v] == bd_delta_cache::kResident) {
-        ++c->hits;
-        ++c->refs[v];
-        *slot_ptr = c->slots + (size_t)c->slot_of[v] * c->slot_bytes;
-        *outcome = BD_CACHE_HIT;
-        return BD_OK;
+    bool joined = false;
+    for (;;) {
+        if (c->state[v] == bd_delta_cache::kLoading) {
+            if (!joined) {
+                ++c->joins;
+                joined = true;
+            }
+            const int64_t seq = c->load_seq[v];
+            c->cv.wait(lk, [&] { return c->state[v] != bd_delta_cache::kLoading || c->load_seq[v] != seq; });
+            if (c->failed_seq[v] == seq)
+                return BD_EDEVICE;  // the load this call waited for failed
+            // loaded: resident now, or evicted (or loading again) before this
+            // call woke; look again
+            continue;
+        }
+        if (c->state[v] == bd_delta_cache::kResident) {
+            if (!joined)
+                ++c->hits;
+            ++c->refs[v];
+            *slot_ptr = c->slots + (size_t)c->slot_of[v] * c->slot_bytes;
+            *outcome = joined ? BD_CACHE_JOINED : BD_CACHE_HIT;
+            return BD_OK;
+        }
+        break;
     }
     const int32_t s = c->take_slot();
     if (s < 0) {
@@ -149,14 +175,28 @@ bd_status bitdelta_cache_acquire(bd_delta_cache *c, int32_t v, void **slot_ptr, 
         return BD_EBUSY;
     }
     ++c->misses;
+    const int64_t seq = ++c->load_seq[v];
     c->state[v] = bd_delta_cache::kLoading;
     c->slot_of[v] = s;
     c->in_slot[s] = v;
     uint8_t *dst = c->slots + (size_t)s * c->slot_bytes;
+    std::vector<hipEvent_t> pending;
+    pending.swap(c->slot_events[s]);
     lk.unlock();
-    const int rc = c->loader(c->user, v, dst, c->slot_bytes);
+    // GPU work that read the slot's previous contents and was released with
+    // bitdelta_cache_release_on_stream must finish before the loader writes
+    int rc = 0;
+    for (hipEvent_t e : pending) {
+        const hipError_t he = hipEventSynchronize(e);
+        if (he != hipSuccess && rc == 0)
+            rc = (int)he;
+        (void)hipEventDestroy(e);
+    }
+    if (rc == 0)
+        rc = c->loader(c->user, v, dst, c->slot_bytes);
     lk.lock();
     if (rc != 0) {
+        c->failed_seq[v] = seq;
         c->state[v] = bd_delta_cache::kAbsent;
         c->slot_of[v] = -1;
         c->in_slot[s] = -1;
@@ -178,6 +218,35 @@ bd_status bitdelta_cache_release(bd_delta_cache *c, int32_t v)
     std::lock_guard<std::mutex> lk(c->mu);
     if (c->refs[v] <= 0)
         return BD_EINVAL;
+    --c->refs[v];
+    return BD_OK;
+}
+
+bd_status bitdelta_cache_release_on_stream(bd_delta_cache *c, int32_t v, void *stream)
+{
+    if (!c || v < 0 || v >= c->n_variants)
+        return BD_EINVAL;
+    std::lock_guard<std::mutex> lk(c->mu);
+    if (c->refs[v] <= 0)
+        return BD_EINVAL;
+    std::vector<hipEvent_t> &evs = c->slot_events[c->slot_of[v]];
+    // drop the events whose work has finished, so the list stays short
+    size_t keep = 0;
+    for (hipEvent_t e : evs) {
+        if (hipEventQuery(e) == hipSuccess)
+            (void)hipEventDestroy(e);
+        else
+            evs[keep++] = e;
+    }
+    evs.resize(keep);
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        return BD_EDEVICE;
+    if (hipEventRecord(e, static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipEventDestroy(e);
+        return BD_EDEVICE;
+    }
+    evs.push_back(e);
     --c->refs[v];
     return BD_OK;
 }

@@ -384,11 +384,14 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 
     // x copies: instruction j (0..3) of wave w covers tile rows 32w + 8j ..
     // +7; lane l writes LDS position l & 7 of row 8j + l / 8, which holds
-    // logical chunk (l & 7) ^ ((row >> 1) & 7).
+    // logical chunk (l & 7) ^ ((row >> 1) & 7).  Every row has its own lane
+    // offset (out of range past M); the scalar offset carries only the K
+    // position, which the hardware range check does not cover and which
+    // stays inside the row.
     const int p = lane & 7;
-    uint32_t xoff[GATHER ? 4 : 2];
+    uint32_t xoff[4];
 #pragma unroll
-    for (int j = 0; j < (GATHER ? 4 : 2); ++j) {
+    for (int j = 0; j < 4; ++j) {
         const int row = wave * 32 + j * 8 + (lane >> 3);
         const int c = p ^ (((j & 1) * 4 + (lane >> 4)) & 7);
         int64_t tok;
@@ -398,28 +401,22 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
             tok = m0 + row;
         xoff[j] = (tok < 0 || tok >= M) ? kInvalidOffset : (uint32_t)((tok * K + c * 8) * 2);
     }
-    const uint32_t xstride16 = (uint32_t)(16 * K * 2);  // 16 rows further (dense)
     auto dma_x = [&](int t, int buf) {
         const uint32_t kb = kx0 + (uint32_t)(t * BK * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t vo, so;
-            if constexpr (GATHER) {
-                vo = xoff[j];
-                so = kb;
-            } else {
-                vo = xoff[j & 1];
-                so = (uint32_t)(j >> 1) * xstride16 + kb;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 4 + j) * 1024), 16, vo, so, 0,
-                                                     0);
-        }
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(XSb[buf] + (wave * 4 + j) * 1024), 16, xoff[j],
+                                                     kb, 0, 0);
     };
 
     // W_base rows of this wave: load i (0..3) covers feature rows
     // 32*wave + 8i .. +7, lane l -> row 8i + l / 8, chunk l & 7 (8 columns).
-    // One lane offset for i = 0; the 8i rows go in the scalar offset (a row
-    // at or past N lands past the end of W_base / signs: zeros).
+    // One lane offset for i = 0; the 8i rows go in the scalar offset, which
+    // the hardware range check does not cover.  That is safe because the
+    // host runs this kernel only with N a multiple of 32: the wave's 32 rows
+    // n0 + 32 wave .. +31 are then all below N or all at or past it, so a
+    // valid row nw implies valid rows nw + 8i, and an invalid one has the
+    // out-of-range lane offset (zeros).
     const int64_t nw = n0 + wave * 32 + (lane >> 3);
     const uint32_t woff = nw < N ? (uint32_t)((nw * K + p * 8) * 2) : kInvalidOffset;
     const uint32_t soff = nw < N ? (uint32_t)(nw * G + p) : kInvalidOffset;
@@ -697,7 +694,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_tokens(const int32_t *_
     }
 }
 
-// The general kernel over all m_tiles x n_tiles tiles (d_in not a multiple of 64).
+// The general kernel over all m_tiles x n_tiles tiles (d_in not a multiple of
+// 64, or d_out not a multiple of 32).
 template <bool GATHER>
 hipError_t launch_general(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                          const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
@@ -762,10 +760,15 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
 //    it fills the chip and ends sooner, when every range keeps at least 2048
 //    columns (the fixed cost of summing the partials is then repaid);
 //  - otherwise one unsplit launch.
+// Shapes the eight-wave kernel takes (whole 64-column steps; whole 32-row
+// blocks of W_base, see the kernel's W_base loads); the rest run on the
+// general kernel.
+static bool w8_shape(int64_t d_out, int64_t d_in) { return d_in % 64 == 0 && d_out % 32 == 0; }
+
 GemmPlan gemm_plan(int64_t m, int64_t d_out, int64_t d_in)
 {
     GemmPlan p{1, 0, 1};
-    if (d_in % 64 != 0)
+    if (!w8_shape(d_out, d_in))
         return p;
     const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
     if (tiles < 192) {
@@ -811,7 +814,7 @@ hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, con
                        uint16_t *y, void *workspace, hipStream_t s)
 {
     const int64_t m_tiles = (m + BM - 1) / BM;
-    if (d_in % 64 != 0)
+    if (!w8_shape(d_out, d_in))
         return launch_general<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr,
                                            0, s);
     const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
@@ -848,7 +851,7 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (d_in % 64 != 0)
+    if (!w8_shape(d_out, d_in))
         return launch_general<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace,
                                           n_variants, s);
     return launch_w8<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, 0,

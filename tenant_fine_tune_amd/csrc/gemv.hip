@@ -130,9 +130,11 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
                                                      (uint32_t)(c * 1024), 0, 0);
         __builtin_amdgcn_sched_barrier(0);  // the copies stay ahead of the weight loads
     }
-    // Rows past R use an out-of-range offset (zeros, never stored).  In a
-    // ragged last step the lanes past the row read the next row's W_base and
-    // sign byte (finite) and x = 0, so they add nothing.
+    // Rows past R use an out-of-range lane offset (zeros, never stored).
+    // The scalar offset of a load (the step's column offset) is outside the
+    // hardware range check, so it only ever moves within a row whose lane
+    // offset is valid: in a ragged last step the lanes past the row use the
+    // out-of-range offset for W_base, the sign byte and x alike (zeros).
     uint32_t wrow[RW], srow[RW];
     float a[RW];
 #pragma unroll
@@ -155,9 +157,10 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
             live = (int64_t)s * 64 + lane < G;
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            wq[d][r] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wrow[r], (uint32_t)s * 1024u, kStream));
-            sq[d][r] = __builtin_amdgcn_raw_buffer_load_b8(rs, srow[r], (uint32_t)s * 64u, kStream);
+            wq[d][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rw, live ? wrow[r] : kInvalidOffset, (uint32_t)s * 1024u, kStream));
+            sq[d][r] = __builtin_amdgcn_raw_buffer_load_b8(rs, live ? srow[r] : kInvalidOffset, (uint32_t)s * 64u,
+                                                           kStream);
         }
         if constexpr (!XL) {
 #pragma unroll
@@ -274,7 +277,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
     };
     Stage st[2];
     // Stages past the wave's last super-block are issued with out-of-range
-    // offsets: no traffic, and zeros (x = 0 adds nothing when consumed).
+    // offsets: no traffic, and zeros (x = 0 adds nothing when consumed).  The
+    // scalar offset (the super-block's column offset) is outside the hardware
+    // range check, so a chunk past the row (ragged d_in) gets the out-of-range
+    // lane offset for W_base, its sign byte and x alike.
     auto issue = [&](int b, int t) {
         const bool live = t < nt;
         const int sb = wave + t * KW;
@@ -288,17 +294,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
             st[b].s[1] = v.y;
             st[b].s[2] = v.z;
             st[b].s[3] = v.w;
-        } else {
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj)
-                st[b].s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, sv + 4 * jj + q, (uint32_t)sb * (kSuperK / 8), 0);
         }
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
             bool ok = live;
-            if constexpr (!EVEN)
+            if constexpr (!EVEN) {
                 ok = ok && (int64_t)sb * (kSuperK / 8) + 4 * jj + q < G;
-            st[b].w[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wv + 64 * jj, so, 0));
+                st[b].s[jj] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? sv + 4 * jj + q : kInvalidOffset,
+                                                                  (uint32_t)sb * (kSuperK / 8), 0);
+            }
+            st[b].w[jj] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wv + 64 * jj : kInvalidOffset, so, 0));
             st[b].x[jj] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xrow + 64 * jj : kInvalidOffset, so, 0));
         }

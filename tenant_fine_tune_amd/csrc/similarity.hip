@@ -48,7 +48,7 @@ constexpr int kTreeThreads = 256;
 __host__ __device__ constexpr int pair_index(int a, int b, int V) { return a * V - a * (a + 1) / 2 + (b - a - 1); }
 
 // EVEN: d_in / 8 is a multiple of 64 (whole 64-byte chunks); otherwise the
-// bytes past the row in the last chunk are masked off in every variant, so
+// bytes past the row in the last chunk read as zero in every variant, so
 // they add no disagreement.
 template <int V, bool EVEN>
 __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_t *__restrict__ signs, int64_t R,
@@ -72,36 +72,39 @@ __global__ __launch_bounds__(64 * kSimWaves) void similarity_counts(const uint8_
 #pragma unroll
     for (int p = 0; p < P; ++p)
         d[p] = 0;
-    // chunk k of this lane's row for every variant; chunks past the row
-    // (k >= nk) use an out-of-range offset and read zeros (no disagreement)
+    // Chunk k of this lane's row for every variant.  The scalar offset (the
+    // chunk's position and the variant's block) is outside the hardware range
+    // check, so it only moves inside valid rows: with whole chunks (EVEN) a
+    // chunk k < nk lies inside the row, and chunks past it (k >= nk) use the
+    // out-of-range lane offset (zeros: no disagreement).  With a ragged last
+    // chunk each dword gets its own lane offset (d_in % 32 == 0 makes the row
+    // a whole number of dwords), out of range past the row: zeros in every
+    // variant, so they add no disagreement either.
     auto load = [&](uint4 (&s)[V], int k) {
-        const uint32_t b = k < nk ? base : kInvalidOffset;
-        const uint32_t off = (uint32_t)k * 64u;
+        if constexpr (EVEN) {
+            const uint32_t b = k < nk ? base : kInvalidOffset;
+            const uint32_t off = (uint32_t)k * 64u;
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-            s[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, b, off + (uint32_t)v * vstride, kStream));
-    };
-    auto count = [&](uint4 (&s)[V], int k) {
-        if constexpr (!EVEN) {
-            // valid bytes of this lane's 16-byte piece (0..16); the rest is
-            // masked to zero in every variant
-            const int64_t left = G - ((int64_t)k * 64 + 16 * q);
-            const int nb = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-            uint32_t m[4];
+            for (int v = 0; v < V; ++v)
+                s[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs, b, off + (uint32_t)v * vstride, kStream));
+        } else {
+            const int64_t start = (int64_t)k * 64 + 16 * q;
+            uint32_t vo[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int b = nb - 4 * i;
-                m[i] = b >= 4 ? 0xFFFFFFFFu : (b <= 0 ? 0u : (1u << (8 * b)) - 1u);
-            }
+            for (int i = 0; i < 4; ++i)
+                vo[i] = (row_ok && start + 4 * i < G) ? base + (uint32_t)(k * 64 + 4 * i) : kInvalidOffset;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                s[v].x &= m[0];
-                s[v].y &= m[1];
-                s[v].z &= m[2];
-                s[v].w &= m[3];
+                s[v].x = __builtin_amdgcn_raw_buffer_load_b32(rs, vo[0], (uint32_t)v * vstride, kStream);
+                s[v].y = __builtin_amdgcn_raw_buffer_load_b32(rs, vo[1], (uint32_t)v * vstride, kStream);
+                s[v].z = __builtin_amdgcn_raw_buffer_load_b32(rs, vo[2], (uint32_t)v * vstride, kStream);
+                s[v].w = __builtin_amdgcn_raw_buffer_load_b32(rs, vo[3], (uint32_t)v * vstride, kStream);
             }
         }
+    };
+    auto count = [&](uint4 (&s)[V], int k) {
+        (void)k;
 #pragma unroll
         for (int a = 0; a < V; ++a)
 #pragma unroll

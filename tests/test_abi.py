@@ -101,6 +101,21 @@ def test_linear_validation(bd):
     assert bd.lib.bitdelta_linear_workspace(4096, 4096, 4096) == 0
 
 
+def test_decode_rejects_rows_past_32bit_offsets(bd):
+    """The decode kernels address W_base in chunks of at least 16 rows (and x)
+    through 32-bit buffer offsets: a d_in whose 16 rows reach 2 GiB is a shape
+    error, not a silent wrap.  The boundary itself still validates further."""
+    f = bd.lib.bitdelta_linear
+    lim = (1 << 31) // (16 * 2)            # 16 rows of bf16 reach 2 GiB at d_in = 2^26
+    for m in (1, 4, 16):
+        assert f(FAKE, m, FAKE, FAKE, FAKE, 0, 1, lim, FAKE, None, 0, None) == bd.BD_ESHAPE, m
+        assert "2 GiB" in err(bd)
+        assert f(FAKE, m, FAKE, FAKE, FAKE, 0, 1, 1 << 27, FAKE, None, 0, None) == bd.BD_ESHAPE
+    # one step below the limit passes the shape check and fails only on the
+    # (deliberately misaligned) output pointer, so nothing is launched
+    assert f(FAKE, 16, FAKE, FAKE, FAKE, 0, 1, lim - 8, FAKE_ODD, None, 0, None) == bd.BD_EALIGN
+
+
 def test_linear_split_k_workspace(bd):
     """Prefill with few 256 x 256 output tiles splits K, and so does a last
     partial wave of at most 128 tiles; the workspace holds one fp32 256 x 256
@@ -111,7 +126,7 @@ def test_linear_split_k_workspace(bd):
     assert W(2048, 8192, 8192) == 0                # 256 tiles fill the chip
     assert W(2048, 8192, 28672) == 0
     assert W(2048, 28672, 8192) == 2 * 128 * tile  # 896 tiles: last 128 in 2 K ranges
-    assert W(4000, 4100, 4096) == 2 * 16 * tile    # 272 tiles: K/2 = 2048 is the floor
+    assert W(4000, 4128, 4096) == 2 * 16 * tile    # 272 tiles: K/2 = 2048 is the floor
     assert W(256, 256 * 264, 16384) == 8 * 8 * tile
     assert W(4096, 6400, 8192) == 0                # last wave of 144 tiles: over half the CUs
     assert W(4096, 4352, 2048) == 0                # K/2 = 1024: too short to repay the sum
@@ -121,6 +136,7 @@ def test_linear_split_k_workspace(bd):
     assert W(40, 1024, 8192) == 16 * 4 * tile      # capped at 16 splits
     assert W(512, 8192, 28672) == 4 * 64 * tile
     assert W(600, 64, 1032) == 0                   # d_in not a multiple of 64: general kernel
+    assert W(600, 80, 4096) == 0                   # d_out not a multiple of 32: general kernel
     assert W(600, 64, 960) == 0                    # K too short to split
     f = bd.lib.bitdelta_linear
     need = W(600, 64, 4096)

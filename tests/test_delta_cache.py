@@ -183,3 +183,62 @@ def test_create_validation(bd):
     assert bd.lib.bitdelta_cache_slot_of(h, 99) == -1
     bd.lib.bitdelta_cache_destroy(h)
     bd.lib.bitdelta_cache_destroy(None)
+
+
+def test_joined_waiters_never_report_a_successful_load_as_failed(bd):
+    """A caller that joins a load that succeeds must not get BD_EDEVICE, even
+    when the variant was evicted again before the caller woke: it retries.
+    Eight threads over three variants and one slot (a loader that never
+    fails) make that interleaving common; only BD_OK and BD_EBUSY are
+    acceptable outcomes."""
+    import time
+
+    fake = Fake(bd)
+    for v in range(3):
+        fake.hooks[v] = lambda: time.sleep(0.0005)
+    h = _create(bd, fake, 3, 1, 0, 4)
+    bad, ok = [], [0]
+    lock = threading.Lock()
+
+    def worker(seed):
+        rng = np.random.default_rng(seed)
+        for _ in range(150):
+            v = int(rng.integers(0, 3))
+            st, p, o = _acquire(bd, h, v)
+            if st == bd.BD_OK:
+                time.sleep(0.0002)
+                assert bd.lib.bitdelta_cache_release(h, v) == bd.BD_OK
+                with lock:
+                    ok[0] += 1
+            elif st != bd.BD_EBUSY:
+                with lock:
+                    bad.append((v, st))
+
+    ts = [threading.Thread(target=worker, args=(s,)) for s in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(60)
+    bd.lib.bitdelta_cache_destroy(h)
+    assert not bad, f"{len(bad)} acquires failed after a successful load: {bad[:5]}"
+    assert ok[0] > 0
+
+
+def test_release_on_stream_checks_holds(bd):
+    """bitdelta_cache_release_on_stream: BD_EINVAL for a variant that is not
+    held; without a device the event cannot be made (BD_EDEVICE) and the hold
+    is kept, so a plain release still succeeds once."""
+    import torch
+
+    fake = Fake(bd)
+    h = _create(bd, fake, 3, 2, 0, 8)
+    assert bd.lib.bitdelta_cache_release_on_stream(h, 1, None) == bd.BD_EINVAL
+    assert bd.lib.bitdelta_cache_release_on_stream(None, 1, None) == bd.BD_EINVAL
+    assert _acquire(bd, h, 1)[0] == bd.BD_OK
+    if torch.cuda.device_count() == 0:
+        assert bd.lib.bitdelta_cache_release_on_stream(h, 1, None) == bd.BD_EDEVICE
+        assert bd.lib.bitdelta_cache_release(h, 1) == bd.BD_OK
+    else:
+        assert bd.lib.bitdelta_cache_release_on_stream(h, 1, None) == bd.BD_OK
+    assert bd.lib.bitdelta_cache_release(h, 1) == bd.BD_EINVAL
+    bd.lib.bitdelta_cache_destroy(h)

@@ -45,3 +45,31 @@ def test_host_loader_round_trip(bd):
     cache.release(0)
     cache.release(0)
     cache.close()
+
+
+def test_release_on_stream_orders_the_next_load(bd):
+    """A kernel still queued on another stream reads a slot when its hold is
+    released with release_on_stream; the miss that evicts the variant and
+    reloads the slot must wait for it.  The read runs after a bounded spin of
+    some tens of milliseconds on a side stream, so without the wait the
+    loader (on the null stream) would overwrite the slot first."""
+    V, S, NB = 2, 1, 1 << 22
+    host = [torch.from_numpy(synth.u64(NB, 12, 7600 + v).astype(np.uint8)).pin_memory() for v in range(V)]
+    slots = torch.empty(S * NB, dtype=torch.uint8, device="cuda")
+    cache = bd.DeltaCache(V, S, 0, 8, slots, NB, host=host)
+    ptr, outcome = cache.acquire(0)
+    assert outcome == bd.BD_CACHE_MISS and ptr == slots.data_ptr()
+    seen = torch.empty(NB, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50_000_000)
+        seen.copy_(slots[:NB])
+    cache.release_on_stream(0, side)
+    ptr1, outcome1 = cache.acquire(1)   # evicts variant 0 and loads variant 1 into the same slot
+    assert outcome1 == bd.BD_CACHE_MISS and ptr1 == ptr
+    torch.cuda.synchronize()
+    assert torch.equal(seen.cpu(), host[0])
+    assert torch.equal(slots[:NB].cpu(), host[1])
+    cache.release(1)
+    cache.close()
