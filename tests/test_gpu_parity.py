@@ -135,7 +135,9 @@ def test_linear_decode(bd, case, per_matrix):
 PREFILL_CASES = [((256, 512), 17), ((256, 512), 64), ((256, 512), 256), ((256, 512), 300),
                  ((300, 200), 257), ((1000, 1032), 513), ((520, 64), 40), ((64, 4096), 600),
                  # split-K: few output tiles, K cut into 2..16 ranges
-                 ((200, 4096), 64), ((520, 1024), 300), ((1024, 8192), 40), ((300, 2112), 17 + 256)]
+                 ((200, 4096), 64), ((520, 1024), 300), ((1024, 8192), 40), ((300, 2112), 17 + 256),
+                 # eight-wave kernel (d_out a multiple of 32) with ragged tiles and token counts
+                 ((224, 4096), 64), ((544, 1024), 300), ((288, 2112), 17 + 256), ((96, 640), 33)]
 
 
 @pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
@@ -200,7 +202,7 @@ def test_dyadic_exact(bd, M, C):
     assert np.array_equal(synth.bf16_bits_to_f32(y).astype(np.float64), y64)
 
 
-@pytest.mark.parametrize("case", [((200, 4096), 64), ((1024, 8192), 40), ((256, 2048), 300)],
+@pytest.mark.parametrize("case", [((224, 4096), 64), ((1024, 8192), 40), ((256, 2048), 300)],
                          ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
 def test_split_k_dyadic_exact(bd, case):
     """Split-K shapes on exact-arithmetic inputs: y bit for bit, and the
@@ -216,7 +218,7 @@ def test_split_k_dyadic_exact(bd, case):
     assert torch.equal(bd.linear(x2, wd, sd, ad), bd.linear(x2, wd, sd, ad))
 
 
-@pytest.mark.parametrize("shape", [(256, 2048), (520, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", [(256, 2048), (544, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_identity_prefill_split_k(bd, shape):
     """x = I on split-K shapes: each y element comes from one split, the
     others add zeros, so y = W_eff^T bit for bit."""
@@ -229,7 +231,7 @@ def test_identity_prefill_split_k(bd, shape):
     assert same_bits_pm0(y, weff.T)
 
 
-@pytest.mark.parametrize("case", [((4100, 4096), 4000), ((4352, 8192), 4096)],
+@pytest.mark.parametrize("case", [((4128, 4096), 4000), ((4352, 8192), 4096)],
                          ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
 def test_last_wave_split_dyadic_exact(bd, case):
     """More tiles than CUs with a last partial wave (16 or 17 tiles of 272):
@@ -251,9 +253,9 @@ def test_last_wave_split_dyadic_exact(bd, case):
 
 
 def test_identity_last_wave_split(bd):
-    """x = I on 4100 x 4096 (272 tiles, the last 16 split in K): each y element
+    """x = I on 4128 x 4096 (272 tiles, the last 16 split in K): each y element
     comes from one K range, the other adds zeros, so y = W_eff^T bit for bit."""
-    R, C = 4100, 4096
+    R, C = 4128, 4096
     assert bd.lib.bitdelta_linear_workspace(C, R, C) > 0
     w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=13)
     weff = oracle.reconstruct(w_base, so, ao)
