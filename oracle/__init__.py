@@ -40,6 +40,8 @@ def _bind(lib):
     lib.oracle_linear_grouped_rows.restype = I
     lib.oracle_similarity.argtypes = [P, P, I, ctypes.c_int32, I64, I64, P, P]
     lib.oracle_similarity.restype = I
+    lib.oracle_similarity_delta.argtypes = [P, P, I, ctypes.c_int32, I64, I64, P, P]
+    lib.oracle_similarity_delta.restype = I
     lib.oracle_monosoup.argtypes = [P, P, ctypes.c_int32, I64, I64, ctypes.c_int32, P, P]
     lib.oracle_monosoup.restype = I
     lib.oracle_num_threads.restype = I
@@ -190,6 +192,32 @@ class Oracle:
         return gram, cos
 
 
+    def similarity_delta(self, w_base, w_ft):
+        """Gram matrix and cosines of the variants' full task vectors (R9):
+        Delta_v = fl32(W_ft_v - W_base), summed in the fixed fp64 order.
+
+        w_base: uint16 [R, C]; w_ft: float32 or uint16 (bf16 bits) [V, R, C].
+        Returns (gram [V, V], cos [V, V]) as float64.
+        """
+        lib = self.lib
+        w_base = _c(w_base, np.uint16)
+        w_ft = np.ascontiguousarray(w_ft)
+        if w_ft.dtype == np.float32:
+            is_f32 = 1
+        elif w_ft.dtype == np.uint16:
+            is_f32 = 0
+        else:
+            raise TypeError("w_ft must be float32 or uint16 (bf16 bits)")
+        V, R, C = w_ft.shape
+        if w_base.shape != (R, C):
+            raise ValueError("w_base shape mismatch")
+        gram = np.zeros((V, V), dtype=np.float64)
+        cos = np.zeros((V, V), dtype=np.float64)
+        rc = lib.oracle_similarity_delta(_ptr(w_base), _ptr(w_ft), is_f32, V, R, C, _ptr(gram), _ptr(cos))
+        if rc != 0:
+            raise ValueError(f"oracle_similarity_delta failed ({rc})")
+        return gram, cos
+
     def monosoup(self, w_base, w_ft, rank: int):
         """MonoSoup merge (R8): W_base + (1/k) sum_i tau_i, tau_i the rank-`rank`
         truncated SVD of Delta_i = fl32(W_i - W_base).  w_base: uint16 [R, C];
@@ -250,6 +278,10 @@ def linear_grouped(*a, **k):
 
 def similarity(*a, **k):
     return default().similarity(*a, **k)
+
+
+def similarity_delta(*a, **k):
+    return default().similarity_delta(*a, **k)
 
 
 def monosoup(*a, **k):

@@ -41,6 +41,11 @@
  *      server holds, tau[r][j] = alpha[r] * s[r][j] with s = +1 for bit 1 and
  *      -1 for bit 0; the similarity of two variants is the cosine of their
  *      task vectors over one matrix, from the dot products (Gram matrix).
+ *   R9 similarity of the full task vectors ([KM] with the task vector of
+ *      [MS], Delta = W_ft - W_base): Delta_v = fl32(W_ft_v - f32(W_base)) as
+ *      in R3; the Gram matrix <Delta_a, Delta_b> in the fixed fp64 order
+ *      given below, cosines as in R7.  R7's form (over the stored 1-bit code)
+ *      is kept beside it: a server that holds only the code can use that one.
  *   R8 MonoSoup ([MS]): Delta_i = fl32(W_i - f32(W_base)) as in R3, then
  *      fp64; tau_i = the exact rank-r truncated SVD (the r largest singular
  *      values and their vectors), computed here by one-sided Jacobi in fp64;
@@ -53,6 +58,17 @@
  * fp64 partials, row r into p[r mod 256] in increasing r, then the halving
  * tree below; gram[a][b] = p[0].  cos[a][b] = gram[a][b] /
  * sqrt(gram[a][a] * gram[b][b]) in fp64 (0 when either norm is 0).
+ *
+ * Fixed order for the full task-vector Gram matrix (R9).  Each product
+ * (double)Delta_a[r][j] * (double)Delta_b[r][j] of two fp32 values is exact in
+ * fp64 (so a fused multiply-add gives the same result as multiply-then-add).
+ * Row term of row r: 64 fp64 partials p[0..63], all +0; the 8-column groups
+ * g = 0 .. C/8-1 in increasing order add their eight products, in increasing
+ * column order, into p[g mod 64]; then for s = 32, 16, ..., 1: p[k] = p[k] +
+ * p[k+s] for k < s; the row term is p[0].  The row terms then follow R7's row
+ * order: row r into q[r mod 256] in increasing r, the 256-wide halving tree,
+ * gram[a][b] = q[0]; cos[a][b] = gram[a][b] / sqrt(gram[a][a] gram[b][b]) (0
+ * when either norm is 0).
  *
  * Fixed summation order for alpha (R4).  For row r with C columns, split the
  * columns into 8-column groups g = 0 .. C/8-1.  There are 256 fp64 partial
@@ -322,6 +338,62 @@ int oracle_similarity(const uint8_t *signs, const float *alpha, int per_matrix, 
             double na = gram[(int64_t)a * V + a], nb = gram[(int64_t)b * V + b];
             double d = sqrt(na * nb);
             cosv[(int64_t)a * V + b] = d > 0.0 ? gram[(int64_t)a * V + b] / d : 0.0;
+        }
+    return 0;
+}
+
+/* ---- similarity of the full task vectors ([KM] step 1, R9) ------------- */
+
+/* The halving tree over 64 fp64 partial sums (s = 32, 16, ..., 1). */
+static double halving_tree_64(double *p)
+{
+    for (int s = 32; s >= 1; s >>= 1)
+        for (int k = 0; k < s; ++k)
+            p[k] = p[k] + p[k + s];
+    return p[0];
+}
+
+/* w_base: bf16 bits [R, C]; w_ft: [V, R, C] fp32 (ft_is_f32 = 1) or bf16
+ * bits (0), variant v at offset v*R*C.  gram, cosv: [V, V] fp64 (both
+ * triangles).  Returns 0, or -1 when C is not a positive multiple of 8, R is
+ * negative or V < 1. */
+int oracle_similarity_delta(const uint16_t *w_base, const void *w_ft, int ft_is_f32, int32_t V, int64_t R,
+                            int64_t C, double *gram, double *cosv)
+{
+    if (R < 0 || C <= 0 || C % 8 != 0 || V < 1)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ab = 0; ab < (int64_t)V * V; ++ab) {
+        int32_t a = (int32_t)(ab / V), b = (int32_t)(ab % V);
+        if (b < a)
+            continue;
+        double q[256];
+        for (int k = 0; k < 256; ++k)
+            q[k] = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+            double p[64];
+            for (int k = 0; k < 64; ++k)
+                p[k] = 0.0;
+            for (int64_t j = 0; j < C; ++j) {
+                float base = oracle_f32_from_bf16(w_base[r * C + j]);
+                float da = w_ft_at(w_ft, ft_is_f32, ((int64_t)a * R + r) * C + j) - base;  /* fl32, R3 */
+                float db = w_ft_at(w_ft, ft_is_f32, ((int64_t)b * R + r) * C + j) - base;
+                double prod = (double)da * (double)db;  /* exact: 24 x 24 significand bits */
+                int k = (int)((j / 8) % 64);
+                p[k] = p[k] + prod;
+            }
+            double term = halving_tree_64(p);
+            q[r % 256] = q[r % 256] + term;
+        }
+        double total = halving_tree_256(q);
+        gram[(int64_t)a * V + b] = total;
+        gram[(int64_t)b * V + a] = total;
+    }
+    for (int32_t a = 0; a < V; ++a)
+        for (int32_t b = 0; b < V; ++b) {
+            double norm2 = gram[(int64_t)a * V + a] * gram[(int64_t)b * V + b];
+            double den = sqrt(norm2);
+            cosv[(int64_t)a * V + b] = den > 0.0 ? gram[(int64_t)a * V + b] / den : 0.0;
         }
     return 0;
 }

@@ -417,6 +417,133 @@ def pin_similarity_invariants(o):
         assert abs(cos[a, b]) < 6.0 / math.sqrt(R * C)
 
 
+# ------------------------------------------- similarity of full task vectors
+
+
+def _delta_case(V, R, C, seed, dyadic, ft_bf16=False):
+    """W_base and V fine-tuned copies.  dyadic: W_base = k 2^-8 (|k| <= 8) and
+    Delta = k 2^-10 (|k| <= 8), so every difference, product and sum below is
+    exact; otherwise W_base ~ N(0, 0.02) bf16 and Delta ~ Laplace(0, b) with a
+    different b per variant (fp32 W_ft = fl32(W_base + Delta))."""
+    if dyadic:
+        kb = (synth.u64((R, C), seed, 7201) % np.uint64(17)).astype(np.int64) - 8
+        base = (kb * 2.0 ** -8).astype(np.float32)
+        kd = (synth.u64((V, R, C), seed, 7202) % np.uint64(17)).astype(np.int64) - 8
+        ft = (base[None] + (kd * 2.0 ** -10)).astype(np.float32)
+        wb = _torch_bf16_bits(base)
+        return wb, (_torch_bf16_bits(ft) if ft_bf16 else ft)
+    wb = synth.to_bf16_bits(synth.normal_f32((R, C), 0.02, seed, 7203))
+    base = synth.bf16_bits_to_f32(wb)
+    fts = []
+    for v in range(V):
+        d = synth.laplace_f32((R, C), 1e-3 * (1 + v), seed, 7204 + v)
+        fts.append((base + d).astype(np.float32))
+    ft = np.stack(fts)
+    return wb, (_torch_bf16_bits(ft) if ft_bf16 else ft)
+
+
+def _deltas64(wb, ft):
+    """Delta = fl32(W_ft - W_base) by numpy's IEEE fp32 subtraction, as fp64."""
+    base = synth.bf16_bits_to_f32(wb)
+    f = synth.bf16_bits_to_f32(ft) if ft.dtype == np.uint16 else ft
+    return (f - base[None]).astype(np.float32).astype(np.float64)
+
+
+def pin_similarity_delta_exact_rational(o):
+    """K-Merge's similarity over the task vector Delta = W_ft - W_base: on
+    dyadic inputs every difference, product and partial sum is exact, so the
+    Gram matrix must equal the exact rational sum of Delta_a Delta_b over every
+    weight (fp32 and bf16 W_ft), and the cosines the exact ratio to fp64
+    rounding."""
+    V, R, C = 3, 5, 24
+    for ft_bf16 in (False, True):
+        wb, ft = _delta_case(V, R, C, seed=61, dyadic=True, ft_bf16=ft_bf16)
+        base = [Fraction(float(v)) for v in synth.bf16_bits_to_f32(wb).ravel()]
+        f = synth.bf16_bits_to_f32(ft) if ft_bf16 else ft
+        d = [[Fraction(float(x)) - base[i] for i, x in enumerate(f[v].ravel())] for v in range(V)]
+        gram, cos = o.similarity_delta(wb, ft)
+        for a in range(V):
+            for b in range(V):
+                exact = sum((d[a][i] * d[b][i] for i in range(R * C)), Fraction(0))
+                assert gram[a, b] == float(exact), (ft_bf16, a, b)
+        for a in range(V):
+            for b in range(V):
+                ref = float(gram[a, b]) / math.sqrt(float(gram[a, a]) * float(gram[b, b]))
+                assert abs(cos[a, b] - ref) <= 2 * np.spacing(abs(ref) + 1e-300)
+
+
+def pin_similarity_delta_rounding_bound(o):
+    """Random Laplace deltas over 300 rows of 1024 columns (every one of the
+    64 column partials and the 256 row partials visited at least twice): each
+    Gram entry lies within the worst-case rounding of its summation tree of
+    the correctly rounded exact sum (math.fsum of the exact fp64 products),
+    and agrees with numpy's float64 einsum over the fp32 differences to a
+    relative 1e-12."""
+    V, R, C = 3, 300, 1024
+    wb, ft = _delta_case(V, R, C, seed=62, dyadic=False)
+    d = _deltas64(wb, ft)
+    gram, cos = o.similarity_delta(wb, ft)
+    depth = (C // 8) // 64 * 8 + 6 + (R + 255) // 256 + 8 + 1
+    for a in range(V):
+        for b in range(V):
+            prods = (d[a] * d[b]).ravel()
+            exact = math.fsum(prods)
+            bound = depth * 2.0 ** -53 * float(np.sum(np.abs(prods)))
+            assert abs(gram[a, b] - exact) <= bound, (a, b, gram[a, b], exact, bound)
+    ref = np.einsum("arj,brj->ab", d, d)
+    assert np.allclose(gram, ref, rtol=1e-12, atol=0)
+    nrm = np.sqrt(np.diag(ref))
+    assert np.allclose(cos, ref / nrm[:, None] / nrm[None, :], rtol=1e-12, atol=1e-15)
+
+
+def pin_similarity_delta_invariants(o):
+    """Symmetry, unit self-similarity, -1 for the negated delta, +1 and four
+    times the squared norm for the doubled delta (exact on dyadic inputs),
+    equivariance under a permutation of the variants, near-zero cosine for
+    independent Laplace deltas."""
+    V, R, C = 4, 40, 136
+    wb, ft = _delta_case(V, R, C, seed=63, dyadic=True)
+    base = synth.bf16_bits_to_f32(wb)
+    ft[2] = (base - (ft[0] - base)).astype(np.float32)          # Delta_2 = -Delta_0
+    ft[3] = (base + 2 * (ft[0] - base)).astype(np.float32)      # Delta_3 = 2 Delta_0
+    gram, cos = o.similarity_delta(wb, ft)
+    assert np.array_equal(gram, gram.T)
+    assert np.all(np.abs(np.diag(cos) - 1.0) <= 2.0 ** -52)
+    assert gram[0, 2] == -gram[0, 0] and abs(cos[0, 2] + 1.0) <= 2.0 ** -52
+    assert gram[3, 3] == 4 * gram[0, 0] and abs(cos[0, 3] - 1.0) <= 2.0 ** -52
+    perm = np.array([2, 0, 3, 1])
+    gp, _ = o.similarity_delta(wb, ft[perm])
+    assert np.array_equal(gp, gram[np.ix_(perm, perm)])
+    wb2, ft2 = _delta_case(3, 64, 256, seed=64, dyadic=False)
+    _, c2 = o.similarity_delta(wb2, ft2)
+    for a, b in ((0, 1), (1, 2)):
+        assert abs(c2[a, b]) < 6.0 / math.sqrt(64 * 256)
+
+
+def pin_similarity_delta_matches_code(o):
+    """A delta of one magnitude per row (Delta = alpha_r s, alpha_r dyadic) is
+    exactly what the 1-bit code stores: compress gives back alpha_r and s, and
+    the Gram matrix of the full task vectors then equals the Gram matrix of
+    the code (a second oracle function), bit for bit."""
+    V, R, C = 3, 20, 64
+    kb = (synth.u64((R, C), 65, 7205) % np.uint64(17)).astype(np.int64) - 8
+    base = (kb * 2.0 ** -8).astype(np.float32)
+    wb = _torch_bf16_bits(base)
+    alpha = ((1 + synth.u64((V, R), 65, 7206) % np.uint64(8)).astype(np.float64) * 2.0 ** -11).astype(np.float32)
+    s = 2.0 * (synth.u64((V, R, C), 65, 7207) % np.uint64(2)).astype(np.float64) - 1.0
+    ft = (base[None] + alpha[:, :, None] * s).astype(np.float32)
+    signs, alphas = [], []
+    for v in range(V):
+        sv, av = o.compress(wb, ft[v])
+        assert np.array_equal(av, alpha[v])
+        signs.append(sv)
+        alphas.append(av)
+    g_code, c_code = o.similarity(np.stack(signs), np.stack(alphas))
+    g_full, c_full = o.similarity_delta(wb, ft)
+    assert np.array_equal(g_code, g_full)
+    assert np.array_equal(c_code, c_full)
+
+
 def _orthonormal(rng, n, k):
     q, _ = np.linalg.qr(rng.standard_normal((n, k)))
     return q
@@ -508,4 +635,6 @@ ALL = [pin_bf16_widen, pin_bf16_round, pin_bf16_hand_ties, pin_compress_handbuil
        pin_alpha_least_squares, pin_reconstruct_hand_cases, pin_reconstruct_vs_torch,
        pin_linear_exact_rational, pin_linear_vs_numpy, pin_linear_dyadic, pin_grouped,
        pin_shape_4096, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants,
+       pin_similarity_delta_exact_rational, pin_similarity_delta_rounding_bound, pin_similarity_delta_invariants,
+       pin_similarity_delta_matches_code,
        pin_monosoup_known_svd, pin_monosoup_vs_numpy, pin_monosoup_special_cases]

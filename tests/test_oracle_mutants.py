@@ -54,6 +54,14 @@ MUTANTS = {
                                        "sigma[(int64_t)ck * n + j] = norm[order[0]];"),
     "monosoup_first_checkpoint": ("const float *wi = w_ft + (int64_t)ck * R * C;", "const float *wi = w_ft;"),
     "monosoup_rank_minus_one": ("for (int32_t t = 0; t < r; ++t)", "for (int32_t t = 1; t < r; ++t)"),
+    "simdelta_base_kept_in_b": ("float db = w_ft_at(w_ft, ft_is_f32, ((int64_t)b * R + r) * C + j) - base;",
+                                "float db = w_ft_at(w_ft, ft_is_f32, ((int64_t)b * R + r) * C + j);"),
+    "simdelta_row_of_a_twice": ("float db = w_ft_at(w_ft, ft_is_f32, ((int64_t)b * R + r) * C + j) - base;",
+                                "float db = w_ft_at(w_ft, ft_is_f32, ((int64_t)a * R + r) * C + j) - base;"),
+    "simdelta_fp32_products": ("double prod = (double)da * (double)db;", "double prod = (double)(da * db);"),
+    "simdelta_tree_drops_last": ("for (int s = 32; s >= 1; s >>= 1)", "for (int s = 32; s >= 2; s >>= 1)"),
+    "simdelta_rows_tree_skipped": ("double total = halving_tree_256(q);", "double total = q[0];"),
+    "simdelta_no_sqrt": ("double den = sqrt(norm2);", "double den = norm2;"),
     "similarity_row_of_b": ("const uint8_t *rb = signs + ((int64_t)b * R + r) * G;",
                             "const uint8_t *rb = signs + ((int64_t)a * R + r) * G;"),
 }
