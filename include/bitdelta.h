@@ -183,6 +183,39 @@ BD_API bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, i
                               double *gram, double *cosine,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* -------------------------------------------------------- similarity_delta
+ * "K-Merge: Online LoRA Adapter Management for the Edge", step 1 of the pool
+ * policy (the cosine similarity of two adapters' task vectors), with the task
+ * vector of section "MonoSoup": the fine-tuned weights minus the base
+ * weights.  For n_variants fine-tuned copies W_ft_v of one matrix,
+ * Delta_v[r][j] = fl32(W_ft_v[r][j] - W_base[r][j]) (the same fp32 difference
+ * as bitdelta_compress).  Outputs (fp64 [n_variants, n_variants], row-major,
+ * both triangles, device, 8-byte aligned):
+ *   gram[a][b]   = <Delta_a, Delta_b>, summed in a fixed order: per row r the
+ *                  products Delta_a Delta_b (exact in fp64) of 8-column group
+ *                  g go into partial g mod 64 (columns and groups in
+ *                  increasing order), the 64 partials are combined by the
+ *                  halving tree p[k] += p[k + s], s = 32 .. 1; the row terms
+ *                  then go into partial r mod 256 in increasing r, combined
+ *                  by the halving tree s = 128 .. 1.  The same bits on every
+ *                  call and every GPU.
+ *   cosine[a][b] = gram[a][b] / sqrt(gram[a][a] * gram[b][b]) (0 when a
+ *                  norm is 0).
+ * w_base: bf16 [d_out, d_in]; w_ft: [n_variants, d_out, d_in] of type
+ * ft_dtype (BD_BF16 or BD_F32), variant v at element offset v*d_out*d_in;
+ * both 16-byte aligned.  n_variants in [1, 16] (BD_EINVAL otherwise).
+ * Unlike bitdelta_similarity this reads the full-precision weights (HBM-bound
+ * on W_ft); it needs no compressed code.
+ * workspace: at least bitdelta_similarity_delta_workspace() bytes (fp64 per
+ * row and pair of variants, diagonal included), 8-byte aligned; owned by the
+ * caller, scratch on entry, undefined after; calls in flight at once must
+ * not share one. */
+BD_API size_t bitdelta_similarity_delta_workspace(int32_t n_variants, int64_t d_out, int64_t d_in);
+BD_API bd_status bitdelta_similarity_delta(const bd_bf16 *w_base, const void *w_ft, int ft_dtype,
+                                    int32_t n_variants, int64_t d_out, int64_t d_in,
+                                    double *gram, double *cosine,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------- MonoSoup
  * "BitDelta: Serving 14 Zen Models from One GPU Cluster", section "MonoSoup":
  * k fine-tuned checkpoints W_1..W_k of one matrix are merged through the

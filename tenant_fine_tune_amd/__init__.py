@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
-           "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
+           "similarity_delta", "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
            "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
            "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
@@ -53,6 +53,8 @@ EXPORTS = {
     "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
     "bitdelta_similarity_workspace": (_SZ, [_I32, _I64, _I64]),
     "bitdelta_similarity": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitdelta_similarity_delta_workspace": (_SZ, [_I32, _I64, _I64]),
+    "bitdelta_similarity_delta": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "bitdelta_monosoup_workspace": (_SZ, [_I64, _I64, _I32, _I32]),
     "bitdelta_monosoup": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     # include/bitdelta_cache.h
@@ -249,6 +251,29 @@ def similarity(signs, alpha, per_matrix: bool | None = None):
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=signs.device)
     check(lib.bitdelta_similarity(_ptr(signs), _ptr(alpha), mode, V, d_out, d_in, _ptr(gram), _ptr(cos), _ptr(ws),
                                   nws, _stream(signs.device)))
+    return gram, cos
+
+
+def similarity_delta(w_base, w_ft):
+    """Gram matrix <Delta_a, Delta_b> and cosines of V variants' full task
+    vectors Delta_v = fl32(W_ft_v - W_base) over one matrix.  w_base bf16
+    [d_out, d_in]; w_ft fp32 or bf16 [V, d_out, d_in].  Returns (gram,
+    cosine), float64 [V, V] on the weights' device."""
+    torch = _torch()
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    if w_ft.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("w_ft must be float32 or bfloat16")
+    _dev_tensor(w_ft, w_ft.dtype, "w_ft")
+    if w_ft.dim() != 3 or w_base.dim() != 2 or tuple(w_ft.shape[1:]) != tuple(w_base.shape):
+        raise ValueError("w_ft must be [V, d_out, d_in] over w_base [d_out, d_in]")
+    V, d_out, d_in = w_ft.shape
+    gram = torch.empty((V, V), dtype=torch.float64, device=w_base.device)
+    cos = torch.empty((V, V), dtype=torch.float64, device=w_base.device)
+    nws = lib.bitdelta_similarity_delta_workspace(V, d_out, d_in)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=w_base.device)
+    ft = BD_F32 if w_ft.dtype == torch.float32 else BD_BF16
+    check(lib.bitdelta_similarity_delta(_ptr(w_base), _ptr(w_ft), ft, V, d_out, d_in, _ptr(gram), _ptr(cos),
+                                        _ptr(ws), nws, _stream(w_base.device)))
     return gram, cos
 
 

@@ -315,6 +315,41 @@ bd_status bitdelta_similarity(const uint8_t *signs, const float *alpha, int alph
                   "bitdelta_similarity");
 }
 
+size_t bitdelta_similarity_delta_workspace(int32_t n_variants, int64_t d_out, int64_t d_in)
+{
+    (void)d_in;
+    if (n_variants < 1 || n_variants > bd::kSimilarityMaxVariants)
+        return 0;
+    return bd::similarity_delta_workspace_bytes(n_variants, d_out);
+}
+
+bd_status bitdelta_similarity_delta(const bd_bf16 *w_base, const void *w_ft, int ft_dtype, int32_t n_variants,
+                                    int64_t d_out, int64_t d_in, double *gram, double *cosine, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    if (ft_dtype != BD_BF16 && ft_dtype != BD_F32)
+        return fail(BD_EINVAL, "ft_dtype must be BD_BF16 (0) or BD_F32 (1), got %d", ft_dtype);
+    if (n_variants < 1 || n_variants > bd::kSimilarityMaxVariants)
+        return fail(BD_EINVAL, "n_variants must be in [1, %d] (got %d)", bd::kSimilarityMaxVariants, n_variants);
+    BD_TRY(check_matrix(d_out, d_in));
+    const size_t need = bitdelta_similarity_delta_workspace(n_variants, d_out, d_in);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "similarity_delta needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    BD_NONNULL(w_base);
+    BD_NONNULL(w_ft);
+    BD_NONNULL(gram);
+    BD_NONNULL(cosine);
+    BD_NONNULL(workspace);
+    BD_ALIGNED(w_base, 16);
+    BD_ALIGNED(w_ft, 16);
+    BD_ALIGNED(gram, 8);
+    BD_ALIGNED(cosine, 8);
+    BD_ALIGNED(workspace, 8);
+    return device(bd::launch_similarity_delta(w_base, w_ft, ft_dtype == BD_F32, n_variants, d_out, d_in, gram, cosine,
+                                              static_cast<double *>(workspace), (hipStream_t)stream),
+                  "bitdelta_similarity_delta");
+}
+
 size_t bitdelta_monosoup_workspace(int64_t rows, int64_t cols, int32_t k, int32_t rank)
 {
     const int64_t lim = (int64_t)1 << 21;

@@ -61,6 +61,15 @@ hipError_t launch_similarity(const uint8_t *signs, const float *alpha, bool per_
                              int64_t d_out, int64_t d_in, double *gram, double *cosine, int32_t *counts,
                              hipStream_t s);
 
+// similarity_delta.hip: Gram matrix and cosines of up to
+// kSimilarityMaxVariants variants' full task vectors W_ft - W_base; `terms`
+// holds similarity_delta_workspace_bytes() bytes (fp64 per row and pair,
+// diagonal included).
+size_t similarity_delta_workspace_bytes(int32_t n_variants, int64_t d_out);
+hipError_t launch_similarity_delta(const uint16_t *w_base, const void *w_ft, bool ft_f32, int32_t n_variants,
+                                   int64_t d_out, int64_t d_in, double *gram, double *cosine, double *terms,
+                                   hipStream_t s);
+
 // monosoup.hip: MonoSoup merge through a 64-column randomized range finder.
 constexpr int kMsL = 64;
 size_t monosoup_workspace_bytes(int64_t rows, int64_t cols, int32_t k, int32_t rank);

@@ -257,3 +257,31 @@ def test_similarity_validation(bd):
     assert call(signs=FAKE_ODD) == bd.BD_EALIGN
     assert call(gram=ctypes.c_void_p(4100)) == bd.BD_EALIGN
     assert call(ws=FAKE_ODD) == bd.BD_EALIGN
+
+
+def test_similarity_delta_validation(bd):
+    """Host-side checks of bitdelta_similarity_delta (FAKE pointers are never
+    dereferenced: every call below fails before a launch)."""
+    W = bd.lib.bitdelta_similarity_delta_workspace
+    f = bd.lib.bitdelta_similarity_delta
+    assert W(14, 8192, 8192) == 8 * 8192 * 105       # fp64 per row and pair, diagonal included
+    assert W(1, 100, 64) == 8 * 100
+    assert W(17, 100, 64) == 0 and W(0, 100, 64) == 0
+    need = W(4, 64, 256)
+    ok = (FAKE, FAKE, 1, 4, 64, 256, FAKE, FAKE, FAKE, need, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["wb", "wft", "ft", "V", "d_out", "d_in", "gram", "cos", "ws", "nws", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(ft=2) == bd.BD_EINVAL
+    assert call(V=0) == bd.BD_EINVAL and call(V=17) == bd.BD_EINVAL
+    assert call(d_in=12) == bd.BD_ESHAPE and call(d_out=0) == bd.BD_ESHAPE and call(d_in=0) == bd.BD_ESHAPE
+    assert call(nws=need - 1) == bd.BD_EWORKSPACE
+    assert call(wb=None) == bd.BD_EINVAL and call(wft=None) == bd.BD_EINVAL
+    assert call(gram=None) == bd.BD_EINVAL and call(cos=None) == bd.BD_EINVAL and call(ws=None) == bd.BD_EINVAL
+    assert call(wb=FAKE_ODD) == bd.BD_EALIGN and call(wft=ctypes.c_void_p(4104)) == bd.BD_EALIGN
+    assert call(gram=ctypes.c_void_p(4100)) == bd.BD_EALIGN and call(ws=ctypes.c_void_p(4100)) == bd.BD_EALIGN
