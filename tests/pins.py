@@ -341,6 +341,66 @@ def pin_shape_4096(o):
     assert np.all(signs == 0xFF) and np.all(alpha == 0)
 
 
+STACK_SHAPES = {"q": (8192, 8192), "k": (1024, 8192), "v": (1024, 8192), "o": (8192, 8192),
+                "gate": (28672, 8192), "up": (28672, 8192), "down": (8192, 28672)}
+STACK_LAYERS = 80
+
+
+def _sign_bytes_written(o, R, C):
+    """Bytes of packed signs the C oracle writes for an R x C matrix whose
+    deltas are all >= 0, counted in a buffer with a sentinel tail (the
+    wrapper's own allocation is bypassed, so an oracle that wrote more or
+    fewer than one bit per weight shows here)."""
+    import ctypes
+
+    w_base = np.zeros((R, C), dtype=np.uint16)
+    w_ft = np.zeros((R, C), dtype=np.float32)
+    n = R * C // 8
+    buf = np.full(n + 4096, 0xA5, dtype=np.uint8)
+    alpha = np.zeros(R, dtype=np.float32)
+    sums = np.zeros(R, dtype=np.float64)
+    P = ctypes.c_void_p
+    rc = o.lib.oracle_compress(w_base.ctypes.data_as(P), w_ft.ctypes.data_as(P), 1, R, C, 0,
+                               buf.ctypes.data_as(P), alpha.ctypes.data_as(P), sums.ctypes.data_as(P))
+    assert rc == 0
+    assert np.all(buf[n:] == 0xA5), "the oracle wrote past one bit per weight"
+    written = int(np.count_nonzero(buf[:n] == 0xFF))
+    assert written == n, "the oracle left part of the packed code unwritten"
+    return written
+
+
+def pin_storage_arithmetic(o):
+    """The post's storage arithmetic ("Mathematical Foundation"): a 70B model
+    in bf16 is 140 GB; fourteen full copies are 1.96 TB; one bit per weight is
+    8.75 GB per variant, so the base plus 14 delta sets is 262.5 GB, 86.6%
+    less ("-87%").  The oracle's packed code holds exactly one bit per weight
+    on every matrix shape of the 70B-shaped stack (80 layers of q, k, v, o,
+    gate, up, down, counted with a sentinel past the code), so one variant of
+    the stack's 68,451,041,280 weights is 8,556,380,160 sign bytes; its fp32
+    alpha per output row adds 26,869,760 bytes, 0.31% of the signs (32/d_in,
+    not the post's 'about 0.1%', a reading recorded in the design notes)."""
+    n = 70e9
+    assert n * 2 == 140e9
+    assert n / 8 == 8.75e9
+    assert 14 * n * 2 == 1.96e12
+    total = n * 2 + 14 * n / 8
+    assert total == 262.5e9
+    assert round(100 * (1 - total / 1.96e12), 1) == 86.6
+    per_row = {}
+    for d_out, d_in in set(STACK_SHAPES.values()):
+        per_row[d_in] = _sign_bytes_written(o, 2, d_in) // 2
+        assert per_row[d_in] * 8 == d_in
+    params = STACK_LAYERS * sum(d_out * d_in for d_out, d_in in STACK_SHAPES.values())
+    sign_bytes = STACK_LAYERS * sum(d_out * per_row[d_in] for d_out, d_in in STACK_SHAPES.values())
+    assert params == 68_451_041_280
+    assert sign_bytes == 8_556_380_160 == params // 8
+    alpha_bytes = STACK_LAYERS * sum(4 * d_out for d_out, _ in STACK_SHAPES.values())
+    assert alpha_bytes == 26_869_760
+    assert round(100 * alpha_bytes / sign_bytes, 2) == 0.31
+    # the post's [4096, 4096] -> [4096, 512] example ("Infrastructure Details")
+    assert _sign_bytes_written(o, 4096, 4096) == 4096 * 512
+
+
 # --------------------------------------------------------------- similarity
 
 
@@ -634,7 +694,7 @@ ALL = [pin_bf16_widen, pin_bf16_round, pin_bf16_hand_ties, pin_compress_handbuil
        pin_compress_packing_vs_numpy, pin_alpha_exact_mean, pin_alpha_laplace,
        pin_alpha_least_squares, pin_reconstruct_hand_cases, pin_reconstruct_vs_torch,
        pin_linear_exact_rational, pin_linear_vs_numpy, pin_linear_dyadic, pin_grouped,
-       pin_shape_4096, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants,
+       pin_shape_4096, pin_storage_arithmetic, pin_similarity_exact_rational, pin_similarity_vs_numpy, pin_similarity_invariants,
        pin_similarity_delta_exact_rational, pin_similarity_delta_rounding_bound, pin_similarity_delta_invariants,
        pin_similarity_delta_matches_code,
        pin_monosoup_known_svd, pin_monosoup_vs_numpy, pin_monosoup_special_cases]
