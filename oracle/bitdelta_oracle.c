@@ -400,12 +400,13 @@ int oracle_similarity_delta(const uint16_t *w_base, const void *w_ft, int ft_is_
 
 /* ---- MonoSoup merge ([MS], R8) ------------------------------------------ */
 
-/* One-sided Jacobi (Hestenes): rotate column pairs of A [m, n] (row-major,
- * overwritten, m >= n) until every pair is orthogonal to 1e-15 relative; V
- * [n, n] accumulates the rotations.  Afterwards column j of A is sigma_j u_j
- * and A = (A V^T) V, i.e. the input equals sum_j A[:, j] V[:, j]^T.  Columns
- * whose squared norm is below 1e-30 of the whole matrix's (singular values
- * under 1e-15 of its norm) are left alone. */
+/* One-sided Jacobi (Hestenes) on a matrix M [m, n], m >= n, held by columns
+ * (entry (i, j) at A[j*m + i], overwritten): rotate column pairs until every
+ * pair is orthogonal to 1e-15 relative; V [n, n], also held by columns (entry
+ * (i, j) at V[j*n + i]), accumulates the rotations.  Afterwards column j of
+ * A is sigma_j u_j and M = sum_j A[:, j] V[:, j]^T.  Columns whose squared
+ * norm is below 1e-30 of the whole matrix's (singular values under 1e-15 of
+ * its norm) are left alone. */
 static void jacobi_columns(double *A, int64_t m, int64_t n, double *V)
 {
     double frob2 = 0.0;
@@ -420,9 +421,10 @@ static void jacobi_columns(double *A, int64_t m, int64_t n, double *V)
         int rotated = 0;
         for (int64_t p = 0; p < n - 1; ++p)
             for (int64_t q = p + 1; q < n; ++q) {
+                double *cp = A + p * m, *cq = A + q * m;
                 double alpha = 0.0, beta = 0.0, gamma = 0.0;
                 for (int64_t i = 0; i < m; ++i) {
-                    double ap = A[i * n + p], aq = A[i * n + q];
+                    double ap = cp[i], aq = cq[i];
                     alpha += ap * ap;
                     beta += aq * aq;
                     gamma += ap * aq;
@@ -434,14 +436,15 @@ static void jacobi_columns(double *A, int64_t m, int64_t n, double *V)
                 double tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
                 double c = 1.0 / sqrt(1.0 + tt * tt), s = c * tt;
                 for (int64_t i = 0; i < m; ++i) {
-                    double ap = A[i * n + p], aq = A[i * n + q];
-                    A[i * n + p] = c * ap - s * aq;
-                    A[i * n + q] = s * ap + c * aq;
+                    double ap = cp[i], aq = cq[i];
+                    cp[i] = c * ap - s * aq;
+                    cq[i] = s * ap + c * aq;
                 }
+                double *vp = V + p * n, *vq = V + q * n;
                 for (int64_t i = 0; i < n; ++i) {
-                    double vp = V[i * n + p], vq = V[i * n + q];
-                    V[i * n + p] = c * vp - s * vq;
-                    V[i * n + q] = s * vp + c * vq;
+                    double xp = vp[i], xq = vq[i];
+                    vp[i] = c * xp - s * xq;
+                    vq[i] = s * xp + c * xq;
                 }
             }
         if (!rotated)
@@ -463,31 +466,40 @@ int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_
     const int wide = C > R;
     if (k < 1 || R < 1 || C < 1 || r < 0 || r > n)
         return -1;
-    double *A = malloc(sizeof(double) * m * n), *V = malloc(sizeof(double) * n * n);
-    double *norm = malloc(sizeof(double) * n);
-    int64_t *order = malloc(sizeof(int64_t) * n);
-    if (!A || !V || !norm || !order) {
-        free(A); free(V); free(norm); free(order);
+    /* tau[ck] holds checkpoint ck's truncation; the checkpoints are
+     * independent (one thread each), and their sum below runs in checkpoint
+     * order */
+    double *tau = malloc(sizeof(double) * (size_t)k * R * C);
+    if (!tau)
         return -1;
-    }
-    for (int64_t i = 0; i < R * C; ++i)
-        out[i] = 0.0; /* sum of the tau_i until the end */
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
     for (int32_t ck = 0; ck < k; ++ck) {
+        double *A = malloc(sizeof(double) * m * n), *V = malloc(sizeof(double) * n * n);
+        double *norm = malloc(sizeof(double) * n);
+        int64_t *order = malloc(sizeof(int64_t) * n);
+        if (!A || !V || !norm || !order) {
+            free(A); free(V); free(norm); free(order);
+            failed = 1;
+            continue;
+        }
         const float *wi = w_ft + (int64_t)ck * R * C;
-        /* A = Delta_i [R, C], or its transpose [C, R] when wide */
+        double *tk = tau + (int64_t)ck * R * C;
+        /* M = Delta_i [R, C], or its transpose [C, R] when wide, held by
+         * columns: M(i, j) at A[j*m + i] */
         for (int64_t i = 0; i < R; ++i)
             for (int64_t c = 0; c < C; ++c) {
                 double d = (double)(wi[i * C + c] - oracle_f32_from_bf16(w_base[i * C + c]));
                 if (wide)
-                    A[c * n + i] = d;
+                    A[i * m + c] = d;
                 else
-                    A[i * n + c] = d;
+                    A[c * m + i] = d;
             }
         jacobi_columns(A, m, n, V);
         for (int64_t j = 0; j < n; ++j) {
             double s = 0.0;
             for (int64_t i = 0; i < m; ++i)
-                s += A[i * n + j] * A[i * n + j];
+                s += A[j * m + i] * A[j * m + i];
             norm[j] = sqrt(s);
             order[j] = j;
         }
@@ -503,21 +515,30 @@ int oracle_monosoup(const uint16_t *w_base, const float *w_ft, int32_t k, int64_
         if (sigma)
             for (int64_t j = 0; j < n; ++j)
                 sigma[(int64_t)ck * n + j] = norm[order[j]];
-        /* truncation of A = sum over the r largest of A[:, j] V[:, j]^T; tau_i
+        /* truncation of M = sum over the r largest of A[:, j] V[:, j]^T; tau_i
          * is that, or its transpose when wide */
         for (int64_t i = 0; i < m; ++i)
             for (int64_t c = 0; c < n; ++c) {
                 double s = 0.0;
                 for (int32_t t = 0; t < r; ++t) {
                     int64_t j = order[t];
-                    s += A[i * n + j] * V[c * n + j];
+                    s += A[j * m + i] * V[j * n + c];
                 }
-                out[wide ? c * C + i : i * C + c] += s;
+                tk[wide ? c * C + i : i * C + c] = s;
             }
+        free(A); free(V); free(norm); free(order);
     }
-    for (int64_t i = 0; i < R * C; ++i)
-        out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i] / (double)k;
-    free(A); free(V); free(norm); free(order);
+    if (failed) {
+        free(tau);
+        return -1;
+    }
+    for (int64_t i = 0; i < R * C; ++i) {
+        double acc = 0.0; /* sum of the tau_i, in checkpoint order */
+        for (int32_t ck = 0; ck < k; ++ck)
+            acc += tau[(int64_t)ck * R * C + i];
+        out[i] = (double)oracle_f32_from_bf16(w_base[i]) + acc / (double)k;
+    }
+    free(tau);
     return 0;
 }
 

@@ -42,14 +42,14 @@ MUTANTS = {
     "similarity_alpha_twice": ("double term = ((double)fa * (double)fb) * (double)c;",
                                "double term = ((double)fa * (double)fa) * (double)c;"),
     "similarity_no_sqrt": ("double d = sqrt(na * nb);", "double d = na * nb;"),
-    "monosoup_no_mean": ("out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i] / (double)k;",
-                         "out[i] = (double)oracle_f32_from_bf16(w_base[i]) + out[i];"),
+    "monosoup_no_mean": ("out[i] = (double)oracle_f32_from_bf16(w_base[i]) + acc / (double)k;",
+                         "out[i] = (double)oracle_f32_from_bf16(w_base[i]) + acc;"),
     "monosoup_smallest_first": ("while (b > 0 && norm[order[b - 1]] < norm[v])",
                                 "while (b > 0 && norm[order[b - 1]] > norm[v])"),
     "monosoup_no_base": ("double d = (double)(wi[i * C + c] - oracle_f32_from_bf16(w_base[i * C + c]));",
                          "double d = (double)wi[i * C + c];"),
-    "monosoup_v_transposed": ("s += A[i * n + j] * V[c * n + j];", "s += A[i * n + j] * V[j * n + c];"),
-    "monosoup_rotation_sign": ("A[i * n + p] = c * ap - s * aq;", "A[i * n + p] = c * ap + s * aq;"),
+    "monosoup_v_transposed": ("s += A[j * m + i] * V[j * n + c];", "s += A[j * m + i] * V[c * n + j];"),
+    "monosoup_rotation_sign": ("cp[i] = c * ap - s * aq;", "cp[i] = c * ap + s * aq;"),
     "monosoup_sigma_of_first_column": ("sigma[(int64_t)ck * n + j] = norm[order[j]];",
                                        "sigma[(int64_t)ck * n + j] = norm[order[0]];"),
     "monosoup_first_checkpoint": ("const float *wi = w_ft + (int64_t)ck * R * C;", "const float *wi = w_ft;"),
