@@ -226,16 +226,22 @@ BD_API bd_status bitdelta_similarity_delta(const bd_bf16 *w_base, const void *w_
  * BD_MONOSOUP_SKETCH (64) columns: Y = Delta Omega, then power_iters rounds
  * of Y <- Delta (Delta^T Y) with the sketch re-orthonormalised between
  * products, then the exact rank-r truncation of the projection of Delta onto
- * range(Y).  It equals the exact truncated SVD when Delta has rank at most
- * 64; otherwise its distance from it shrinks with the gap between the r-th
- * and the 65th singular value and with power_iters.
+ * range(Y).  It equals the exact truncated SVD (up to fp32 rounding) when
+ * Delta has rank at most 64.  Otherwise its relative distance from it is at
+ * most about sqrt(2) t0 (sigma_65 / sigma_r)^(2 power_iters + 1)
+ * sigma_1 / sigma_r in exact arithmetic (t0 = ||(V_rest^T Omega)(V_64^T
+ * Omega)^-1||_2, V_64 the 64 leading right singular vectors of Delta) plus
+ * fp32 rounding, which grows as sigma_r approaches sigma_{r+1}: a spectrum
+ * that drops after the r-th value needs one or two rounds, a flat one (a
+ * random Laplace delta: sigma_65 / sigma_32 about 0.93) one to two hundred.
+ * Each round costs two passes over the k task vectors and two whitenings.
  *   w_base: bf16 [rows, cols], 8-byte aligned.
  *   w_ft:   fp32 [k, rows, cols] (checkpoint i at offset i*rows*cols),
  *           16-byte aligned.
  *   omega:  fp32 [cols, 64], 16-byte aligned: the test matrix, normally
  *           i.i.d. N(0, 1) drawn by the caller (unused, may be NULL, when
  *           rank is 0).
- *   rank:   r in [0, min(64, rows, cols)]; power_iters in [0, 4]
+ *   rank:   r in [0, min(64, rows, cols)]; power_iters in [0, 256]
  *           (BD_EINVAL otherwise); k in [1, 64] (BD_EINVAL).
  *   rows >= 1, cols >= 4 a multiple of 4, both at most 2^21 (BD_ESHAPE).
  *   w_merged: fp32 [rows, cols], 16-byte aligned: f32(W_base) + the fp32

@@ -371,8 +371,8 @@ bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, const floa
     const int64_t max_rank = rows < cols ? (rows < bd::kMsL ? rows : bd::kMsL) : (cols < bd::kMsL ? cols : bd::kMsL);
     if (rank < 0 || rank > max_rank)
         return fail(BD_EINVAL, "monosoup rank must be in [0, %lld] (got %d)", (long long)max_rank, rank);
-    if (power_iters < 0 || power_iters > 4)
-        return fail(BD_EINVAL, "monosoup power_iters must be in [0, 4] (got %d)", power_iters);
+    if (power_iters < 0 || power_iters > 256)
+        return fail(BD_EINVAL, "monosoup power_iters must be in [0, 256] (got %d)", power_iters);
     const size_t need = bitdelta_monosoup_workspace(rows, cols, k, rank);
     if (workspace_bytes < need)
         return fail(BD_EWORKSPACE, "monosoup needs %zu workspace bytes, got %zu", need, workspace_bytes);

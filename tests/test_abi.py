@@ -215,7 +215,7 @@ def test_monosoup_validation(bd):
     assert call(k=0) == bd.BD_EINVAL and call(k=65) == bd.BD_EINVAL
     assert call(r=-1) == bd.BD_EINVAL and call(r=65) == bd.BD_EINVAL
     assert call(R=20, r=21) == bd.BD_EINVAL                # rank above min(rows, cols)
-    assert call(q=-1) == bd.BD_EINVAL and call(q=5) == bd.BD_EINVAL
+    assert call(q=-1) == bd.BD_EINVAL and call(q=257) == bd.BD_EINVAL
     assert call(nws=need - 1) == bd.BD_EWORKSPACE
     assert call(wb=None) == bd.BD_EINVAL and call(out=None) == bd.BD_EINVAL and call(om=None) == bd.BD_EINVAL
     assert call(ws=None) == bd.BD_EINVAL
