@@ -228,10 +228,15 @@ size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t 
     return bd::grouped_workspace_bytes(m, n_variants);
 }
 
-bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids, int32_t n_variants,
-                                  const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
-                                  int alpha_mode, int64_t d_out, int64_t d_in, bd_bf16 *y,
-                                  void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two grouped entry points (everything but the table's
+// memory); BD_OK with *empty set for m = 0, a no-op.
+bd_status check_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids, int32_t n_variants,
+                        const bd_bf16 *w_base, const uint8_t *signs, const float *alpha, int alpha_mode,
+                        int64_t d_out, int64_t d_in, bd_bf16 *y)
 {
     BD_TRY(check_mode(alpha_mode));
     if (n_variants <= 0 || n_variants > 4096)
@@ -241,9 +246,6 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
         return fail(BD_ESHAPE, "m must be >= 0 (got %lld)", (long long)m);
     if (m > std::numeric_limits<int32_t>::max() / 2)
         return fail(BD_ESHAPE, "grouped m=%lld too large for int32 token indices", (long long)m);
-    const size_t need = bitdelta_linear_grouped_workspace(m, n_variants, d_out, d_in);
-    if (workspace_bytes < need)
-        return fail(BD_EWORKSPACE, "linear_grouped needs %zu workspace bytes, got %zu", need, workspace_bytes);
     if (m == 0)
         return BD_OK;
     BD_NONNULL(x);
@@ -252,19 +254,37 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
     BD_NONNULL(signs);
     BD_NONNULL(alpha);
     BD_NONNULL(y);
-    BD_NONNULL(workspace);
     BD_ALIGNED(x, 16);
     BD_ALIGNED(w_base, 16);
     BD_ALIGNED(y, 16);
     BD_ALIGNED(alpha, 4);
     BD_ALIGNED(variant_ids, 4);
-    BD_ALIGNED(workspace, 16);
     if (!operands_fit(m, d_out, d_in))
         return fail(BD_ESHAPE, "grouped operands must each be below 2 GiB (m=%lld, d_out=%lld, d_in=%lld)",
                     (long long)m, (long long)d_out, (long long)d_in);
     const int64_t tiles = bd::grouped_max_tiles(m, n_variants) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
     if (tiles > kMaxGrid)
         return fail(BD_ESHAPE, "grouped m=%lld d_out=%lld exceeds the grid", (long long)m, (long long)d_out);
+    return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *variant_ids, int32_t n_variants,
+                                  const bd_bf16 *w_base, const uint8_t *signs, const float *alpha,
+                                  int alpha_mode, int64_t d_out, int64_t d_in, bd_bf16 *y,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    BD_TRY(check_grouped(x, m, variant_ids, n_variants, w_base, signs, alpha, alpha_mode, d_out, d_in, y));
+    const size_t need = bitdelta_linear_grouped_workspace(m, n_variants, d_out, d_in);
+    if (workspace_bytes < need)
+        return fail(BD_EWORKSPACE, "linear_grouped needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (m == 0)
+        return BD_OK;
+    BD_NONNULL(workspace);
+    BD_ALIGNED(workspace, 16);
     return device(bd::launch_grouped(x, m, variant_ids, n_variants, w_base, signs, alpha,
                                      alpha_mode == BD_ALPHA_MATRIX, d_out, d_in, y,
                                      static_cast<int32_t *>(workspace), (hipStream_t)stream),
