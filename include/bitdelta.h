@@ -152,6 +152,26 @@ BD_API bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int3
                                   int64_t d_out, int64_t d_in, bd_bf16 *y,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* -------------------------------------------------- linear_grouped_noalloc
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments and results as bitdelta_linear_grouped, with the
+ * bucketing table kept in an array of the library in device memory instead
+ * of a caller workspace.  Each GPU the library runs on holds its own copy
+ * (about 307 KiB, until the process ends); its address is looked up once per
+ * device, on the first call made with that device current.  The call
+ * allocates nothing and needs nothing cleared: every call rewrites the
+ * table.  All calls on one GPU share that table, so calls that overlap in
+ * time on one GPU (on different streams, or from different threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.  m at most BD_GROUPED_NOALLOC_MAX_TOKENS (BD_ESHAPE otherwise);
+ * every other check and error as in bitdelta_linear_grouped. */
+#define BD_GROUPED_NOALLOC_MAX_TOKENS 65536
+BD_API bd_status bitdelta_linear_grouped_noalloc(const bd_bf16 *x, int64_t m, const int32_t *variant_ids,
+                                          int32_t n_variants, const bd_bf16 *w_base,
+                                          const uint8_t *signs, const float *alpha, int alpha_mode,
+                                          int64_t d_out, int64_t d_in, bd_bf16 *y, void *stream);
+
 /* -------------------------------------------------------------- similarity
  * "K-Merge: Online LoRA Adapter Management for the Edge", step 1 of the
  * pool policy: the cosine similarity of two variants' task vectors.  The task

@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
-           "similarity_delta", "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
+           "linear_grouped_noalloc", "similarity_delta", "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
            "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
            "BD_BF16", "BD_F32", "BD_ALPHA_ROW", "BD_ALPHA_MATRIX", "EXPORTS"]
@@ -51,6 +51,7 @@ EXPORTS = {
     "bitdelta_linear": (_INT, [_P, _I64, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
     "bitdelta_linear_grouped_workspace": (_SZ, [_I64, _I32, _I64, _I64]),
     "bitdelta_linear_grouped": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P, _SZ, _P]),
+    "bitdelta_linear_grouped_noalloc": (_INT, [_P, _I64, _P, _I32, _P, _P, _P, _INT, _I64, _I64, _P, _P]),
     "bitdelta_similarity_workspace": (_SZ, [_I32, _I64, _I64]),
     "bitdelta_similarity": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "bitdelta_similarity_delta_workspace": (_SZ, [_I32, _I64, _I64]),
@@ -225,6 +226,38 @@ def linear_grouped(x, variant_ids, w_base, signs, alpha, per_matrix: bool | None
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
     check(lib.bitdelta_linear_grouped(_ptr(x), m, _ptr(variant_ids), V, _ptr(w_base), _ptr(signs), _ptr(alpha),
                                       mode, d_out, d_in, _ptr(y), _ptr(ws), nws, _stream(x.device)))
+    return y
+
+
+def linear_grouped_noalloc(x, variant_ids, w_base, signs, alpha, per_matrix: bool | None = None, out=None):
+    """linear_grouped with the library's own device-resident bucketing table
+    (bitdelta_linear_grouped_noalloc): no workspace; at most
+    BD_GROUPED_NOALLOC_MAX_TOKENS (65536) tokens.  `out` (bf16 [m, d_out])
+    receives y when given, so the call itself allocates nothing."""
+    torch = _torch()
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(variant_ids, torch.int32, "variant_ids")
+    _dev_tensor(w_base, torch.bfloat16, "w_base")
+    _dev_tensor(signs, torch.uint8, "signs")
+    _dev_tensor(alpha, torch.float32, "alpha")
+    d_out, d_in = w_base.shape
+    V = signs.shape[0]
+    if tuple(signs.shape) != (V, d_out, d_in // 8):
+        raise ValueError("signs must be [V, d_out, d_in/8]")
+    if per_matrix is None:
+        per_matrix = alpha.dim() == 1 and d_out != 1
+    if alpha.numel() != (V if per_matrix else V * d_out):
+        raise ValueError("alpha must be [V, d_out] (per row) or [V] (per matrix)")
+    mode = BD_ALPHA_MATRIX if per_matrix else BD_ALPHA_ROW
+    m = x.shape[0]
+    if x.dim() != 2 or variant_ids.numel() != m:
+        raise ValueError("x must be [m, d_in] with one variant id per row")
+    y = torch.empty((m, d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _dev_tensor(y, torch.bfloat16, "out")
+    if tuple(y.shape) != (m, d_out):
+        raise ValueError("out must be [m, d_out]")
+    check(lib.bitdelta_linear_grouped_noalloc(_ptr(x), m, _ptr(variant_ids), V, _ptr(w_base), _ptr(signs),
+                                              _ptr(alpha), mode, d_out, d_in, _ptr(y), _stream(x.device)))
     return y
 
 

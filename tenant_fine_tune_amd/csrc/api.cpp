@@ -291,6 +291,29 @@ bd_status bitdelta_linear_grouped(const bd_bf16 *x, int64_t m, const int32_t *va
                   "bitdelta_linear_grouped");
 }
 
+bd_status bitdelta_linear_grouped_noalloc(const bd_bf16 *x, int64_t m, const int32_t *variant_ids,
+                                          int32_t n_variants, const bd_bf16 *w_base, const uint8_t *signs,
+                                          const float *alpha, int alpha_mode, int64_t d_out, int64_t d_in,
+                                          bd_bf16 *y, void *stream)
+{
+    static_assert(BD_GROUPED_NOALLOC_MAX_TOKENS == bd::kGroupedNoallocMaxTokens, "token limit");
+    BD_TRY(check_grouped(x, m, variant_ids, n_variants, w_base, signs, alpha, alpha_mode, d_out, d_in, y));
+    if (m > BD_GROUPED_NOALLOC_MAX_TOKENS)
+        return fail(BD_ESHAPE, "linear_grouped_noalloc takes at most %d tokens (got %lld)",
+                    BD_GROUPED_NOALLOC_MAX_TOKENS, (long long)m);
+    const size_t need = bitdelta_linear_grouped_workspace(m, n_variants, d_out, d_in);
+    if (need > bd::grouped_scratch_bytes())
+        return fail(BD_ESHAPE, "linear_grouped_noalloc needs %zu table bytes, the library holds %zu", need,
+                    bd::grouped_scratch_bytes());
+    if (m == 0)
+        return BD_OK;
+    int32_t *table = nullptr;
+    BD_TRY(device(bd::grouped_scratch(&table), "bitdelta_linear_grouped_noalloc (table address)"));
+    return device(bd::launch_grouped(x, m, variant_ids, n_variants, w_base, signs, alpha,
+                                     alpha_mode == BD_ALPHA_MATRIX, d_out, d_in, y, table, (hipStream_t)stream),
+                  "bitdelta_linear_grouped_noalloc");
+}
+
 size_t bitdelta_similarity_workspace(int32_t n_variants, int64_t d_out, int64_t d_in)
 {
     (void)d_in;

@@ -51,6 +51,12 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
                           const uint16_t *w_base, const uint8_t *signs, const float *alpha,
                           bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                           int32_t *workspace, hipStream_t s);
+// The same table in a device-resident array of the library (one per GPU, no
+// allocation), for calls of at most kGroupedNoallocMaxTokens tokens:
+// grouped_scratch() gives the current device's copy.
+constexpr int64_t kGroupedNoallocMaxTokens = 65536;
+size_t grouped_scratch_bytes();
+hipError_t grouped_scratch(int32_t **table);
 
 // similarity.hip: Gram matrix and cosines of up to kSimilarityMaxVariants
 // variants' task vectors; `counts` holds similarity_workspace_bytes() bytes

@@ -30,6 +30,7 @@
 // branch.  Workgroups are remapped so that the ones sharing an
 // output-feature tile run on the same XCD (blocks are dealt round-robin over
 // the 8 XCDs), so each W_base tile is fetched into one L2 once.
+#include <mutex>
 #include <type_traits>
 
 #include "bd_device.h"
@@ -839,6 +840,49 @@ int64_t grouped_max_tiles(int64_t m, int32_t n_variants)
 size_t grouped_workspace_bytes(int64_t m, int32_t n_variants)
 {
     return sizeof(int32_t) * (size_t)(4 + m + 3 * grouped_max_tiles(m, n_variants));
+}
+
+// ---------------------------------------------------------------------------
+// The bucketing table of bitdelta_linear_grouped_noalloc: a device-resident
+// array (each GPU holds its own copy until the process ends), sized for the
+// largest call that entry point accepts.  bucket_tokens writes every word the
+// grouped GEMM reads (the header, the permutation, the tile table), so
+// nothing in it needs clearing between calls.
+namespace {
+
+constexpr size_t kScratchWords =
+    (4 + kGroupedNoallocMaxTokens + 3 * ((kGroupedNoallocMaxTokens + BM - 1) / BM + kMaxVariants + 1) + 63) / 64 * 64;
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+size_t grouped_scratch_bytes() { return sizeof(int32_t) * kScratchWords; }
+
+hipError_t grouped_scratch(int32_t **table)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        // once per device, with that device current: the address of this
+        // GPU's copy of the array (the array's name in host code is only a
+        // host-side stand-in)
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch[dev] = static_cast<int32_t *>(p);
+    }
+    *table = g_scratch[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int32_t n_variants,

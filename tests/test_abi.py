@@ -159,6 +159,22 @@ def test_grouped_validation(bd):
     assert g(None, 0, None, 3, None, None, None, 0, 64, 64, None, None, W(0, 3, 64, 64), None) == bd.BD_OK
 
 
+def test_grouped_noalloc_validation(bd):
+    """bitdelta_linear_grouped_noalloc: the grouped checks, plus its token limit
+    (the size of the library's table); every call below fails before any
+    device call, and m = 0 is a no-op."""
+    g = bd.lib.bitdelta_linear_grouped_noalloc
+    assert g(FAKE, 100, FAKE, 0, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, FAKE, 4097, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, FAKE, 3, FAKE, FAKE, FAKE, 0, 64, 60, FAKE, None) == bd.BD_ESHAPE
+    assert g(FAKE, 65537, FAKE, 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, None) == bd.BD_ESHAPE
+    assert "65536" in err(bd)
+    assert g(FAKE, 100, None, 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE, None) == bd.BD_EINVAL
+    assert g(FAKE, 100, FAKE, 3, FAKE, FAKE, FAKE, 0, 64, 64, FAKE_ODD, None) == bd.BD_EALIGN
+    assert g(FAKE, 100, FAKE, 3, FAKE, FAKE, FAKE, 2, 64, 64, FAKE, None) == bd.BD_EINVAL
+    assert g(None, 0, None, 3, None, None, None, 0, 64, 64, None, None) == bd.BD_OK
+
+
 def test_python_binding_rejects_host_tensors(bd):
     import torch
 
