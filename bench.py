@@ -2,36 +2,45 @@
 """Benchmark of the BitDelta hot path on one MI355X; prints ONE JSON line.
 
 Workload of the headline number: the decode layer of the post's 70B-class
-model, one 4096 x 4096 bf16 weight with packed 1-bit deltas.  One step is a
-full pass of the single-layer hot path over one batch:
-  compress (per-row alpha) -> compress (per-matrix alpha) -> reconstruct ->
-  fused linear at m = 1, 4, 16 tokens with per-row alpha -> the same three
-  with the per-matrix alpha,
+model, one 4096 x 4096 bf16 weight with packed 1-bit deltas, through the fused
+linear (W_eff never materialised).  One step is one pass of the fused decode
+linear over one batch at every decode size:
+  m = 1, 4, 16 tokens with per-row alpha, then the same three with the
+  per-matrix alpha,
 each launch reading its own weight set out of 16 rotating sets (571 MB of
 weights, more than the 256 MB MALL, so every launch streams from HBM).
-`value` is the step's algorithmic HBM bytes (inputs read + outputs written,
-per kernel) divided by its time: GB/s.  The steps are captured in HIP graphs
-(one per weight set) so the microsecond-scale decode launches are not bound
-by host launch overhead; the timed region replays exactly --steps steps.
+`value` is the step's algorithmic HBM bytes (W_base + packed signs + alpha +
+x + y per launch) divided by its time: GB/s.  The steps are captured in HIP
+graphs (one per weight set) so the microsecond-scale decode launches are not
+bound by host launch overhead; the timed region replays exactly --steps steps.
 
 The same line carries:
-  kernels     per-kernel average launch time (HIP events around graph
-              replays of that kernel alone, on its own stream) and GB/s;
-  roofline    for the dominant kernel of the step (largest share of step
-              time), against 8 TB/s;
+  kernels     per-entry average launch time (HIP events around graph
+              replays of that entry alone, on its own stream) and GB/s: the
+              six fused decode launches, and the offline passes (compress
+              with per-row and per-matrix alpha, reconstruct) beside them;
+  roofline    for the dominant kernel of the step (largest launch time),
+              against 8 TB/s, with its counter-measured HBM traffic;
+  rooflines   the same for every decode entry, compress and reconstruct, each
+              prefill shape (TFLOP/s against 2.5 PFLOP/s) and the grouped GEMM;
   prefill     the fused MFMA GEMM at m = 2048 tokens on the q/o, k/v,
-              gate/up and down shapes (TFLOP/s and fraction of the 2.5
-              PFLOP/s bf16 dense peak);
+              gate/up and down shapes, with the oracle on 512 output rows
+              (extrapolated) beside it;
   grouped     14 variants over one shared 8192 x 8192 base, 4096 tokens in a
-              Zipf(1.1) split (TFLOP/s);
-  similarity  K-Merge's cosine similarity of the 14 variants' task vectors
-              on the grouped layer's packed signs (GB/s);
+              Zipf(1.1) split (TFLOP/s), with the oracle beside it;
+  similarity  K-Merge's cosine similarity of the 14 variants: over the packed
+              code and over the full fp32 task vectors W_ft - W_base (GB/s);
+  monosoup    the MonoSoup merge of two 8192 x 8192 checkpoints;
+  stack       the 70B-shaped stack resident on the GPU (80 layers x 7
+              linears, 14 delta sets, 257 GB): compress of one variant,
+              512-token prefill and 1-token decode through all 560 linears,
+              cold-start upload of one variant's deltas (--no-stack skips it);
   context     reference points from the vendor libraries through torch: a
               34 MiB copy, plain bf16 GEMMs on the prefill shapes, and the
               unfused path (reconstruct to HBM, then a plain GEMM) beside the
               fused call, with the overhead of each over the plain GEMM;
-  cpu_baseline  the oracle timed on the host cores on the same step, at the
-              same shape, on host-generated inputs.
+  cpu_baseline  the oracle timed on the host cores on the same decode step,
+              at the same shape, on host-generated inputs.
 """
 from __future__ import annotations
 
@@ -57,8 +66,10 @@ SETS = 16
 PREFILL_SHAPES = [("q/o", 8192, 8192), ("k/v", 1024, 8192), ("gate/up", 28672, 8192), ("down", 8192, 28672)]
 PREFILL_M = 2048
 
-# GPU kernels behind each entry of the decode step: source file under csrc/
-# and the kernel names (regular expressions on rocprofv3's demangled names)
+# GPU kernels behind each measured decode-layer entry: source file under
+# csrc/ and the kernel names (regular expressions on rocprofv3's demangled
+# names).  The step is the fused linear entries; compress and reconstruct are
+# measured beside it.
 STEP_KERNELS = {
     "compress_row": ("compress.hip", [r"compress_rows<true, false>"]),
     "compress_matrix": ("compress.hip", [r"compress_rows<true, true>", r"alpha_matrix_finish"]),
@@ -70,6 +81,8 @@ STEP_KERNELS = {
     "linear_m16_row": ("gemv.hip", [r"gemv_mfma<false, true>"]),
     "linear_m16_matrix": ("gemv.hip", [r"gemv_mfma<true, true>"]),
 }
+STEP = [f"linear_m{m}_{mode}" for mode in ("row", "matrix") for m in DECODE_M]
+OFFLINE = ["compress_row", "compress_matrix", "reconstruct"]
 
 
 def parse():
@@ -93,6 +106,7 @@ def parse():
                         "14 delta sets, 257 GB resident) and time a compress pass over one variant's full weight set, "
                         "a 512-token prefill pass and a 1-token decode pass through every linear")
     p.add_argument("--stack-layers", type=int, default=80)
+    p.add_argument("--no-stack", action="store_true", help="skip the 70B-shaped stack section of the default line")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (torch copy_), so counter runs can "
                         "calibrate FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
@@ -132,6 +146,10 @@ class DecodeStep:
                      alpha_m=torch.empty((1,), dtype=torch.float32, device=dev),
                      ws=torch.empty((bd.lib.bitdelta_compress_workspace(R, C, 1),), dtype=torch.uint8, device=dev))
             self.sets.append(s)
+        # every set's code (both alpha modes) exists before the linear launches read it
+        for i in range(SETS):
+            self.launch("compress_row", i, torch.cuda.current_stream())
+            self.launch("compress_matrix", i, torch.cuda.current_stream())
         self.weff = [torch.empty((R, C), dtype=torch.bfloat16, device=dev) for _ in range(2)]
         self.x = {m: synth.device_activations(m, C, seed=0, index=m) for m in DECODE_M}
         self.y = {m: [torch.empty((m, R), dtype=torch.bfloat16, device=dev) for _ in range(2)] for m in DECODE_M}
@@ -181,17 +199,17 @@ class DecodeStep:
         bd.check(rc)
 
     def step(self, i, stream):
-        """Step i: its j-th launch uses weight set (len(bytes) * i + j) mod SETS,
+        """Step i: its j-th launch uses weight set (len(STEP) * i + j) mod SETS,
         so consecutive launches over the replayed steps walk the 16 sets in
         order and no launch finds its weights still cached (a set comes back
         after 15 other launches, more than the 256 MB MALL holds)."""
-        n = len(self.bytes)
-        for j, name in enumerate(self.bytes):
+        n = len(STEP)
+        for j, name in enumerate(STEP):
             self.launch(name, (n * i + j) % SETS, stream)
 
     @property
     def step_bytes(self):
-        return sum(self.bytes.values())
+        return sum(self.bytes[k] for k in STEP)
 
 
 def capture(torch, fn):
@@ -289,11 +307,18 @@ def run_prefill(torch, bd, synth, reps=10):
             torch.cuda.synchronize()
             rep_us.append(e0.elapsed_time(e1) / reps * 1e3)
         us = sum(rep_us) / 5
-        flop = 2.0 * PREFILL_M * N * K
+        flop = 2 * PREFILL_M * N * K
         tf = flop / us / 1e6
+        plan = bd.lib.bitdelta_linear_workspace(PREFILL_M, N, K)
         out[label] = {"d_out": N, "d_in": K, "m": PREFILL_M, "us": round(us, 1),
                       "us_median5": round(statistics.median(rep_us), 1), "us_min5": round(min(rep_us), 1),
-                      "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+                      "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                      "roofline": {"kernel": f"prefill_{label}",
+                                   "gpu_kernel": "gemm_tiles_w8" + (" + splitk_reduce" if plan else ""),
+                                   "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                   "traffic": traffic_record(f"prefill_{label}"), "flop_per_launch": flop,
+                                   "avg_launch_us": round(us, 1)}}
         log(f"prefill {label} [{N},{K}] m={PREFILL_M}: {us:.1f} us, {tf:.1f} TFLOP/s")
         del sets, x, y
         torch.cuda.empty_cache()
@@ -315,12 +340,14 @@ def run_grouped(torch, bd, synth, reps=10):
     bv = synth.variant_scales(V, seed=0)
     signs = torch.empty((V, N, K // 8), dtype=torch.uint8, device=dev)
     alpha = torch.empty((V, N), dtype=torch.float32, device=dev)
+    w_fts = torch.empty((V, N, K), dtype=torch.float32, device=dev)  # the variants' fp32 weights (3.76 GB)
     for v in range(V):
-        w_ft = w_base.float().add_(synth.device_laplace((N, K), float(bv[v]), 2, synth.tag(synth.TAG_VARIANT + v), dev))
-        sg, a = bd.compress(w_base, w_ft)
+        w_fts[v].copy_(w_base.float().add_(synth.device_laplace((N, K), float(bv[v]), 2,
+                                                                 synth.tag(synth.TAG_VARIANT + v), dev)))
+        sg, a = bd.compress(w_base, w_fts[v])
         signs[v].copy_(sg)
         alpha[v].copy_(a)
-        del w_ft, sg, a
+        del sg, a
     counts = synth.zipf_counts(M, V, 1.1)
     ids = torch.from_numpy(synth.variant_ids(counts, seed=0)).to(dev)
     x = synth.device_activations(M, K, seed=2)
@@ -356,14 +383,61 @@ def run_grouped(torch, bd, synth, reps=10):
         us = min(us, timed())
         ids = ids_sorted
         us_sorted = min(us_sorted, timed())
-    flop = 2.0 * M * N * K
+    flop = 2 * M * N * K
     tf = flop / us / 1e6
     log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s "
         f"(ids pre-sorted: {us_sorted:.1f} us)")
     sim = run_similarity(torch, bd, signs, alpha)
+    sim["full_task_vectors"] = run_similarity_delta(torch, bd, w_base, w_fts)
+    del w_fts
+    torch.cuda.empty_cache()
+    roof = {"kernel": "grouped", "gpu_kernel": "bucket_tokens + gemm_tiles_w8 (gathered)", "bound": "mfma",
+            "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic_record("grouped"), "flop_per_launch": flop,
+            "avg_launch_us": round(us, 1)}
     return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
             "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-            "us_ids_presorted": round(us_sorted, 1)}, sim
+            "us_ids_presorted": round(us_sorted, 1), "roofline": roof}, sim
+
+
+def run_similarity_delta(torch, bd, w_base, w_fts, reps=5):
+    """K-Merge similarity over the full task vectors (W_ft - W_base) of the
+    grouped layer's 14 variants: reads the fp32 W_ft of every variant and the
+    bf16 base once (algorithmic bytes), writes the two V x V fp64 outputs."""
+    V, N, K = w_fts.shape
+    dev = w_fts.device
+    gram = torch.empty((V, V), dtype=torch.float64, device=dev)
+    cos = torch.empty((V, V), dtype=torch.float64, device=dev)
+    nws = bd.lib.bitdelta_similarity_delta_workspace(V, N, K)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bd.check(bd.lib.bitdelta_similarity_delta(P(w_base.data_ptr()), P(w_fts.data_ptr()), bd.BD_F32, V, N, K,
+                                                  P(gram.data_ptr()), P(cos.data_ptr()), P(ws.data_ptr()), nws,
+                                                  P(stream.cuda_stream)))
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    rep_us = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_us.append(e0.elapsed_time(e1) / reps * 1e3)
+    us = sum(rep_us) / 3
+    nbytes = V * N * K * 4 + N * K * 2 + 2 * V * V * 8
+    gbs = nbytes / us / 1e3
+    log(f"similarity over full task vectors, {V} variants [{N},{K}] fp32: {us:.1f} us, {gbs:.1f} GB/s "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
+    return {"variants": V, "d_out": N, "d_in": K, "w_ft": "fp32", "us": round(us, 1),
+            "us_min3": round(min(rep_us), 1), "bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def run_similarity(torch, bd, signs, alpha, reps=20):
@@ -700,29 +774,23 @@ def run_delta_upload(torch, bd, st, reps=3):
 
 
 def run_cpu_baseline(target_s):
-    """The oracle, untuned, on the same decode step on host-generated inputs of
-    the same shape; repeated until about target_s seconds have elapsed."""
-    import numpy as np
-
+    """The oracle, untuned, on the same decode step (the fused linear at m = 1,
+    4, 16 with per-row and per-matrix alpha) on host-generated inputs of the
+    same shape; repeated until about target_s seconds have elapsed."""
     import oracle
     import synth
 
     w_base, w_ft = synth.layer(R, C, seed=0)
+    signs, alpha = oracle.compress(w_base, w_ft)
+    _, alpha_m = oracle.compress(w_base, w_ft, per_matrix=True)
     xs = {m: synth.activations(m, C, seed=0, index=m) for m in DECODE_M}
-    bytes_step = 0
-    w = R * C
-    bytes_step += 2 * (w * 6 + w // 8) + 4 * R + 4          # two compresses
-    bytes_step += w * 4 + w // 8 + 4 * R                    # reconstruct
-    for m in DECODE_M:
-        bytes_step += 2 * (w * 2 + w // 8 + 2 * m * C + 2 * m * R) + 4 * R + 4
+    bytes_step = sum(DecodeStep.algorithmic_bytes()[k] for k in STEP)
     n = 0
     t0 = time.perf_counter()
     while True:
-        signs, alpha = oracle.compress(w_base, w_ft)
-        _, alpha_m = oracle.compress(w_base, w_ft, per_matrix=True)
-        oracle.reconstruct(w_base, signs, alpha)
         for m in DECODE_M:
             oracle.linear(xs[m], w_base, signs, alpha)
+        for m in DECODE_M:
             oracle.linear(xs[m], w_base, signs, alpha_m, per_matrix=True)
         n += 1
         el = time.perf_counter() - t0
@@ -730,12 +798,102 @@ def run_cpu_baseline(target_s):
             break
     gbs = bytes_step * n / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(oracle.num_threads()), "kind": "oracle",
-            "sample": f"the full decode step (2 compresses, reconstruct, linear m=1,4,16 x 2 alpha modes) on one "
-                      f"4096x4096 layer, host-generated inputs, repeated {n} times in {el:.1f} s",
+            "sample": f"the full decode step (fused linear m=1,4,16 x 2 alpha modes) on one 4096x4096 layer, "
+                      f"host-generated inputs, repeated {n} times in {el:.1f} s",
             "seconds_per_step": round(el / n, 4), "host_cpus": os.cpu_count()}
 
 
+CPU_ROWS = 512  # output rows of each large matrix the oracle computes; its time is scaled to all rows
+
+
+def _host_code(rows, d_in, seed, tg, n_variants=None):
+    """Host inputs for a timing sample of the oracle: bf16 W_base rows, random
+    packed signs and alpha near 1e-3 (the oracle's time does not depend on the
+    values)."""
+    import numpy as np
+
+    import synth
+
+    wb = synth.to_bf16_bits(synth.normal_f32((rows, d_in), 0.02, seed, tg))
+    shape = (rows,) if n_variants is None else (n_variants, rows)
+    sg = synth.u64(shape + (d_in // 8,), seed, tg + 1).astype(np.uint8)
+    al = (np.abs(synth.normal_f32(shape, 1e-3, seed, tg + 2)) + np.float32(1e-5)).astype(np.float32)
+    return wb, sg, al
+
+
+def run_cpu_prefill():
+    """The oracle on the prefill layer (m = 2048 on the q/o, k/v, gate/up, down
+    shapes): the first 512 output rows of each, timed once, scaled by d_out /
+    512 (extrapolated)."""
+    import oracle
+    import synth
+
+    out, tot_flop, tot_s = {}, 0.0, 0.0
+    for i, (label, N, K) in enumerate(PREFILL_SHAPES):
+        wb, sg, al = _host_code(CPU_ROWS, K, 7, 8100 + 10 * i)
+        x = synth.activations(PREFILL_M, K, seed=7, index=i)
+        t0 = time.perf_counter()
+        oracle.linear(x, wb, sg, al)
+        el = (time.perf_counter() - t0) * N / CPU_ROWS
+        flop = 2.0 * PREFILL_M * N * K
+        out[label] = {"seconds_extrapolated": round(el, 2), "TFLOP/s": round(flop / el / 1e12, 5)}
+        tot_flop, tot_s = tot_flop + flop, tot_s + el
+        log(f"cpu oracle prefill {label}: {el:.1f} s (extrapolated from {CPU_ROWS} rows)")
+    return {"kind": "oracle", "cores": int(oracle.num_threads()), "shapes": out,
+            "layer_TFLOP/s": round(tot_flop / tot_s / 1e12, 5),
+            "sample": f"the first {CPU_ROWS} output rows of each shape at m={PREFILL_M}, host-generated inputs, "
+                      f"timed once and scaled by d_out/{CPU_ROWS} (extrapolated)"}
+
+
+def run_cpu_grouped(counts):
+    """The oracle on the grouped layer (14 variants, 4096 tokens, Zipf split):
+    the first 512 output rows, timed once, scaled by 8192 / 512."""
+    import oracle
+    import synth
+
+    N = K = 8192
+    V, M = len(counts), sum(counts)
+    wb, sg, al = _host_code(CPU_ROWS, K, 8, 8200, n_variants=V)
+    ids = synth.variant_ids(counts, seed=0)
+    x = synth.activations(M, K, seed=8)
+    t0 = time.perf_counter()
+    oracle.linear_grouped(x, ids, wb, sg, al)
+    el = (time.perf_counter() - t0) * N / CPU_ROWS
+    flop = 2.0 * M * N * K
+    log(f"cpu oracle grouped: {el:.1f} s (extrapolated from {CPU_ROWS} rows)")
+    return {"kind": "oracle", "cores": int(oracle.num_threads()), "seconds_extrapolated": round(el, 2),
+            "TFLOP/s": round(flop / el / 1e12, 5),
+            "sample": f"the first {CPU_ROWS} output rows of the shared 8192x8192 layer, 14 variants, {M} tokens, "
+                      f"host-generated inputs, timed once and scaled by {N}/{CPU_ROWS} (extrapolated)"}
+
+
 # ----------------------------------------------------------------------- main
+
+
+def hbm_roofline(entry, k):
+    """Roofline record of a decode-layer entry: algorithmic bytes per launch
+    over its average launch time, against 8 TB/s, with the counter-measured
+    HBM bytes per launch (null when the counters predate its source)."""
+    return {"kernel": entry, "gpu_kernel": STEP_KERNELS[entry][1][0], "bound": "hbm", "achieved": k["GB/s"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k["GB/s"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(entry), "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": k["us"]}
+
+
+def traffic_record(entry):
+    """HBM bytes per launch of a prefill shape or the grouped GEMM from the
+    committed counter runs (profiles/traffic.json), if taken on the current
+    gemm.hip; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    e = rec.get("gemm", {}).get(entry)
+    if not e or e.get("source_sha") != source_sha("gemm.hip"):
+        return None
+    return e.get("bytes_per_launch")
 
 
 def traffic_for(entry):
@@ -1008,26 +1166,38 @@ def main():
     ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup, args.kernel_reps)
     ms_per_step = dev_s / args.steps * 1e3
     value = ds.step_bytes * args.steps / dev_s / 1e9
-    log(f"decode step: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s (wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
+    log(f"decode step (fused linear m=1,4,16 x 2 alpha modes): {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s "
+        f"(wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
     for k, v in kernels.items():
         log(f"  {k:22s} {v['us']:8.2f} us  {v['GB/s']:8.1f} GB/s  {100 * v['frac_hbm']:.1f}% of HBM")
-    # dominant kernel: the single-kernel entry with the largest share of the step's time
-    dom = max((k for k in kernels if len(STEP_KERNELS[k][1]) == 1), key=lambda k: kernels[k]["us"])
-    kd = kernels[dom]
-    roofline = {"kernel": dom, "gpu_kernel": STEP_KERNELS[dom][1][0], "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom),
-                "algorithmic_bytes_per_launch": kd["bytes"], "avg_launch_us": kd["us"]}
+    rooflines = {k: hbm_roofline(k, kernels[k]) for k in STEP + OFFLINE}
+    # dominant kernel: the step entry with the largest launch time
+    dom = max(STEP, key=lambda k: kernels[k]["us"])
+    roofline = rooflines[dom]
     step_bytes = ds.step_bytes
     del ds
     torch.cuda.empty_cache()
 
     prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
+    if prefill is not None:
+        for label, e in prefill["shapes"].items():
+            rooflines[f"prefill_{label}"] = e["roofline"]
     grouped, similarity = (None, None) if args.no_grouped else run_grouped(torch, bd, synth)
+    if grouped is not None:
+        rooflines["grouped"] = grouped["roofline"]
     monosoup = None if args.no_monosoup else run_monosoup(torch, bd, synth)
     context = None if args.no_context else run_context(torch)
     if context is not None and prefill is not None:
         context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill)
+    torch.cuda.empty_cache()
+    stack = None if args.no_stack else run_stack(torch, bd, synth, args.stack_layers)
+    torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        if prefill is not None:
+            prefill["cpu_oracle"] = run_cpu_prefill()
+        if grouped is not None:
+            grouped["cpu_oracle"] = run_cpu_grouped(grouped["group_sizes"])
 
     line = {
         "metric": METRIC,
@@ -1042,16 +1212,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode layer 4096x4096 bf16 + packed 1-bit deltas: compress (row and matrix alpha), "
-                               "reconstruct, fused linear m=1,4,16 (row and matrix alpha); 16 rotating weight sets",
+        "config": {"workload": "decode layer 4096x4096 bf16 + packed 1-bit deltas through the fused linear: "
+                               "m=1,4,16 tokens with row and matrix alpha; 16 rotating weight sets",
                    "d_out": R, "d_in": C, "m": list(DECODE_M), "weight_sets": SETS, "parallelism": "single GPU",
                    "step_bytes": step_bytes},
         "roofline": roofline,
+        "rooflines": rooflines,
         "kernels": kernels,
         "prefill": prefill,
         "grouped": grouped,
         "similarity": similarity,
         "monosoup": monosoup,
+        "stack": stack,
         "context": context,
         "cpu_baseline": cpu,
     }
