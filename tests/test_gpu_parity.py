@@ -469,3 +469,82 @@ def test_stack_two_layers(bd):
             y64, sc = oracle.linear(xs_h[name], wb_rows, s9, a9)
             check_linear(host_bits(ys[name])[:, rows_of[0, name]], y64, sc, f"stack variant 9 {name} m={m}")
     assert st.resident_bytes() == st.params() * 2 + 14 * (st.params() // 8 + 4 * 2 * sum(o for _, o, _ in st.shapes))
+
+
+def test_stack_full_80_layers(bd):
+    """The whole 70B-shaped stack resident on the GPU (80 layers x 7 linears,
+    14 packed delta sets, 257 GB, as the post's memory arithmetic has it):
+    variant 0 compressed matrix by matrix from streamed fine-tuned weights,
+    the other 13 random packed codes.  Compress is bit-exact on sampled rows of
+    layers 0 and 79; the fused linear at m = 512 (prefill) and m = 1 (decode)
+    matches the oracle on sampled output features of every matrix of layers 0
+    and 79, for variant 0 and for variant 9; a full pass through all 560
+    linears runs and gives finite outputs."""
+    from tenant_fine_tune_amd.stack import LinearStack
+
+    torch.cuda.empty_cache()
+    free, total = torch.cuda.mem_get_info()
+    if free < 270e9:
+        pytest.skip(f"needs about 260 GB of free device memory ({free / 1e9:.0f} GB free of {total / 1e9:.0f})")
+    print("stack 80 layers: allocating", flush=True)
+    st = LinearStack(n_layers=80, n_variants=14)
+    st.reserve(512)
+    dev = st.device
+    names = [s[0] for s in st.shapes]
+    bv = synth.variant_scales(14, seed=5)
+    checked = (0, 79)
+    rows_of, orc_rows = {}, {}
+    for l, name, d_out, d_in in st.matrices():
+        idx = 2000 + 10 * l + names.index(name)
+        st.base[l, name].copy_(synth.device_normal((d_out, d_in), 0.02, 5, synth.tag(synth.TAG_WBASE, idx), dev,
+                                                   torch.bfloat16))
+        w_ft = st.base[l, name].float().add_(synth.device_laplace((d_out, d_in), float(bv[0]), 5,
+                                                                  synth.tag(synth.TAG_DELTA, idx), dev))
+        st.compress_into(0, l, name, w_ft)
+        if l in checked:
+            rows = np.unique(np.concatenate([[0, d_out - 1], synth.u64(6, 5, 9400 + idx) % np.uint64(d_out)]))
+            rows_of[l, name] = rows.astype(np.int64)
+            r_t = torch.from_numpy(rows_of[l, name]).to(dev)
+            wb_rows = host_bits(st.base[l, name].index_select(0, r_t))
+            so, ao = oracle.compress(wb_rows, host(w_ft.index_select(0, r_t)))
+            assert np.array_equal(host(st.signs[0, l, name].index_select(0, r_t)), so), (l, name)
+            assert np.array_equal(_bits32(host(st.alpha[0, l, name].index_select(0, r_t))), _bits32(ao)), (l, name)
+            orc_rows[l, name] = (wb_rows, so, ao)
+        del w_ft
+        g = torch.Generator(device=dev)
+        g.manual_seed(idx)
+        for v in range(1, 14):
+            st.signs[v, l, name].copy_(torch.randint(0, 256, st.signs[v, l, name].shape, generator=g, device=dev,
+                                                     dtype=torch.int32).to(torch.uint8))
+            st.alpha[v, l, name].copy_(torch.rand(st.alpha[v, l, name].shape, generator=g, device=dev)
+                                       .mul_(float(bv[v])).add_(float(bv[v]) * 0.5))
+        if name == names[-1] and l % 20 == 19:
+            torch.cuda.synchronize()
+            print(f"stack 80 layers: layer {l + 1} filled and compressed", flush=True)
+    widths = {name: d_in for name, _, d_in in st.shapes}
+    outs = {name: d_out for name, d_out, _ in st.shapes}
+    for m in (512, 1):
+        xs_h = {name: synth.activations(m, widths[name], seed=5, index=m + i) for i, name in enumerate(widths)}
+        xs = {name: bf16_dev(a) for name, a in xs_h.items()}
+        ys = {name: torch.empty((m, outs[name]), dtype=torch.bfloat16, device=dev) for name in outs}
+        st.forward(0, xs, ys)
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(ys[n].float()).all() for n in outs)
+        for l in checked:
+            for v in (0, 9):
+                for name in outs:
+                    st.linear(v, l, name, xs[name], ys[name])
+                    wb_rows, so, ao = orc_rows[l, name]
+                    if v != 0:
+                        r_t = torch.from_numpy(rows_of[l, name]).to(dev)
+                        so = host(st.signs[v, l, name].index_select(0, r_t))
+                        ao = host(st.alpha[v, l, name].index_select(0, r_t))
+                    y64, sc = oracle.linear(xs_h[name], wb_rows, so, ao)
+                    check_linear(host_bits(ys[name])[:, rows_of[l, name]], y64, sc,
+                                 f"stack 80 layers: layer {l} {name} variant {v} m={m}")
+        print(f"stack 80 layers: m={m} checked on layers {checked}, variants 0 and 9", flush=True)
+    # 136.9 GB of bf16 base + 14 x (8,556,380,160 sign bytes + 26,869,760 alpha bytes), the storage the pins
+    # derive from the post's arithmetic
+    assert st.resident_bytes() == 136_902_082_560 + 14 * (8_556_380_160 + 26_869_760) == 257_067_581_440
+    del st, xs, ys
+    torch.cuda.empty_cache()
