@@ -54,8 +54,9 @@ bd_status check_matrix(int64_t d_out, int64_t d_in)
 // offsets: each operand (per variant for signs) must stay below 2 GiB.
 bool operands_fit(int64_t m, int64_t d_out, int64_t d_in)
 {
-    const int64_t lim = (int64_t)1 << 31;
-    return m * d_in * 2 < lim && d_out * d_in * 2 < lim && m * d_out * 2 < lim;
+    // a * b * 2 < 2^31 for positive a, b, without forming the product
+    const auto fits = [](int64_t a, int64_t b) { return a <= 0 || b <= 0 || a <= ((int64_t(1) << 30) - 1) / b; };
+    return fits(m, d_in) && fits(d_out, d_in) && fits(m, d_out);
 }
 
 bd_status check_mode(int mode)
@@ -165,7 +166,8 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
 
 size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in)
 {
-    if (m <= bd::kGemvMaxM || d_out <= 0 || d_in <= 0 || d_in % 8 != 0)
+    // shapes the prefill path rejects need no workspace
+    if (m <= bd::kGemvMaxM || d_out <= 0 || d_in <= 0 || d_in % 8 != 0 || !operands_fit(m, d_out, d_in))
         return 0;
     return bd::gemm_workspace_bytes(m, d_out, d_in);
 }
@@ -206,10 +208,10 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, co
         return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
                       "bitdelta_linear (decode)");
     }
-    const int64_t tiles = ((m + bd::kGemmBM - 1) / bd::kGemmBM) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
     if (!operands_fit(m, d_out, d_in))
         return fail(BD_ESHAPE, "prefill operands must each be below 2 GiB (m=%lld, d_out=%lld, d_in=%lld)",
                     (long long)m, (long long)d_out, (long long)d_in);
+    const int64_t tiles = ((m + bd::kGemmBM - 1) / bd::kGemmBM) * ((d_out + bd::kGemmBN - 1) / bd::kGemmBN);
     if (tiles > kMaxGrid)
         return fail(BD_ESHAPE, "linear m=%lld d_out=%lld exceeds the prefill grid", (long long)m, (long long)d_out);
     if (need >= ((size_t)1 << 31))
@@ -223,7 +225,7 @@ size_t bitdelta_linear_grouped_workspace(int64_t m, int32_t n_variants, int64_t 
 {
     (void)d_out;
     (void)d_in;
-    if (m < 0 || n_variants <= 0)
+    if (m < 0 || m > std::numeric_limits<int32_t>::max() / 2 || n_variants <= 0 || n_variants > 4096)
         return 0;
     return bd::grouped_workspace_bytes(m, n_variants);
 }
