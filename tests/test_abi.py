@@ -127,7 +127,8 @@ def test_linear_split_k_workspace(bd):
     assert W(2048, 8192, 28672) == 0
     assert W(2048, 28672, 8192) == 2 * 128 * tile  # 896 tiles: last 128 in 2 K ranges
     assert W(4000, 4128, 4096) == 2 * 16 * tile    # 272 tiles: K/2 = 2048 is the floor
-    assert W(256, 256 * 264, 16384) == 8 * 8 * tile
+    assert W(256, 256 * 264, 15872) == 4 * 8 * tile   # 264 tiles: last 8 in 4 K ranges (K/8 < 2048)
+    assert W(256, 256 * 264, 16384) == 0           # W_base of 2 GiB or more: rejected, no workspace
     assert W(4096, 6400, 8192) == 0                # last wave of 144 tiles: over half the CUs
     assert W(4096, 4352, 2048) == 0                # K/2 = 1024: too short to repay the sum
     assert W(512, 28672, 8192) == 0                # 224 tiles: one wave
