@@ -78,8 +78,8 @@ STEP_KERNELS = {
     "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true, false>"]),
     "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 1, \d+, false, true, true>"]),
     "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 1, \d+, true, true, true>"]),
-    "linear_m16_row": ("gemv.hip", [r"gemv_mfma<false, true>"]),
-    "linear_m16_matrix": ("gemv.hip", [r"gemv_mfma<true, true>"]),
+    "linear_m16_row": ("gemv.hip", [r"gemv_rows<8, false>"]),
+    "linear_m16_matrix": ("gemv.hip", [r"gemv_rows<8, true>"]),
 }
 STEP = [f"linear_m{m}_{mode}" for mode in ("row", "matrix") for m in DECODE_M]
 OFFLINE = ["compress_row", "compress_matrix", "reconstruct"]

@@ -118,7 +118,8 @@ DECODE_CASES = [((256, 512), m) for m in (1, 2, 3, 4, 5, 8, 9, 16)] + \
                [((4096, 4096), m) for m in (1, 4, 16)] + \
                [((300, 200), 3), ((7, 8), 16), ((1000, 1032), 7), ((33, 24), 1)] + \
                [((1000, 1024), 9), ((512, 8192), 16), ((1000, 28672), 16), ((300, 28672), 1),  # the kernels' steady loops, D = 1
-                ((300, 28672), 4), ((40, 8704), 2), ((1000, 6144), 12)]
+                ((300, 28672), 4), ((40, 8704), 2), ((1000, 6144), 12)] + \
+               [((1000, 4096), 13), ((33, 8192), 5), ((24, 4096), 16), ((7, 12288), 8)]  # whole-row MFMA kernel
 
 
 @pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
