@@ -107,6 +107,14 @@ def parse():
                         "a 512-token prefill pass and a 1-token decode pass through every linear")
     p.add_argument("--stack-layers", type=int, default=80)
     p.add_argument("--no-stack", action="store_true", help="skip the 70B-shaped stack section of the default line")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode step (counter runs of other sections; the line then has no value)")
+    p.add_argument("--prefill-shapes", default="", help="comma-separated prefill shapes to run (default: all)")
+    p.add_argument("--grouped-rows", type=int, default=8192,
+                   help="d_out of the grouped layer (8192; 28672 puts the shared base above the MALL)")
+    p.add_argument("--summarize-gemm-counters", nargs=4, metavar=("ENTRY", "FETCH_CSV", "WRITE_CSV", "COPY_MB"),
+                   help="record the HBM bytes per call of one prefill shape (fused and unfused) or of the grouped "
+                        "GEMM from a counter pass of that section alone into profiles/traffic.json (no GPU)")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (torch copy_), so counter runs can "
                         "calibrate FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
@@ -271,10 +279,16 @@ def run_decode(torch, bd, synth, steps, warmup, kernel_reps):
 # -------------------------------------------------------------------- prefill
 
 
-def run_prefill(torch, bd, synth, reps=10):
+def prefill_shapes(only):
+    """The prefill shapes to run: all, or the comma-separated labels in `only`."""
+    want = [w for w in only.split(",") if w]
+    return [s for s in PREFILL_SHAPES if not want or s[0] in want]
+
+
+def run_prefill(torch, bd, synth, reps=10, only=""):
     out = {}
     dev = torch.device("cuda")
-    for label, N, K in PREFILL_SHAPES:
+    for label, N, K in prefill_shapes(only):
         sets = []
         for i in range(2):
             w_base, w_ft = synth.device_layer(N, K, seed=1, index=10 * i + len(out))
@@ -332,9 +346,9 @@ def run_prefill(torch, bd, synth, reps=10):
 # -------------------------------------------------------------------- grouped
 
 
-def run_grouped(torch, bd, synth, reps=10):
+def run_grouped(torch, bd, synth, reps=10, rows=8192):
     dev = torch.device("cuda")
-    N = K = 8192
+    N, K = rows, 8192
     V, M = 14, 4096
     w_base = synth.device_normal((N, K), 0.02, 2, synth.tag(synth.TAG_WBASE), dev, torch.bfloat16)
     bv = synth.variant_scales(V, seed=0)
@@ -385,7 +399,7 @@ def run_grouped(torch, bd, synth, reps=10):
         us_sorted = min(us_sorted, timed())
     flop = 2 * M * N * K
     tf = flop / us / 1e6
-    log(f"grouped 14 variants [8192,8192] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s "
+    log(f"grouped 14 variants [{N},{K}] m=4096: {us:.1f} us, {tf:.1f} TFLOP/s "
         f"(ids pre-sorted: {us_sorted:.1f} us)")
     sim = run_similarity(torch, bd, signs, alpha)
     sim["full_task_vectors"] = run_similarity_delta(torch, bd, w_base, w_fts)
@@ -544,7 +558,7 @@ def run_monosoup(torch, bd, synth, reps=3):
 # ----------------------------------------------------------------- context
 
 
-def run_context(torch, reps=20):
+def run_context(torch, reps=20, only=""):
     """Reference points measured with the vendor libraries through torch (not
     the product path): a copy over 16 rotating buffers the size of the decode
     layer's weights (torch copy_, read + write), and a plain bf16 GEMM without
@@ -570,7 +584,7 @@ def run_context(torch, reps=20):
     log(f"context: copy of 34 MiB (torch copy_, read + write) {us:.2f} us, {4 * n / us / 1e3:.1f} GB/s")
     del src, dst
     gemm = {}
-    for label, N, K in PREFILL_SHAPES:
+    for label, N, K in prefill_shapes(only):
         # the workload's laws: x ~ N(0, 1), weights ~ N(0, 0.02) (the GEMM's
         # speed depends on the data: its power draw sets the clock)
         x = torch.randn((PREFILL_M, K), device=dev, dtype=torch.bfloat16)
@@ -599,7 +613,7 @@ def run_context(torch, reps=20):
     return out
 
 
-def run_unfused(torch, bd, synth, fused, reps=10):
+def run_unfused(torch, bd, synth, fused, reps=10, only=""):
     """The unfused alternative on the four prefill shapes at m = 2048:
     bitdelta_reconstruct writes W_eff to HBM, then a plain bf16 GEMM
     (torch.mm -> hipBLASLt) reads it; timed back to back per call, next to
@@ -623,7 +637,7 @@ def run_unfused(torch, bd, synth, fused, reps=10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3
 
-    for label, N, K in PREFILL_SHAPES:
+    for label, N, K in prefill_shapes(only):
         sets = []
         for i in range(2):
             w_base, w_ft = synth.device_layer(N, K, seed=1, index=10 * i + len(out))
@@ -1010,10 +1024,95 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
                      f"{(tf_ + tw_) / algo_b:.3f}")
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
+    prev = os.path.join(out_dir, "traffic.json")
+    if os.path.exists(prev):  # keep the per-shape GEMM passes recorded beside the decode entries
+        try:
+            g = json.load(open(prev)).get("gemm")
+        except ValueError:
+            g = None
+        if g:
+            out["gemm"] = g
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print("\n".join(lines))
+
+
+def summarize_gemm_counters(entry, fetch_csv, write_csv, copy_mb, command, out_dir=None):
+    """HBM bytes per call of one prefill shape or of the grouped GEMM, from a
+    FETCH_SIZE and a WRITE_SIZE pass of that section alone (bench.py
+    --no-decode --prefill-shapes LABEL, or --no-prefill --grouped-rows N),
+    each scaled like the decode entries by a copy of copy_mb MiB.  A call of
+    the fused linear is its GEMM launch(es) and, when it splits K, the
+    fixed-order reduce; the unfused path (same run, context leg) is the
+    reconstruct to HBM plus the vendor GEMM.  Recorded under "gemm" in
+    traffic.json with the algorithmic bytes beside it."""
+    import csv
+    import re
+    import statistics
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        return [(_short(r["Kernel_Name"]), float(r["Counter_Value"]) * 1024.0) for r in rows]
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mb << 20
+    f_fetch = copy_bytes / max(v for n, v in fetch if "copyBuffer" in n)
+    f_write = copy_bytes / max(v for n, v in write if "copyBuffer" in n)
+
+    def per_call(patterns):
+        """Sum over the kernels of one call of the median scaled bytes of each;
+        the kernels found (a pattern without dispatches adds nothing)."""
+        tf = tw = 0.0
+        found = []
+        for pat in patterns:
+            rx = re.compile(pat)
+            fv = [v for nm, v in fetch if rx.search(nm)]
+            wv = [v for nm, v in write if rx.search(nm)]
+            if fv and wv:
+                tf += statistics.median(fv) * f_fetch
+                tw += statistics.median(wv) * f_write
+                found.append(next(nm for nm, _ in fetch if rx.search(nm)))
+        return {"kernels": found, "fetch_bytes": round(tf), "write_bytes": round(tw),
+                "bytes_per_launch": round(tf + tw)}
+
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    gemm = rec.setdefault("gemm", {})
+    if entry.startswith("prefill_"):
+        label = entry[len("prefill_"):]
+        N, K = next((n, k) for lb, n, k in PREFILL_SHAPES if lb == label)
+        fused = per_call([r"gemm_tiles_w8<(true|false), false, false>", r"gemm_tiles_w8<(true|false), false, true>",
+                          r"splitk_reduce"])
+        unfused = per_call([r"reconstruct_rows<false>", r"^Cijk|^void Cijk|Cijk_"])
+        algo = {"weights_fused": N * K * 2 + N * K // 8 + 4 * N,
+                "weights_unfused": N * K * 2 + N * K // 8 + 4 * N + 2 * (N * K * 2),
+                "x": PREFILL_M * K * 2, "y": PREFILL_M * N * 2}
+        e = {"fused": fused, "unfused": unfused, "algorithmic": algo,
+             "bytes_per_launch": fused["bytes_per_launch"], "source_sha": source_sha("gemm.hip"),
+             "command": command, "calibration": {"fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}}
+        print(f"{entry}: fused call {fused['fetch_bytes']} B fetched + {fused['write_bytes']} B written "
+              f"({' + '.join(fused['kernels'])}); unfused call {unfused['fetch_bytes']} B + {unfused['write_bytes']} B "
+              f"({' + '.join(unfused['kernels'])}); weights {algo['weights_fused']} B fused vs "
+              f"{algo['weights_unfused']} B unfused algorithmic")
+    else:
+        rows = int(entry.split("_")[-1]) if entry.startswith("grouped_") else 8192
+        g = per_call([r"gemm_tiles_w8<(true|false), true, false>", r"bucket_tokens"])
+        K, V, M = 8192, 14, 4096
+        algo = {"w_base": rows * K * 2, "signs": V * rows * K // 8, "alpha": V * rows * 4, "x": M * K * 2,
+                "y": M * rows * 2}
+        e = {**g, "algorithmic": algo, "algorithmic_bytes": sum(algo.values()),
+             "fetch_over_w_base": round(g["fetch_bytes"] / algo["w_base"], 3),
+             "fetch_over_reads": round(g["fetch_bytes"] / (algo["w_base"] + algo["signs"] + algo["alpha"] + algo["x"]),
+                                       3),
+             "source_sha": source_sha("gemm.hip"), "command": command}
+        print(f"{entry}: {g['fetch_bytes']} B fetched, {g['write_bytes']} B written per launch; reads algorithmic "
+              f"{algo['w_base'] + algo['signs'] + algo['alpha'] + algo['x']} B (W_base {algo['w_base']}): fetched "
+              f"{e['fetch_over_reads']}x the reads, {e['fetch_over_w_base']}x W_base")
+    gemm[entry] = e
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
 
 
 def summarize_trace(trace_csv, gap=12):
@@ -1138,6 +1237,10 @@ def main():
     if args.summarize_kernels:
         summarize_kernels(*args.summarize_kernels)
         return
+    if args.summarize_gemm_counters:
+        e, f, w, mb = args.summarize_gemm_counters
+        summarize_gemm_counters(e, f, w, int(mb), args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               f"Sharding is described in the design notes; run with --gpus 1.", file=sys.stderr)
@@ -1163,32 +1266,36 @@ def main():
                 "stack": res}
         print(json.dumps(line), flush=True)
         return
-    ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup, args.kernel_reps)
-    ms_per_step = dev_s / args.steps * 1e3
-    value = ds.step_bytes * args.steps / dev_s / 1e9
-    log(f"decode step (fused linear m=1,4,16 x 2 alpha modes): {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s "
-        f"(wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
-    for k, v in kernels.items():
-        log(f"  {k:22s} {v['us']:8.2f} us  {v['GB/s']:8.1f} GB/s  {100 * v['frac_hbm']:.1f}% of HBM")
-    rooflines = {k: hbm_roofline(k, kernels[k]) for k in STEP + OFFLINE}
-    # dominant kernel: the step entry with the largest launch time
-    dom = max(STEP, key=lambda k: kernels[k]["us"])
-    roofline = rooflines[dom]
-    step_bytes = ds.step_bytes
-    del ds
-    torch.cuda.empty_cache()
+    if args.no_decode:
+        value = ms_per_step = roofline = step_bytes = None
+        kernels, rooflines = {}, {}
+    else:
+        ds, dev_s, wall_s, kernels = run_decode(torch, bd, synth, args.steps, args.warmup, args.kernel_reps)
+        ms_per_step = dev_s / args.steps * 1e3
+        value = ds.step_bytes * args.steps / dev_s / 1e9
+        log(f"decode step (fused linear m=1,4,16 x 2 alpha modes): {ms_per_step * 1e3:.2f} us/step, "
+            f"{value:.1f} GB/s (wall {wall_s * 1e3:.1f} ms for {args.steps} steps)")
+        for k, v in kernels.items():
+            log(f"  {k:22s} {v['us']:8.2f} us  {v['GB/s']:8.1f} GB/s  {100 * v['frac_hbm']:.1f}% of HBM")
+        rooflines = {k: hbm_roofline(k, kernels[k]) for k in STEP + OFFLINE}
+        # dominant kernel: the step entry with the largest launch time
+        dom = max(STEP, key=lambda k: kernels[k]["us"])
+        roofline = rooflines[dom]
+        step_bytes = ds.step_bytes
+        del ds
+        torch.cuda.empty_cache()
 
-    prefill = None if args.no_prefill else run_prefill(torch, bd, synth)
+    prefill = None if args.no_prefill else run_prefill(torch, bd, synth, only=args.prefill_shapes)
     if prefill is not None:
         for label, e in prefill["shapes"].items():
             rooflines[f"prefill_{label}"] = e["roofline"]
-    grouped, similarity = (None, None) if args.no_grouped else run_grouped(torch, bd, synth)
+    grouped, similarity = (None, None) if args.no_grouped else run_grouped(torch, bd, synth, rows=args.grouped_rows)
     if grouped is not None:
         rooflines["grouped"] = grouped["roofline"]
     monosoup = None if args.no_monosoup else run_monosoup(torch, bd, synth)
-    context = None if args.no_context else run_context(torch)
+    context = None if args.no_context else run_context(torch, only=args.prefill_shapes)
     if context is not None and prefill is not None:
-        context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill)
+        context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill, only=args.prefill_shapes)
     torch.cuda.empty_cache()
     stack = None if args.no_stack else run_stack(torch, bd, synth, args.stack_layers)
     torch.cuda.empty_cache()
@@ -1201,12 +1308,12 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(value, 1) if value is not None else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms_per_step, 5) if ms_per_step is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

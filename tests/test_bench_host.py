@@ -164,3 +164,40 @@ def test_traffic_is_dropped_when_the_kernel_source_changed(monkeypatch):
     assert bench.traffic_for(entry) == rec["kernels"][entry]["bytes_per_launch"]
     monkeypatch.setattr(bench, "source_sha", lambda src: "0" * 16)
     assert bench.traffic_for(entry) is None
+
+
+def test_summarize_gemm_counters(tmp_path):
+    """A prefill shape's fused call (GEMM + split reduce) and unfused call
+    (reconstruct + vendor GEMM), and the grouped GEMM, from synthetic counter
+    CSVs: medians per kernel, scaled by the copy calibration, summed per call,
+    recorded under "gemm" without touching the decode entries."""
+    import bench
+
+    copy_mb = 256
+    fetch_rows, write_rows = [], []
+
+    def add(name, fetch_b, write_b, n=3):
+        for _ in range(n):
+            base = {"Kernel_Name": f"void bd::(anonymous namespace)::{name}(int)", "Grid_Size": 64}
+            fetch_rows.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": fetch_b / 2 / 1024})
+            write_rows.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": write_b / 1024})
+
+    add("__amd_rocclr_copyBuffer", copy_mb << 20, copy_mb << 20, n=1)
+    add("gemm_tiles_w8<false, false, true>", 1000 * 1024, 8 * 1024 ** 2)
+    add("splitk_reduce", 8 * 1024 ** 2, 4 * 1024 ** 2)
+    add("reconstruct_rows<false>", 17 * 1024 ** 2, 16 * 1024 ** 2)
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    _write_csv(tmp_path / "f.csv", fields, fetch_rows)
+    _write_csv(tmp_path / "w.csv", fields, write_rows)
+    (tmp_path / "traffic.json").write_text(json.dumps({"kernels": {"linear_m1_row": {"bytes_per_launch": 7}}}))
+    bench.summarize_gemm_counters("prefill_k/v", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy_mb, "cmd",
+                                  out_dir=str(tmp_path))
+    rec = json.load(open(tmp_path / "traffic.json"))
+    assert rec["kernels"]["linear_m1_row"]["bytes_per_launch"] == 7
+    e = rec["gemm"]["prefill_k/v"]
+    assert e["fused"]["fetch_bytes"] == 1000 * 1024 + 8 * 1024 ** 2
+    assert e["fused"]["write_bytes"] == 12 * 1024 ** 2
+    assert e["unfused"]["fetch_bytes"] == 17 * 1024 ** 2 and e["unfused"]["write_bytes"] == 16 * 1024 ** 2
+    assert e["bytes_per_launch"] == e["fused"]["bytes_per_launch"] == 1000 * 1024 + 20 * 1024 ** 2
+    assert e["algorithmic"]["weights_fused"] == 1024 * 8192 * 2 + 1024 * 1024 + 4 * 1024
+    assert e["source_sha"] == bench.source_sha("gemm.hip")
