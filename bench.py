@@ -122,6 +122,8 @@ def parse():
                    help="no GPU: turn the counter_collection CSVs of a FETCH_SIZE run and a WRITE_SIZE run (each "
                         "made with --copy-probe-mb) into HBM bytes per launch of each decode-step kernel; writes "
                         "profiles/traffic.json and prints a table")
+    p.add_argument("--summarize-stack", metavar="TRACE_CSV",
+                   help="per-linear decode durations of the 70B-shaped stack from a kernel trace of --stack")
     p.add_argument("--summarize-trace", metavar="TRACE_CSV",
                    help="no GPU: per (kernel, grid) dispatch count and durations from a kernel_trace CSV")
     p.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
@@ -407,7 +409,8 @@ def run_grouped(torch, bd, synth, reps=10, rows=8192):
     torch.cuda.empty_cache()
     roof = {"kernel": "grouped", "gpu_kernel": "bucket_tokens + gemm_tiles_w8 (gathered)", "bound": "mfma",
             "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic_record("grouped"), "flop_per_launch": flop,
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_record("grouped" if rows == 8192 else f"grouped_{rows}"), "flop_per_launch": flop,
             "avg_launch_us": round(us, 1)}
     return {"d_out": N, "d_in": K, "m": M, "variants": V, "group_sizes": counts, "us": round(us, 1),
             "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
@@ -943,6 +946,16 @@ def _short(name):
     return re.sub(r"\(.*", "", name)
 
 
+def _copy_probe(dispatches):
+    """Counter value of the copy probe: the run's last copy-kernel dispatch
+    (bench.py --copy-probe-mb issues it after everything else; earlier copies
+    of other sizes, e.g. torch's copy_ of a whole weight tensor, are not it)."""
+    vals = [v for n, v in dispatches if "copyBuffer" in n]
+    if not vals:
+        raise SystemExit("no copy-kernel dispatch in the counter CSV: run with --copy-probe-mb")
+    return vals[-1]
+
+
 def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
     """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each decode-step
     kernel by what the same counters read for a copy of copy_mb MiB, and
@@ -958,8 +971,8 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
     copy_bytes = copy_mb << 20
-    cf = max(v for n, _, v in fetch if "copyBuffer" in n)
-    cw = max(v for n, _, v in write if "copyBuffer" in n)
+    cf = _copy_probe([(n, v) for n, _, v in fetch])
+    cw = _copy_probe([(n, v) for n, _, v in write])
     f_fetch, f_write = copy_bytes / cf, copy_bytes / cw
     algo = DecodeStep.algorithmic_bytes()
     out = {"command": command, "calibration": {"copy_bytes": copy_bytes, "fetch_factor": round(f_fetch, 4),
@@ -1057,8 +1070,8 @@ def summarize_gemm_counters(entry, fetch_csv, write_csv, copy_mb, command, out_d
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
     copy_bytes = copy_mb << 20
-    f_fetch = copy_bytes / max(v for n, v in fetch if "copyBuffer" in n)
-    f_write = copy_bytes / max(v for n, v in write if "copyBuffer" in n)
+    f_fetch = copy_bytes / _copy_probe(fetch)
+    f_write = copy_bytes / _copy_probe(write)
 
     def per_call(patterns):
         """Sum over the kernels of one call of the median scaled bytes of each;
@@ -1172,6 +1185,53 @@ def summarize_kernels(trace_csv, pattern, anchor):
     print(f"{'total':28s} {'':6s} {'':9s} {'':9s} {'':9s} {total:9.1f}")
 
 
+def summarize_stack(trace_csv, n_layers=80):
+    """Decode pass of the 70B-shaped stack from a kernel trace of bench.py
+    --stack: the m = 1 launches (gemv_stream<1, ...>) come in the stack's
+    order, q, k, v, o, gate, up, down per layer, so dispatch i of them is the
+    linear i mod 7.  Per linear shape: launches, average / median duration
+    and the rate over its algorithmic bytes (W_base 2 B + signs 1/8 B per
+    weight, alpha, x, y); then the whole pass (kernel time only, no gaps).
+    The prefill (m = 512) kernels are listed per (kernel, grid)."""
+    import csv
+    import re
+
+    from tenant_fine_tune_amd.stack import LAYER_SHAPES
+
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+    dec = [r for r in rows if re.search(r"gemv_stream<1, ", r["Kernel_Name"])]
+    per_pass = n_layers * len(LAYER_SHAPES)
+    if not dec or len(dec) % per_pass:
+        raise SystemExit(f"{len(dec)} m = 1 launches: not whole passes of {per_pass} linears")
+    passes = len(dec) // per_pass
+    print(f"decode m = 1: {passes} passes x {per_pass} linears")
+    print(f"{'linear':8s} {'d_out':>6s} {'d_in':>6s} {'kernel':40s} {'n':>6s} {'avg us':>8s} {'median':>8s} "
+          f"{'bytes':>11s} {'GB/s':>7s}")
+    tot_us = tot_b = 0.0
+    for j, (name, d_out, d_in) in enumerate(LAYER_SHAPES):
+        sel = dec[j::len(LAYER_SHAPES)]
+        v = [dur(r) for r in sel]
+        b = d_out * d_in * 2 + d_out * d_in // 8 + 4 * d_out + 2 * d_in + 2 * d_out
+        avg = statistics.mean(v)
+        tot_us += sum(v)
+        tot_b += b * len(v)
+        print(f"{name:8s} {d_out:6d} {d_in:6d} {_short(sel[0]['Kernel_Name'])[:40]:40s} {len(v):6d} {avg:8.2f} "
+              f"{statistics.median(v):8.2f} {b:11d} {b / avg / 1e3:7.1f}")
+    print(f"pass: {tot_us / passes / 1e3:.3f} ms of kernel time for {tot_b / passes / 1e9:.2f} GB: "
+          f"{tot_b / tot_us / 1e3:.1f} GB/s ({tot_b / tot_us / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
+    pre = {}
+    for r in rows:
+        if re.search(r"gemm_tiles|splitk_reduce", r["Kernel_Name"]):
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1))
+            pre.setdefault(k, []).append(dur(r))
+    if pre:
+        print("prefill m = 512 kernels, per (kernel, grid):")
+        print(f"{'kernel':44s} {'threads':>9s} {'n':>6s} {'avg us':>9s} {'median':>9s}")
+        for (k, g), v in pre.items():
+            print(f"{k[:44]:44s} {g:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f}")
+
+
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
                  "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU",
                  "GRBM_GUI_ACTIVE")
@@ -1230,6 +1290,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_stack:
+        summarize_stack(args.summarize_stack, args.stack_layers)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

@@ -95,7 +95,7 @@ def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
             fetch_rows.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": fetch_b / 2 / 1024})
             write_rows.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": write_b / 1024})
 
-    add("__amd_rocclr_copyBuffer", 4096, copy_mb << 20, copy_mb << 20, n=1)
+    add("__amd_rocclr_copyBuffer", 4096, 4 * (copy_mb << 20), 4 * (copy_mb << 20), n=1)  # not the probe
     algo = bench.DecodeStep.algorithmic_bytes()
     names = {"compress_row": ["compress_rows<true, false>"],
              "compress_matrix": ["compress_rows<true, true>", "alpha_matrix_finish"],
@@ -111,6 +111,7 @@ def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
         for k in kernels:
             add(k, 1048576, algo[entry] // len(kernels), 4096)
     add("compress_rows<true, false>", 64, 10 ** 9, 10 ** 9, n=2)   # another call of the kernel
+    add("__amd_rocclr_copyBuffer", 4096, copy_mb << 20, copy_mb << 20, n=1)  # the probe, issued last
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     _write_csv(tmp_path / "f.csv", fields, fetch_rows)
     _write_csv(tmp_path / "w.csv", fields, write_rows)
@@ -182,10 +183,11 @@ def test_summarize_gemm_counters(tmp_path):
             fetch_rows.append({**base, "Counter_Name": "FETCH_SIZE", "Counter_Value": fetch_b / 2 / 1024})
             write_rows.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": write_b / 1024})
 
-    add("__amd_rocclr_copyBuffer", copy_mb << 20, copy_mb << 20, n=1)
+    add("__amd_rocclr_copyBuffer", 3 * (copy_mb << 20), 3 * (copy_mb << 20), n=1)  # a weight copy, not the probe
     add("gemm_tiles_w8<false, false, true>", 1000 * 1024, 8 * 1024 ** 2)
     add("splitk_reduce", 8 * 1024 ** 2, 4 * 1024 ** 2)
     add("reconstruct_rows<false>", 17 * 1024 ** 2, 16 * 1024 ** 2)
+    add("__amd_rocclr_copyBuffer", copy_mb << 20, copy_mb << 20, n=1)
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     _write_csv(tmp_path / "f.csv", fields, fetch_rows)
     _write_csv(tmp_path / "w.csv", fields, write_rows)
@@ -201,3 +203,43 @@ def test_summarize_gemm_counters(tmp_path):
     assert e["bytes_per_launch"] == e["fused"]["bytes_per_launch"] == 1000 * 1024 + 20 * 1024 ** 2
     assert e["algorithmic"]["weights_fused"] == 1024 * 8192 * 2 + 1024 * 1024 + 4 * 1024
     assert e["source_sha"] == bench.source_sha("gemm.hip")
+
+
+def test_summarize_stack_assigns_linears_by_order(tmp_path, capsys):
+    """The m = 1 launches of the stack's decode pass are the linears in the
+    stack's order (q, k, v, o, gate, up, down per layer): dispatch i is
+    linear i mod 7, and the pass rate is the algorithmic bytes over the
+    summed kernel time; a launch count that is not whole passes is refused."""
+    from tenant_fine_tune_amd.stack import LAYER_SHAPES
+
+    rows, i = [], 0
+
+    def add(name, us):
+        nonlocal i
+        i += 1
+        rows.append({"Dispatch_Id": i, "Kernel_Name": f"void bd::(anonymous namespace)::{name}(int)",
+                     "Grid_Size_X": 4096, "Grid_Size_Y": 1, "Workgroup_Size_X": 256,
+                     "Start_Timestamp": 10 ** 6 * i, "End_Timestamp": 10 ** 6 * i + int(us * 1000)})
+
+    n_layers, passes = 2, 3
+    for _ in range(passes):
+        for _ in range(n_layers):
+            for j, _ in enumerate(LAYER_SHAPES):
+                add("gemv_stream<1, 1, 8, false, true, false>", 10.0 * (j + 1))
+        add("gemm_tiles_w8<false, false, false>", 100.0)
+    path = tmp_path / "trace.csv"
+    _write_csv(path, list(rows[0]), rows)
+    bench.summarize_stack(str(path), n_layers)
+    out = capsys.readouterr().out.splitlines()
+    assert out[0] == f"decode m = 1: {passes} passes x {n_layers * len(LAYER_SHAPES)} linears"
+    per = {ln.split()[0]: ln.split() for ln in out[2:2 + len(LAYER_SHAPES)]}
+    tot_b = 0
+    for j, (name, d_out, d_in) in enumerate(LAYER_SHAPES):
+        b = d_out * d_in * 2 + d_out * d_in // 8 + 4 * d_out + 2 * d_in + 2 * d_out
+        tot_b += b
+        assert int(per[name][-5]) == passes * n_layers and float(per[name][-4]) == 10.0 * (j + 1)
+        assert int(per[name][-2]) == b
+    pass_us = n_layers * sum(10.0 * (j + 1) for j in range(len(LAYER_SHAPES)))
+    assert f"{tot_b * n_layers / pass_us / 1e3:.1f} GB/s" in out[2 + len(LAYER_SHAPES)]
+    with pytest.raises(SystemExit):
+        bench.summarize_stack(str(path), n_layers + 2)
