@@ -26,12 +26,15 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
 // gemm.hip: dense prefill GEMM and the grouped variant
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 256;
-// How a call is cut: every tile's K loop in `splits` ranges, or (tail > 0)
-// the last `tail` tiles in a second launch with K in `tail_splits` ranges.
+constexpr int kGemmBNNarrow = 128;
+// How a call is cut: tiles kGemmBM x tn, every tile's K loop in `splits`
+// ranges, or (tail > 0) the last `tail` tiles in a second launch with K in
+// `tail_splits` ranges.
 struct GemmPlan {
     int splits;
     int64_t tail;
     int tail_splits;
+    int tn;
 };
 GemmPlan gemm_plan(int64_t m, int64_t d_out, int64_t d_in);
 int64_t gemm_k_split(int64_t d_in, int splits);

@@ -8,7 +8,8 @@
 // many variants over one shared, HBM-resident W_base, which the grouped form
 // serves in one launch.
 //
-// Tile: 256 tokens x 256 output features per workgroup, K stepped by 64.
+// Tile: 256 tokens x 256 output features per workgroup (or 128 features in
+// the eight-wave kernel when a call has few tiles), K stepped by 64.
 // Two kernels share the tiling:
 //  - gemm_tiles_w8 (d_in a multiple of 64: every 70B-class shape), eight
 //    waves; its own comment below gives the pipeline;
@@ -298,9 +299,11 @@ constexpr int kWsBytes = BN * BK * 2;                    // 32768
 // wave's barrier, copy issue and LDS waits are covered by the other's MFMAs.
 // Wave (wm, wn) = (wave / 4, wave % 4) owns output rows wm*128 .. +127 and
 // features wn*64 .. +63 of the 256 x 256 tile (4 x 2 MFMA tiles of 32 x 32,
-// 128 accumulators, so two waves fit the register file).  Per K step of 64:
+// 128 accumulators, so two waves fit the register file); in a tile 128
+// features wide, (wave / 2, wave % 2) owns rows wm*64 .. +63 and features
+// wn*64 .. +63 (2 x 2 MFMA tiles).  Per K step of 64:
 //  - x tile: direct-to-LDS copies one step ahead, into two LDS buffers;
-//  - W_base: each wave loads the 32 feature rows 32*wave .. +31 of the tile
+//  - W_base: each wave loads the 32 (16) feature rows of the tile
 //    straight into VGPRs two steps ahead (1 KB per instruction: 8 rows x 128
 //    contiguous bytes) with their sign bytes, forms W_eff = bf16(W_base +
 //    s alpha) for them once (one fma per weight, sign table in LDS), and
@@ -309,8 +312,16 @@ constexpr int kWsBytes = BN * BK * 2;                    // 32768
 //    there.  W_eff is built exactly once per workgroup and never leaves LDS.
 //  - one barrier per step.
 constexpr int kThreads8 = 512;
+// Tile width TN (features): 256, or 128 for shapes with few tiles.  Waves
+// across the features, 32-row MFMA blocks per wave, 8-row W_base groups per
+// wave: TN = 256 -> 2 waves over the tokens x 4 over the features, each 128
+// tokens x 64 features, 4 groups; TN = 128 -> 4 x 2 waves of 64 tokens x 64
+// features, 2 groups.
+template <int TN> constexpr int kW8Wn = TN / 64;
+template <int TN> constexpr int kW8Mb = BM / 32 / (8 / kW8Wn<TN>);
+template <int TN> constexpr int kW8Groups = TN / 64;
 
-template <bool PER_MATRIX, bool GATHER, bool SPLIT>
+template <bool PER_MATRIX, bool GATHER, bool SPLIT, int TN>
 __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__restrict__ w_base,
                    const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
@@ -337,13 +348,13 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / kW8Wn<TN>, wn = wave % kW8Wn<TN>;
     const int hi = lane >> 5;
     // this launch covers tiles tile0 .. tile0 + gridDim.x - 1
     const int64_t local = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t b = tile0 + local;
     const int64_t mt = b % m_tiles, nt = b / m_tiles;
-    const int64_t n0 = nt * BN;
+    const int64_t n0 = nt * TN;
 
     int64_t m0 = mt * BM;
     const uint8_t *signs = signs_all;
@@ -364,7 +375,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
         if (v >= n_variants) {
             for (int i = 0; i < nrows; ++i) {
                 const int64_t tok = rows_s[i];
-                for (int64_t j = n0 + threadIdx.x; j < min(N, n0 + BN); j += kThreads8)
+                for (int64_t j = n0 + threadIdx.x; j < min(N, n0 + TN); j += kThreads8)
                     y[tok * N + j] = 0;
             }
             return;
@@ -410,27 +421,28 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
                                                      kb, 0, 0);
     };
 
-    // W_base rows of this wave: load i (0..3) covers feature rows
-    // 32*wave + 8i .. +7, lane l -> row 8i + l / 8, chunk l & 7 (8 columns).
-    // One lane offset for i = 0; the 8i rows go in the scalar offset, which
-    // the hardware range check does not cover.  That is safe because the
-    // host runs this kernel only with N a multiple of 32: the wave's 32 rows
-    // n0 + 32 wave .. +31 are then all below N or all at or past it, so a
-    // valid row nw implies valid rows nw + 8i, and an invalid one has the
-    // out-of-range lane offset (zeros).
-    const int64_t nw = n0 + wave * 32 + (lane >> 3);
+    // W_base rows of this wave: load i (0 .. NG-1) covers feature rows
+    // 8 NG wave + 8i .. +7, lane l -> row 8i + l / 8, chunk l & 7 (8
+    // columns).  One lane offset for i = 0; the 8i rows go in the scalar
+    // offset, which the hardware range check does not cover.  That is safe
+    // because the host runs this kernel only with N a multiple of 32: the
+    // wave's 8 NG rows (32 or 16, from a multiple of that) are then all below
+    // N or all at or past it, so a valid row nw implies valid rows nw + 8i,
+    // and an invalid one has the out-of-range lane offset (zeros).
+    constexpr int NG = kW8Groups<TN>, MB = kW8Mb<TN>;
+    const int64_t nw = n0 + wave * (8 * NG) + (lane >> 3);
     const uint32_t woff = nw < N ? (uint32_t)((nw * K + p * 8) * 2) : kInvalidOffset;
     const uint32_t soff = nw < N ? (uint32_t)(nw * G + p) : kInvalidOffset;
     const uint32_t wrow8 = (uint32_t)(8 * K * 2), srow8 = (uint32_t)(8 * G);
-    float a[4];
+    float a[NG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NG; ++i) {
         const int64_t n = nw + 8 * i;
         a[i] = PER_MATRIX ? alpha[0] : (n < N ? alpha[n] : 0.0f);
     }
     struct WRaw8 {
-        uint4 w[4];
-        uint32_t s[4];
+        uint4 w[NG];
+        uint32_t s[NG];
     };
     // group i of the W_base rows (8 rows x 64 columns) and its sign bytes
     auto load_w = [&](WRaw8 &r, int i, int t) {
@@ -439,9 +451,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
         r.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, kb + i * wrow8, 0));
         r.s[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff, ksb + i * srow8, 0);
     };
-    // W_eff of load i -> LDS row n_local = 32*wave + 8i + l/8, position p ^ swizzle
+    // W_eff of load i -> LDS row n_local = 8 NG wave + 8i + l/8, position p ^ swizzle
     auto build_store = [&](const WRaw8 &r, int i, int buf) {
-        const int nl = wave * 32 + i * 8 + (lane >> 3);
+        const int nl = wave * (8 * NG) + i * 8 + (lane >> 3);
         const int sw = ((i & 1) * 4 + (lane >> 4)) & 7;  // (nl >> 1) & 7
         const uint4 e = weff8h(sgn, r.s[i], r.w[i], a[i]);
         *reinterpret_cast<uint4 *>(WEb[buf] + nl * 128 + ((p ^ sw) * 16)) = e;
@@ -451,9 +463,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     // compiler select the AGPR form of the MFMA (left alone, it keeps them in
     // VGPRs, where the MFMAs and the W_eff builds contend for the same
     // register file and barely overlap).
-    f32x16 acc[4][2];
+    f32x16 acc[MB][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
@@ -464,10 +476,10 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 
     const int frow = lane & 31;
     const int fsw = (frow >> 1) & 7;
-    auto read_a = [&](bf16x8 (&A)[4], int buf, int kb) {
-        const uint8_t *base = XSb[buf] + (wm * 128 + frow) * 128 + (((kb * 2 + hi) ^ fsw) * 16);
+    auto read_a = [&](bf16x8 (&A)[MB], int buf, int kb) {
+        const uint8_t *base = XSb[buf] + (wm * (32 * MB) + frow) * 128 + (((kb * 2 + hi) ^ fsw) * 16);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
             A[mb] = *reinterpret_cast<const bf16x8 *>(base + mb * 32 * 128);
     };
     auto read_b = [&](bf16x8 (&B)[2], int buf, int kb) {
@@ -483,31 +495,31 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     dma_x(0, 0);
     dma_x(T > 1 ? 1 : 0, 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NG; ++i)
         load_w(wr, i, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NG; ++i) {
         build_store(wr, i, 0);
         load_w(wr, i, T > 1 ? 1 : 0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bf16x8 A[2][4], B[2][2];
+    bf16x8 A[2][MB], B[2][2];
     read_a(A[0], 0, 0);
     read_b(B[0], 0, 0);
 
     // Step t (x(t) in XS cur, W_eff(t) in WE cur, k-block 0 fragments in
     // registers): k-blocks 0..2 read the next k-block's fragments and run
-    // their MFMAs; after them the four groups of W_eff(t+1) are formed (two
-    // after k-block 0, one after each of k-blocks 1 and 2, so every build has
-    // MFMAs to overlap) into WE nxt, each group's registers refilled with
-    // W(t+2).  Then, with every read of buffer cur done, the barrier; after
+    // their MFMAs; after them the groups of W_eff(t+1) are formed into WE
+    // nxt, each group's registers refilled with W(t+2): with four groups, two
+    // after k-block 0 and one after each of k-blocks 1 and 2; with two, one
+    // after each of k-blocks 0 and 1 (so every build has MFMAs to overlap).  Then, with every read of buffer cur done, the barrier; after
     // it, x(t+2) is copied into XS cur, step t+1's k-block 0 fragments are
     // read, and step t's last 8 MFMAs (k-block 3, from registers) cover that
     // transition.
     auto mfma_kb = [&](int kb) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb & 1][mb], B[kb & 1][nb], acc[mb][nb], 0,
@@ -522,17 +534,23 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
             read_a(A[(kb + 1) & 1], cur, kb + 1);
             read_b(B[(kb + 1) & 1], cur, kb + 1);
             mfma_kb(kb);
-            if (kb == 0) {
-                build_store(wr, 0, nxt);
-                load_w(wr, 0, t2);
+            if constexpr (NG == 4) {
+                if (kb == 0) {
+                    build_store(wr, 0, nxt);
+                    load_w(wr, 0, t2);
+                }
+                build_store(wr, kb + 1, nxt);
+                load_w(wr, kb + 1, t2);  // 2 loads
+            } else if (kb < NG) {
+                build_store(wr, kb, nxt);
+                load_w(wr, kb, t2);
             }
-            build_store(wr, kb + 1, nxt);
-            load_w(wr, kb + 1, t2);  // 2 loads
             __builtin_amdgcn_sched_barrier(0);
         }
-        // x(t+1) has landed (the 8 W loads issued after it may be in flight),
-        // W_eff(t+1) is written and this wave's reads of buffer cur are done
-        wait_vmcnt_lgkm0<8>();
+        // x(t+1) has landed (the 2 NG W loads issued after it may be in
+        // flight), W_eff(t+1) is written and this wave's reads of buffer cur
+        // are done
+        wait_vmcnt_lgkm0<2 * NG>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         dma_x(t2, cur);  // 4 copies: x(t+2)
@@ -556,9 +574,9 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     if constexpr (SPLIT) {
         // fp32 partials in accumulator order: [split][tile - tile0][wave][mb][nb][quarter][lane][4]
         const int64_t tiles = (int64_t)gridDim.x;
-        float *base = partial + (((int64_t)blockIdx.y * tiles + local) * 8 + wave) * (4 * 2 * 4 * 256);
+        float *base = partial + (((int64_t)blockIdx.y * tiles + local) * 8 + wave) * (MB * 2 * 4 * 256);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -572,10 +590,10 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
         for (int nb = 0; nb < 2; ++nb) {
             const int64_t j = n0 + wn * 64 + nb * 32 + (lane & 31);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int i = wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+                    const int i = wm * (32 * MB) + mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
                     int64_t tok;
                     if constexpr (GATHER)
                         tok = rows_s[i];
@@ -592,20 +610,23 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 // Sum the split-K partials of gemm_tiles_w8 in split order (fixed, so the
 // result is deterministic) and write bf16 y.  One thread per 4 accumulators;
 // partial tile i holds output tile tile0 + i.
+template <int TN>
 __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ partial, int splits, int64_t tiles,
                                                      int64_t tile0, int64_t m_tiles, int64_t M, int64_t N,
                                                      uint16_t *__restrict__ y)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * 256 chunks * 64 lanes
+    constexpr int MB = kW8Mb<TN>, WN = kW8Wn<TN>;
+    constexpr int kChunks = 8 * MB * 2 * 4;  // 256-float chunks per tile: [wave][mb][nb][quarter]
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over tiles * kChunks chunks * 64 lanes
     const int lane = (int)(gid & 63);
     const int64_t chunk = gid >> 6;
     const int q = (int)(chunk & 3), nb = (int)((chunk >> 2) & 1);
-    const int mb = (int)((chunk >> 3) & 3);
-    const int wave = (int)((chunk >> 5) & 7);
-    const int64_t tile = chunk >> 8;
+    const int mb = (int)((chunk >> 3) % MB);
+    const int wave = (int)((chunk >> 3) / MB % 8);
+    const int64_t tile = chunk / kChunks;
     if (tile >= tiles)
         return;
-    const int64_t stride = tiles * 256 * 256;  // floats per split
+    const int64_t stride = tiles * BM * TN;  // floats per split
     const float *src = partial + chunk * 256 + lane * 4;
     float4 s = *reinterpret_cast<const float4 *>(src);
     for (int sp = 1; sp < splits; ++sp) {
@@ -616,8 +637,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ p
         s.w += v.w;
     }
     const int64_t mt = (tile0 + tile) % m_tiles, nt = (tile0 + tile) / m_tiles;
-    const int64_t j = nt * BN + (wave & 3) * 64 + nb * 32 + (lane & 31);
-    const int64_t i0 = mt * BM + (wave >> 2) * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
+    const int64_t j = nt * TN + (wave % WN) * 64 + nb * 32 + (lane & 31);
+    const int64_t i0 = mt * BM + (wave / WN) * (32 * MB) + mb * 32 + 8 * q + 4 * (lane >> 5);
     if (j >= N)
         return;
     const float v4[4] = {s.x, s.y, s.z, s.w};
@@ -713,10 +734,10 @@ hipError_t launch_general(const uint16_t *x, int64_t m, const uint16_t *w_base, 
     return hipGetLastError();
 }
 
-// One launch of gemm_tiles_w8 over tiles tile0 .. tile0 + count - 1, K cut
-// into `splits` ranges (partials into `partial`, then summed by
-// splitk_reduce) or unsplit.
-template <bool GATHER>
+// One launch of gemm_tiles_w8 (tiles TN features wide) over tiles tile0 ..
+// tile0 + count - 1, K cut into `splits` ranges (partials into `partial`,
+// then summed by splitk_reduce) or unsplit.
+template <bool GATHER, int TN>
 hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const uint8_t *signs,
                      const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in, uint16_t *y,
                      int64_t m_tiles, const int32_t *table, int32_t n_variants, int64_t tile0, int64_t count,
@@ -727,8 +748,8 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
     float *part = used > 1 ? partial : nullptr;
     const dim3 grid((unsigned)count, (unsigned)used);
 #define BD_W8(PM, SP)                                                                                      \
-    hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs, alpha, \
-                       d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0)
+    hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP, TN>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs,   \
+                       alpha, d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0)
     if constexpr (GATHER) {  // the grouped GEMM never splits K
         if (per_matrix) BD_W8(true, false);
         else BD_W8(false, false);
@@ -743,9 +764,9 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || GATHER || part == nullptr)
         return e;
-    const int64_t threads = count * 256 * 64;
-    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used, count,
-                       tile0, m_tiles, m, d_out, y);
+    const int64_t threads = count * (8 * kW8Mb<TN> * 2 * 4) * 64;
+    hipLaunchKernelGGL(splitk_reduce<TN>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
+                       count, tile0, m_tiles, m, d_out, y);
     return hipGetLastError();
 }
 
@@ -755,7 +776,9 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
 // CU at a time):
 //  - few tiles (under 192): the K loop of every tile is cut into equal
 //    64-aligned ranges so the grid covers the CUs; each range keeps at least
-//    512 columns (8 steps) to amortise the pipeline fill;
+//    512 columns (8 steps) to amortise the pipeline fill.  With at most 128
+//    such tiles, tiles 128 features wide where that pays (twice as many, so
+//    half the K ranges and half the partials to sum for the same grid);
 //  - more tiles than CUs with a last partial wave of at most half the CUs:
 //    that wave's tiles run as a second launch with K cut in 2 (or 4, 8) so
 //    it fills the chip and ends sooner, when every range keeps at least 2048
@@ -768,16 +791,35 @@ static bool w8_shape(int64_t d_out, int64_t d_in) { return d_in % 64 == 0 && d_o
 
 GemmPlan gemm_plan(int64_t m, int64_t d_out, int64_t d_in)
 {
-    GemmPlan p{1, 0, 1};
+    GemmPlan p{1, 0, 1, BN};
     if (!w8_shape(d_out, d_in))
         return p;
-    const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
+    const int64_t m_tiles = (m + BM - 1) / BM;
+    const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
     if (tiles < 192) {
-        int sp = 1;
-        while (sp < 16 && tiles * sp < kCus && d_in / (2 * sp) >= 512)
-            sp *= 2;
-        const int64_t ks = gemm_k_split(d_in, sp);
-        p.splits = (int)((d_in + ks - 1) / ks);
+        // K ranges of one launch over `t` tiles
+        auto ranges = [&](int64_t t) {
+            int sp = 1;
+            while (sp < 16 && t * sp < kCus && d_in / (2 * sp) >= 512)
+                sp *= 2;
+            const int64_t ks = gemm_k_split(d_in, sp);
+            return (int)((d_in + ks - 1) / ks);
+        };
+        p.splits = ranges(tiles);
+        // Narrow tiles cost more per flop (half the MFMAs per copied x tile
+        // and per fragment read) but need half the K ranges: worth it where
+        // the wide plan's ranges are short (at most 1024 columns, where
+        // pipeline fill and the partials dominate) or where narrow tiles
+        // need no split at all.  Measured: +5-16% on such shapes; -18% on
+        // 512 x 8192 x 28672, whose wide ranges are 7168 columns.
+        if (tiles <= 128) {
+            const int64_t narrow = m_tiles * ((d_out + kGemmBNNarrow - 1) / kGemmBNNarrow);
+            const int sp_n = ranges(narrow);
+            if (sp_n == 1 || gemm_k_split(d_in, p.splits) <= 1024) {
+                p.tn = kGemmBNNarrow;
+                p.splits = sp_n;
+            }
+        }
         return p;
     }
     const int64_t rem = tiles % kCus;
@@ -801,12 +843,12 @@ int64_t gemm_k_split(int64_t d_in, int splits)
 size_t gemm_workspace_bytes(int64_t m, int64_t d_out, int64_t d_in)
 {
     const GemmPlan p = gemm_plan(m, d_out, d_in);
-    const size_t tile = (size_t)BM * BN * sizeof(float);
+    const size_t tile = (size_t)BM * p.tn * sizeof(float);
     if (p.tail > 0)
         return (size_t)p.tail_splits * (size_t)p.tail * tile;
     if (p.splits <= 1)
         return 0;
-    const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + BN - 1) / BN);
+    const int64_t tiles = ((m + BM - 1) / BM) * ((d_out + p.tn - 1) / p.tn);
     return (size_t)p.splits * (size_t)tiles * tile;
 }
 
@@ -818,18 +860,22 @@ hipError_t launch_gemm(const uint16_t *x, int64_t m, const uint16_t *w_base, con
     if (!w8_shape(d_out, d_in))
         return launch_general<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr,
                                            0, s);
-    const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
     const GemmPlan p = gemm_plan(m, d_out, d_in);
     float *part = static_cast<float *>(workspace);
+    if (p.tn == kGemmBNNarrow)
+        return launch_w8<false, kGemmBNNarrow>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles,
+                                               nullptr, 0, 0, m_tiles * ((d_out + p.tn - 1) / p.tn), p.splits,
+                                               part, s);
+    const int64_t tiles = m_tiles * ((d_out + BN - 1) / BN);
     if (p.tail == 0)
-        return launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, 0,
-                                tiles, p.splits, part, s);
-    const hipError_t e = launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles,
-                                          nullptr, 0, 0, tiles - p.tail, 1, nullptr, s);
+        return launch_w8<false, BN>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0, 0,
+                                    tiles, p.splits, part, s);
+    const hipError_t e = launch_w8<false, BN>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles,
+                                              nullptr, 0, 0, tiles - p.tail, 1, nullptr, s);
     if (e != hipSuccess)
         return e;
-    return launch_w8<false>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0,
-                            tiles - p.tail, p.tail, p.tail_splits, part, s);
+    return launch_w8<false, BN>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, m_tiles, nullptr, 0,
+                                tiles - p.tail, p.tail, p.tail_splits, part, s);
 }
 
 int64_t grouped_max_tiles(int64_t m, int32_t n_variants)
@@ -898,7 +944,7 @@ hipError_t launch_grouped(const uint16_t *x, int64_t m, const int32_t *ids, int3
     if (!w8_shape(d_out, d_in))
         return launch_general<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace,
                                           n_variants, s);
-    return launch_w8<true>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, 0,
+    return launch_w8<true, BN>(x, m, w_base, signs, alpha, per_matrix, d_out, d_in, y, T, workspace, n_variants, 0,
                            T * ((d_out + BN - 1) / BN), 1, nullptr, s);
 }
 

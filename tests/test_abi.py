@@ -118,10 +118,13 @@ def test_decode_rejects_rows_past_32bit_offsets(bd):
 
 def test_linear_split_k_workspace(bd):
     """Prefill with few 256 x 256 output tiles splits K, and so does a last
-    partial wave of at most 128 tiles; the workspace holds one fp32 256 x 256
-    partial per split tile and range."""
+    partial wave of at most 128 tiles; the workspace holds one fp32 partial
+    tile per split tile and range.  With at most 128 tiles of 256 x 256 the
+    tiles are 256 x 128 (twice as many, half the K ranges) where the wide
+    plan's K ranges are at most 1024 columns or narrow tiles need no split."""
     W = bd.lib.bitdelta_linear_workspace
     tile = 256 * 256 * 4
+    narrow = 256 * 128 * 4
     assert W(16, 64, 4096) == 0                    # decode path
     assert W(2048, 8192, 8192) == 0                # 256 tiles fill the chip
     assert W(2048, 8192, 28672) == 0
@@ -132,10 +135,14 @@ def test_linear_split_k_workspace(bd):
     assert W(4096, 6400, 8192) == 0                # last wave of 144 tiles: over half the CUs
     assert W(4096, 4352, 2048) == 0                # K/2 = 1024: too short to repay the sum
     assert W(512, 28672, 8192) == 0                # 224 tiles: one wave
-    assert W(600, 64, 4096) == 8 * 3 * tile        # 3 tiles, K/8 = 512 per split
-    assert W(2048, 1024, 8192) == 8 * 32 * tile    # 32 tiles x 8 splits = 256
-    assert W(40, 1024, 8192) == 16 * 4 * tile      # capped at 16 splits
-    assert W(512, 8192, 28672) == 4 * 64 * tile
+    assert W(600, 64, 4096) == 8 * 3 * narrow      # 3 narrow tiles, K/8 = 512 per split
+    assert W(2048, 1024, 8192) == 4 * 64 * narrow  # 64 narrow tiles x 4 splits = 256
+    assert W(40, 1024, 8192) == 16 * 8 * narrow    # 8 narrow tiles, capped at 16 splits
+    assert W(512, 8192, 28672) == 4 * 64 * tile    # wide ranges of 7168 columns: stays 256 wide
+    assert W(512, 8192, 8192) == 4 * 64 * tile      # wide ranges of 2048 columns: stays 256 wide
+    assert W(1024, 4096, 4096) == 2 * 128 * narrow  # wide ranges of 1024 columns: narrow, K in 2
+    assert W(512, 256 * 80, 8192) == 2 * 160 * tile  # 160 tiles (over 128): 256 wide, K in 2
+    assert W(256, 256 * 128, 4096) == 0            # 256 narrow tiles fill the chip unsplit
     assert W(600, 64, 1032) == 0                   # d_in not a multiple of 64: general kernel
     assert W(600, 80, 4096) == 0                   # d_out not a multiple of 32: general kernel
     assert W(600, 64, 960) == 0                    # K too short to split

@@ -112,16 +112,18 @@ def test_gemv_mfma_stays_in_bounds(R, K, m):
 
 # ----------------------------------------------------------------- prefill
 
-def w8_accesses(M, N, K, splits=1, old_x=False):
-    """gemm_tiles_w8, dense: 256 x 256 tiles, K steps of 64, 8 waves."""
-    assert K % 64 == 0
+def w8_accesses(M, N, K, splits=1, old_x=False, tn=256):
+    """gemm_tiles_w8, dense: 256 x tn tiles (tn = 256 or 128), K steps of 64,
+    8 waves, each loading tn / 8 rows of W_base in groups of 8."""
+    assert K % 64 == 0 and tn in (256, 128)
     G = K // 8
-    m_tiles, n_tiles = -(-M // 256), -(-N // 256)
+    ng = tn // 64
+    m_tiles, n_tiles = -(-M // 256), -(-N // tn)
     ks = K if splits == 1 else -(-(-(-K // splits)) // 64) * 64
     out = []
     mt, nt, wave, l = np.meshgrid(np.arange(m_tiles), np.arange(n_tiles), np.arange(8), np.arange(64),
                                   indexing="ij")
-    m0, n0 = mt * 256, nt * 256
+    m0, n0 = mt * 256, nt * tn
     p = l & 7
     for ky in range(-(-K // ks)):
         k_begin = ky * ks
@@ -137,10 +139,10 @@ def w8_accesses(M, N, K, splits=1, old_x=False):
                 vo = np.where(tok < M, (tok * K + c * 8) * 2, INV)
                 so = kb + ((j >> 1) * 16 * K * 2 if old_x else 0)
                 out.append(("x", vo, so, 16, M * K * 2))
-            nw = n0 + wave * 32 + (l >> 3)
+            nw = n0 + wave * (8 * ng) + (l >> 3)
             woff = np.where(nw < N, (nw * K + p * 8) * 2, INV)
             soff = np.where(nw < N, nw * G + p, INV)
-            for i in range(4):
+            for i in range(ng):
                 out.append(("W_base", woff, kb + i * 8 * K * 2, 16, N * K * 2))
                 out.append(("signs", soff, ks0 + t * 8 + i * 8 * G, 1, N * G))
     return out
@@ -154,9 +156,10 @@ def w8_shape(N, K):
                                    (600, 64, 4096), (513, 544, 256), (1000, 320, 64)])
 def test_prefill_stays_in_bounds(M, N, K):
     assert w8_shape(N, K)
-    for splits in (1, 2):
-        for name, vo, so, width, size in w8_accesses(M, N, K, splits):
-            assert _violations(vo, so, width, size) == 0, (name, M, N, K, splits)
+    for tn in (256, 128):
+        for splits in (1, 2):
+            for name, vo, so, width, size in w8_accesses(M, N, K, splits, tn=tn):
+                assert _violations(vo, so, width, size) == 0, (name, M, N, K, splits, tn)
 
 
 def test_prefill_model_sees_rows_in_the_scalar_offset():
@@ -174,9 +177,10 @@ def test_prefill_w_rows_need_whole_32_row_blocks():
     """W_base rows 8, 16, 24 further go in the scalar offset; with N not a
     multiple of 32 that reads past W_base, which is why such shapes run on the
     general kernel (all offsets in the lane offset)."""
-    bad = sum(_violations(vo, so, w, sz) for name, vo, so, w, sz in w8_accesses(64, 80, 64)
-              if name in ("W_base", "signs"))
-    assert bad > 0
+    for tn, n in ((256, 80), (128, 72)):  # a wave's 32 (16) rows straddle N
+        bad = sum(_violations(vo, so, w, sz) for name, vo, so, w, sz in w8_accesses(64, n, 64, tn=tn)
+                  if name in ("W_base", "signs"))
+        assert bad > 0
     assert not w8_shape(80, 64)
 
 

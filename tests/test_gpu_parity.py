@@ -232,6 +232,29 @@ def test_identity_prefill_split_k(bd, shape):
     assert same_bits_pm0(y, weff.T)
 
 
+@pytest.mark.parametrize("case", [((1024, 8192), 2048, 4 * 64), ((4096, 4096), 1024, 2 * 128),
+                                  ((160, 4096), 700, 8 * 6)], ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
+def test_narrow_tiles_dyadic_exact(bd, case):
+    """Few tiles of 256 x 256 with short K ranges: the kernel runs tiles 128
+    features wide (twice as many) with half the K ranges (k/v at m = 2048, a
+    4096-wide layer at m = 1024, a ragged d_out of 160 whose last narrow tile
+    holds 32 rows); the workspace holds one 256 x 128 fp32 partial per narrow
+    tile and range.  Exact-arithmetic inputs: both edge features of every
+    narrow tile and random ones, bit for bit; repeated calls give the same
+    bits."""
+    (R, C), M, partials = case
+    assert bd.lib.bitdelta_linear_workspace(M, R, C) == partials * 256 * 128 * 4
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=70 + M % 11)
+    xd, wd, sd, ad = bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])
+    y = host_bits(bd.linear(xd, wd, sd, ad))
+    edges = np.concatenate([np.arange(0, R, 128), np.minimum(np.arange(127, R + 127, 128), R - 1)])
+    rows = np.unique(np.concatenate([edges, synth.u64(16, 0, 9200 + R) % np.uint64(R)]).astype(np.int64))
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0], rows=rows)
+    assert np.array_equal(synth.bf16_bits_to_f32(y[:, rows]).astype(np.float64), y64)
+    x2 = bf16_dev(synth.activations(M, C, seed=71, index=M))
+    assert torch.equal(bd.linear(x2, wd, sd, ad), bd.linear(x2, wd, sd, ad))
+
+
 @pytest.mark.parametrize("case", [((4128, 4096), 4000), ((4352, 8192), 4096)],
                          ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
 def test_last_wave_split_dyadic_exact(bd, case):
