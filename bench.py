@@ -1005,14 +1005,14 @@ def summarize_counters(fetch_csv, write_csv, copy_mb, command, out_dir=None):
         lines.append(f"{entry:18s} {' + '.join(names)[:46]:46s} {n:4d} {tf:12.0f} {tw:12.0f} {total:12.0f} "
                      f"{algo[entry]:13d} {total / algo[entry]:6.3f}")
     # grouped layer (14 variants sharing one 8192 x 8192 W_base, 4096 tokens), if in the runs
-    rx = re.compile(r"gemm_tiles_w8<false, true, false>")
+    rx = re.compile(r"gemm_tiles_w8<false, true, false, \d+>")
     fv = [v for nm, _, v in fetch if rx.search(nm)]
     wv = [v for nm, _, v in write if rx.search(nm)]
     if fv and wv:
         n_ = k_ = 8192
         tf_, tw_ = statistics.median(fv) * f_fetch, statistics.median(wv) * f_write
         w_bytes, s_bytes, x_bytes = n_ * k_ * 2, 14 * n_ * k_ // 8, 4096 * k_ * 2
-        out["grouped"] = {"kernel": "gemm_tiles_w8<false, true, false>", "fetch_bytes": round(tf_),
+        out["grouped"] = {"kernel": "gemm_tiles_w8<false, true, false, 256>", "fetch_bytes": round(tf_),
                           "write_bytes": round(tw_), "w_base_bytes": w_bytes, "signs_bytes": s_bytes,
                           "x_bytes": x_bytes, "fetch_over_w_base": round(tf_ / w_bytes, 3)}
         lines.append(f"grouped GEMM (14 variants, 4096 tokens): fetched {tf_:.0f} B, written {tw_:.0f} B per launch; "
@@ -1095,7 +1095,8 @@ def summarize_gemm_counters(entry, fetch_csv, write_csv, copy_mb, command, out_d
     if entry.startswith("prefill_"):
         label = entry[len("prefill_"):]
         N, K = next((n, k) for lb, n, k in PREFILL_SHAPES if lb == label)
-        fused = per_call([r"gemm_tiles_w8<(true|false), false, false>", r"gemm_tiles_w8<(true|false), false, true>",
+        fused = per_call([r"gemm_tiles_w8<(true|false), false, false, \d+>",
+                          r"gemm_tiles_w8<(true|false), false, true, \d+>",
                           r"splitk_reduce"])
         unfused = per_call([r"reconstruct_rows<false>", r"^Cijk|^void Cijk|Cijk_"])
         algo = {"weights_fused": N * K * 2 + N * K // 8 + 4 * N,
@@ -1110,7 +1111,7 @@ def summarize_gemm_counters(entry, fetch_csv, write_csv, copy_mb, command, out_d
               f"{algo['weights_unfused']} B unfused algorithmic")
     else:
         rows = int(entry.split("_")[-1]) if entry.startswith("grouped_") else 8192
-        g = per_call([r"gemm_tiles_w8<(true|false), true, false>", r"bucket_tokens"])
+        g = per_call([r"gemm_tiles_w8<(true|false), true, false, \d+>", r"bucket_tokens"])
         K, V, M = 8192, 14, 4096
         algo = {"w_base": rows * K * 2, "signs": V * rows * K // 8, "alpha": V * rows * 4, "x": M * K * 2,
                 "y": M * rows * 2}
@@ -1267,7 +1268,7 @@ def summarize_mfma(counter_csv, gap=12):
             j = len(runs) - 1
         runs[j][2].append(d)
         open_run[k] = (i, j)
-    print(f"{'kernel':40s} {'threads':>9s} {'first':>6s} {'n':>3s} {'avg us':>8s} {'MFMA inst':>10s} "
+    print(f"{'kernel':46s} {'threads':>9s} {'first':>6s} {'n':>3s} {'avg us':>8s} {'MFMA inst':>10s} "
           f"{'busy %':>6s} {'clock GHz':>9s} {'MFMA TF/s':>9s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'bank cf':>7s}")
     for (name, threads), first, v in runs:
         us = statistics.mean(d["us"] for d in v)
@@ -1279,7 +1280,7 @@ def summarize_mfma(counter_csv, gap=12):
         # flop per MFMA instruction: v_mfma_f32_32x32x16_bf16 (prefill) or v_mfma_f32_32x32x2_f32 (MonoSoup)
         tf = mf * (4096 if "ms_" in name else 32768) / us / 1e6 if us else 0.0
         per = (f"{c['SQ_INSTS_VALU'] / mf:9.2f} {c['SQ_INSTS_LDS'] / mf:8.2f}" if mf else f"{'-':>9s} {'-':>8s}")
-        print(f"{name[:40]:40s} {threads:9d} {first:6d} {len(v):3d} {us:8.1f} {mf:10.0f} "
+        print(f"{name[:46]:46s} {threads:9d} {first:6d} {len(v):3d} {us:8.1f} {mf:10.0f} "
               f"{100 * busy:6.1f} {clock:9.2f} {tf:9.0f} {per} {c['SQ_LDS_BANK_CONFLICT']:7.0f}")
 
 

@@ -143,7 +143,7 @@ def test_summarize_mfma_busy_and_clock(tmp_path, capsys):
     rows = []
     for d in (1, 2):
         for n, v in vals.items():
-            rows.append({"Dispatch_Id": d, "Kernel_Name": "void bd::(anonymous namespace)::gemm_tiles_w8<false, false, false>(int)",
+            rows.append({"Dispatch_Id": d, "Kernel_Name": "void bd::(anonymous namespace)::gemm_tiles_w8<false, false, false, 256>(int)",
                          "Grid_Size": 131072, "Counter_Name": n, "Counter_Value": v,
                          "Start_Timestamp": 10 ** 6 * d, "End_Timestamp": 10 ** 6 * d + int(us * 1000)})
     _write_csv(tmp_path / "c.csv", list(rows[0]), rows)
@@ -184,8 +184,8 @@ def test_summarize_gemm_counters(tmp_path):
             write_rows.append({**base, "Counter_Name": "WRITE_SIZE", "Counter_Value": write_b / 1024})
 
     add("__amd_rocclr_copyBuffer", 3 * (copy_mb << 20), 3 * (copy_mb << 20), n=1)  # a weight copy, not the probe
-    add("gemm_tiles_w8<false, false, true>", 1000 * 1024, 8 * 1024 ** 2)
-    add("splitk_reduce", 8 * 1024 ** 2, 4 * 1024 ** 2)
+    add("gemm_tiles_w8<false, false, true, 128>", 1000 * 1024, 8 * 1024 ** 2)
+    add("splitk_reduce<128>", 8 * 1024 ** 2, 4 * 1024 ** 2)
     add("reconstruct_rows<false>", 17 * 1024 ** 2, 16 * 1024 ** 2)
     add("__amd_rocclr_copyBuffer", copy_mb << 20, copy_mb << 20, n=1)
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
@@ -226,7 +226,7 @@ def test_summarize_stack_assigns_linears_by_order(tmp_path, capsys):
         for _ in range(n_layers):
             for j, _ in enumerate(LAYER_SHAPES):
                 add("gemv_stream<1, 1, 8, false, true, false>", 10.0 * (j + 1))
-        add("gemm_tiles_w8<false, false, false>", 100.0)
+        add("gemm_tiles_w8<false, false, false, 256>", 100.0)
     path = tmp_path / "trace.csv"
     _write_csv(path, list(rows[0]), rows)
     bench.summarize_stack(str(path), n_layers)
