@@ -391,6 +391,31 @@ __device__ __forceinline__ void round_pair(int step, int m, int &p, int &q)
     }
 }
 
+// The rotation (c, s) of one pair, t = sign(d) e / (|d| + sqrt(d^2 + e^2)),
+// c = 1 / sqrt(1 + t^2), s = t c, from the hardware reciprocal and reciprocal
+// square root, each refined by two Newton steps (quadratic: from the
+// instructions' half precision to full fp64), so c^2 + s^2 = 1 to rounding.
+__device__ __forceinline__ double2 jacobi_rotation(double app, double aqq, double apq)
+{
+    if (apq == 0.0)
+        return make_double2(1.0, 0.0);
+    const double d = aqq - app, e = 2.0 * apq;
+    const double x = fma(d, d, e * e);
+    double y = __builtin_amdgcn_rsq(x);
+    y = y * fma(-0.5 * x * y, y, 1.5);
+    y = y * fma(-0.5 * x * y, y, 1.5);
+    const double den = fabs(d) + x * y;
+    double z = __builtin_amdgcn_rcp(den);
+    z = z * fma(-den, z, 2.0);
+    z = z * fma(-den, z, 2.0);
+    const double t = (d >= 0.0 ? e : -e) * z;
+    const double u = fma(t, t, 1.0);
+    double c = __builtin_amdgcn_rsq(u);
+    c = c * fma(-0.5 * u * c, c, 1.5);
+    c = c * fma(-0.5 * u * c, c, 1.5);
+    return make_double2(c, t * c);
+}
+
 __device__ void jacobi_eig(double (*A)[kPitch], double (*V)[kPitch], double2 *rot, double *red)
 {
     const int tid = threadIdx.x;
@@ -416,15 +441,7 @@ __device__ void jacobi_eig(double (*A)[kPitch], double (*V)[kPitch], double2 *ro
             if (tid < kL / 2) {
                 int p, q;
                 round_pair(step, tid, p, q);
-                const double apq = A[p][q];
-                double c = 1.0, s = 0.0;
-                if (apq != 0.0) {
-                    const double d = A[q][q] - A[p][p], e = 2.0 * apq;
-                    const double t = (d >= 0.0 ? e : -e) / (fabs(d) + sqrt(d * d + e * e));
-                    c = 1.0 / sqrt(1.0 + t * t);
-                    s = t * c;
-                }
-                rot[tid] = make_double2(c, s);
+                rot[tid] = jacobi_rotation(A[p][p], A[q][q], A[p][q]);
             }
             int p1, q1, p2, q2, pa, qa, pb, qb;
             round_pair(step, m1, p1, q1);
