@@ -616,6 +616,76 @@ def run_context(torch, reps=20, only=""):
     return out
 
 
+def run_probes(torch, bd, reps=125):
+    """The library's measurement probes (no part of the method): the
+    practical streaming-read rate, on 16 rotating buffers of the decode
+    layer's weight size (34 MiB, 544 MiB in all, over the MALL) launched back
+    to back from a HIP graph like the decode kernels, and on one 1 GiB
+    buffer; and the dense bf16 MFMA rate of back-to-back register-operand
+    MFMAs on every CU (2 waves per SIMD)."""
+    dev = torch.device("cuda")
+    P = ctypes.c_void_p
+    out = {}
+    n = 34 << 20
+    bufs = [torch.empty(n // 4, dtype=torch.int32, device=dev).random_() for _ in range(SETS)]
+    sink = torch.empty((bd.lib.bitdelta_probe_read_sink_words(n),), dtype=torch.int32, device=dev)
+
+    def launches(s):
+        for i in range(reps):
+            bd.check(bd.lib.bitdelta_probe_read(P(bufs[i % SETS].data_ptr()), n, P(sink.data_ptr()),
+                                                P(s.cuda_stream)))
+
+    g = capture(torch, launches)
+    rep_us = [time_graphs(torch, [g], 1, 1)[0] / reps * 1e6 for _ in range(5)]
+    us = sum(rep_us) / 5
+    out["read_34MiB"] = {"us": round(us, 3), "us_min5": round(min(rep_us), 3), "GB/s": round(n / us / 1e3, 1),
+                         "frac_hbm": round(n / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "kernel": "probe_read (1 KB per load instruction, 16 rotating buffers, graph-launched)"}
+    log(f"context: read probe 34 MiB: {us:.2f} us, {n / us / 1e3:.1f} GB/s")
+    del g, bufs, sink
+    big = 1 << 30
+    buf = torch.empty(big // 4 - 4, dtype=torch.int32, device=dev).random_()   # below 2 GiB, a multiple of 16 B
+    nb = buf.numel() * 4
+    sink = torch.empty((bd.lib.bitdelta_probe_read_sink_words(nb),), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: bd.check(bd.lib.bitdelta_probe_read(P(buf.data_ptr()), nb, P(sink.data_ptr()),
+                                                       P(stream.cuda_stream)))
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 10 * 1e3
+    out["read_1GiB"] = {"us": round(us, 1), "GB/s": round(nb / us / 1e3, 1),
+                        "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "kernel": "probe_read"}
+    log(f"context: read probe 1 GiB: {us:.1f} us, {nb / us / 1e3:.1f} GB/s")
+    del buf, sink
+    blocks, iters = 2 * 256, 4000
+    sink = torch.empty((4 * blocks,), dtype=torch.float32, device=dev)
+    call = lambda: bd.check(bd.lib.bitdelta_probe_mfma(blocks, iters, 1.0, 1.0, P(sink.data_ptr()),
+                                                       P(stream.cuda_stream)))
+    call()
+    torch.cuda.synchronize()
+    rep_us = []
+    for _ in range(5):
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_us.append(e0.elapsed_time(e1) * 1e3)
+    us = sum(rep_us) / 5
+    flop = blocks * 4 * iters * 8 * 32768
+    out["mfma_bf16"] = {"us": round(us, 1), "TFLOP/s": round(flop / us / 1e6, 1),
+                        "frac_mfma": round(flop / us / 1e6 / BF16_PEAK_TFLOPS, 4), "flop": flop,
+                        "kernel": "probe_mfma (v_mfma_f32_32x32x16_bf16 on registers, 2 waves per SIMD)"}
+    log(f"context: MFMA probe: {flop / us / 1e6:.1f} TFLOP/s bf16 dense ({us:.1f} us)")
+    return out
+
+
 def run_unfused(torch, bd, synth, fused, reps=10, only=""):
     """The unfused alternative on the four prefill shapes at m = 2048:
     bitdelta_reconstruct writes W_eff to HBM, then a plain bf16 GEMM
@@ -814,10 +884,29 @@ def run_cpu_baseline(target_s):
         if el >= target_s:
             break
     gbs = bytes_step * n / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(oracle.num_threads()), "kind": "oracle",
+    # the same step on one thread (one step, or more up to a quarter of the budget)
+    threads = int(oracle.num_threads())
+    oracle.set_num_threads(1)
+    try:
+        n1 = 0
+        t0 = time.perf_counter()
+        while True:
+            for m in DECODE_M:
+                oracle.linear(xs[m], w_base, signs, alpha)
+            for m in DECODE_M:
+                oracle.linear(xs[m], w_base, signs, alpha_m, per_matrix=True)
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= target_s / 4:
+                break
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the full decode step (fused linear m=1,4,16 x 2 alpha modes) on one 4096x4096 layer, "
                       f"host-generated inputs, repeated {n} times in {el:.1f} s",
-            "seconds_per_step": round(el / n, 4), "host_cpus": os.cpu_count()}
+            "seconds_per_step": round(el / n, 4), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(bytes_step * n1 / el1 / 1e9, 3), "unit": "GB/s",
+                              "seconds_per_step": round(el1 / n1, 4), "steps": n1}}
 
 
 CPU_ROWS = 512  # output rows of each large matrix the oracle computes; its time is scaled to all rows
@@ -860,6 +949,41 @@ def run_cpu_prefill():
             "layer_TFLOP/s": round(tot_flop / tot_s / 1e12, 5),
             "sample": f"the first {CPU_ROWS} output rows of each shape at m={PREFILL_M}, host-generated inputs, "
                       f"timed once and scaled by d_out/{CPU_ROWS} (extrapolated)"}
+
+
+def run_cpu_stack(n_layers):
+    """The oracle on the 70B-shaped stack, extrapolated: one layer's seven
+    linears at m = 512 (prefill) and m = 1 (decode) and the compress of each
+    of its seven matrices from fp32 W_ft, on the first CPU_ROWS output rows of
+    each, scaled by d_out / CPU_ROWS and by the layer count (a host-generated
+    stack would take about 411 GB of inputs)."""
+    import oracle
+    import synth
+    from tenant_fine_tune_amd.stack import LAYER_SHAPES
+
+    pre = dec = comp = 0.0
+    for i, (name, d_out, d_in) in enumerate(LAYER_SHAPES):
+        w_base, w_ft = synth.layer(CPU_ROWS, d_in, seed=9, index=9300 + i)
+        t0 = time.perf_counter()
+        sg, al = oracle.compress(w_base, w_ft)
+        comp += (time.perf_counter() - t0) * d_out / CPU_ROWS
+        for m, acc in ((512, "pre"), (1, "dec")):
+            x = synth.activations(m, d_in, seed=9, index=9400 + 10 * i + m % 7)
+            t0 = time.perf_counter()
+            oracle.linear(x, w_base, sg, al)
+            el = (time.perf_counter() - t0) * d_out / CPU_ROWS
+            if acc == "pre":
+                pre += el
+            else:
+                dec += el
+    out = {"kind": "oracle", "cores": int(oracle.num_threads()),
+           "prefill_m512_s": round(pre * n_layers, 1), "decode_m1_s": round(dec * n_layers, 2),
+           "compress_variant_s": round(comp * n_layers, 1),
+           "sample": f"one layer's 7 linears and their compress on the first {CPU_ROWS} output rows, "
+                     f"host-generated inputs, scaled by d_out/{CPU_ROWS} and x {n_layers} layers (extrapolated)"}
+    log(f"cpu oracle stack ({n_layers} layers, extrapolated): prefill m=512 {out['prefill_m512_s']} s, "
+        f"decode m=1 {out['decode_m1_s']} s, compress of a variant {out['compress_variant_s']} s")
+    return out
 
 
 def run_cpu_grouped(counts):
@@ -1358,6 +1482,17 @@ def main():
         rooflines["grouped"] = grouped["roofline"]
     monosoup = None if args.no_monosoup else run_monosoup(torch, bd, synth)
     context = None if args.no_context else run_context(torch, only=args.prefill_shapes)
+    if context is not None:
+        context["probes"] = pr = run_probes(torch, bd)
+        # each roofline against what the chip sustains as well: HBM-bound
+        # entries over the read probe on the same 34 MiB rotation (decode
+        # sizes) or 1 GiB, MFMA-bound ones over the MFMA probe
+        for k, r in rooflines.items():
+            if r["bound"] == "hbm":
+                ref = pr["read_34MiB" if r["algorithmic_bytes_per_launch"] < (256 << 20) else "read_1GiB"]
+                r["frac_of_read_probe"] = round(r["achieved"] / ref["GB/s"], 4)
+            else:
+                r["frac_of_mfma_probe"] = round(r["achieved"] / pr["mfma_bf16"]["TFLOP/s"], 4)
     if context is not None and prefill is not None:
         context["unfused_m2048"] = run_unfused(torch, bd, synth, prefill, only=args.prefill_shapes)
     torch.cuda.empty_cache()
@@ -1369,6 +1504,8 @@ def main():
             prefill["cpu_oracle"] = run_cpu_prefill()
         if grouped is not None:
             grouped["cpu_oracle"] = run_cpu_grouped(grouped["group_sizes"])
+        if stack is not None:
+            stack["cpu_oracle"] = run_cpu_stack(args.stack_layers)
 
     line = {
         "metric": METRIC,

@@ -279,6 +279,34 @@ BD_API bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, con
                             float *w_merged, double *sigma,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* -------------------------------------------------------------- probes
+ * Measurement utilities with no counterpart in the method: they give the
+ * practical streaming-read rate and dense bf16 MFMA rate of the device, so
+ * the method's kernels can be read against what the chip sustains as well as
+ * against its published peaks.
+ *
+ * bitdelta_probe_read: reads `bytes` bytes at `src` once (16-byte streaming
+ * loads, one 1 KB contiguous run per 64-lane instruction) and writes one
+ * 32-bit word per wave to `sink`: the XOR of every 32-bit word the wave
+ * read, so the XOR of all sink words is the XOR of the whole buffer.
+ *   src:   device, 16-byte aligned; bytes a multiple of 16 in [16, 2^31 - 1]
+ *          (BD_ESHAPE otherwise).
+ *   sink:  device, 4-byte aligned, bitdelta_probe_read_sink_words(bytes)
+ *          words (0 for an invalid size), fully overwritten.
+ * bitdelta_probe_mfma: `blocks` workgroups of 4 waves; each wave runs `iters`
+ * rounds of 8 independent v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 bf16
+ * products, fp32 accumulation) on register operands whose every element is
+ * bf16(a) (A) and bf16(b) (B), then writes to sink[wave] the fp32 bits of the
+ * sum over its 8 accumulators of lane 0's first element: 8 * 16 * iters *
+ * bf16(a) * bf16(b) (exact while that stays below 2^24 ulps).  flop =
+ * blocks * 4 * iters * 8 * 32768.
+ *   blocks in [1, 2^20], iters in [1, 2^20] (BD_ESHAPE otherwise); sink:
+ *   device, 4-byte aligned, blocks * 4 words. */
+BD_API int64_t bitdelta_probe_read_sink_words(int64_t bytes);
+BD_API bd_status bitdelta_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+BD_API bd_status bitdelta_probe_mfma(int32_t blocks, int32_t iters, float a, float b, uint32_t *sink,
+                                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
+           "probe_read", "probe_mfma",
            "linear_grouped_noalloc", "similarity_delta", "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
            "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
@@ -58,6 +59,9 @@ EXPORTS = {
     "bitdelta_similarity_delta": (_INT, [_P, _P, _INT, _I32, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "bitdelta_monosoup_workspace": (_SZ, [_I64, _I64, _I32, _I32]),
     "bitdelta_monosoup": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "bitdelta_probe_read_sink_words": (_I64, [_I64]),
+    "bitdelta_probe_read": (_INT, [_P, _I64, _P, _P]),
+    "bitdelta_probe_mfma": (_INT, [_I32, _I32, ctypes.c_float, ctypes.c_float, _P, _P]),
     # include/bitdelta_cache.h
     "bitdelta_cache_create": (_INT, [_I32, _I32, _I32, _I64, _P, _SZ, _P, _P, _P]),
     "bitdelta_cache_destroy": (None, [_P]),
@@ -339,6 +343,35 @@ def monosoup(w_base, w_ft, omega, rank: int, power_iters: int = 1, out=None, sig
                                 power_iters, _ptr(out), _ptr(sig) if sig is not None else None, _ptr(ws), nws,
                                 _stream(w_base.device)))
     return out, sig
+
+
+def probe_read(src, sink=None):
+    """Measurement probe (no part of the method): read the bytes of the
+    device tensor `src` once with 1 KB-per-instruction streaming loads.
+    Returns the int32 sink (one XOR word per wave, so the XOR of all of them
+    is the XOR of the buffer's 32-bit words)."""
+    torch = _torch()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    words = lib.bitdelta_probe_read_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty((max(words, 1),), dtype=torch.int32, device=src.device)
+    check(lib.bitdelta_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(src.device)))
+    return sink
+
+
+def probe_mfma(blocks: int, iters: int, a: float = 1.0, b: float = 1.0, sink=None, device=None):
+    """Measurement probe (no part of the method): `blocks` workgroups of 4
+    waves, each running iters x 8 independent bf16 32x32x16 MFMAs on register
+    operands.  Returns the float32 sink, one word per wave, each equal to
+    128 * iters * bf16(a) * bf16(b)."""
+    torch = _torch()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    if sink is None:
+        sink = torch.empty((blocks * 4,), dtype=torch.float32, device=dev)
+    check(lib.bitdelta_probe_mfma(blocks, iters, a, b, _ptr(sink), _stream(dev)))
+    return sink
 
 
 class DeltaCache:

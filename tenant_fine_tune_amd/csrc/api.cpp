@@ -442,4 +442,32 @@ bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, const floa
                   "bitdelta_monosoup");
 }
 
+int64_t bitdelta_probe_read_sink_words(int64_t bytes)
+{
+    if (bytes < 16 || bytes % 16 != 0 || bytes >= ((int64_t)1 << 31))
+        return 0;
+    return bd::probe_read_sink_words(bytes);
+}
+
+bd_status bitdelta_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes < 16 || bytes % 16 != 0 || bytes >= ((int64_t)1 << 31))
+        return fail(BD_ESHAPE, "probe_read needs bytes a multiple of 16 in [16, 2^31 - 1] (got %lld)",
+                    (long long)bytes);
+    BD_NONNULL(src);
+    BD_NONNULL(sink);
+    BD_ALIGNED(src, 16);
+    BD_ALIGNED(sink, 4);
+    return device(bd::launch_probe_read(src, bytes, sink, (hipStream_t)stream), "bitdelta_probe_read");
+}
+
+bd_status bitdelta_probe_mfma(int32_t blocks, int32_t iters, float a, float b, uint32_t *sink, void *stream)
+{
+    if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+        return fail(BD_ESHAPE, "probe_mfma needs blocks and iters in [1, 2^20] (got %d, %d)", blocks, iters);
+    BD_NONNULL(sink);
+    BD_ALIGNED(sink, 4);
+    return device(bd::launch_probe_mfma(blocks, iters, a, b, sink, (hipStream_t)stream), "bitdelta_probe_mfma");
+}
+
 }  // extern "C"

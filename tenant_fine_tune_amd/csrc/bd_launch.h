@@ -86,4 +86,11 @@ hipError_t launch_monosoup(const uint16_t *w_base, const float *w_ft, const floa
                            int64_t rows, int64_t cols, int32_t rank, int32_t power_iters, float *out,
                            double *sigma, void *workspace, hipStream_t s);
 
+// probe.hip: measurement probes (no part of the method).  probe_read reads
+// `bytes` (a multiple of 16, below 2 GiB) and writes
+// probe_read_sink_words(bytes) words; probe_mfma writes blocks * 4 words.
+int64_t probe_read_sink_words(int64_t bytes);
+hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_mfma(int32_t blocks, int32_t iters, float a, float b, uint32_t *sink, hipStream_t s);
+
 }  // namespace bd

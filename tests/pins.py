@@ -399,6 +399,14 @@ def pin_storage_arithmetic(o):
     assert round(100 * alpha_bytes / sign_bytes, 2) == 0.31
     # the post's [4096, 4096] -> [4096, 512] example ("Infrastructure Details")
     assert _sign_bytes_written(o, 4096, 4096) == 4096 * 512
+    # "1/32 of the full-precision delta": the packed code of a matrix is
+    # exactly 1/32 of its fp32 delta (1/16 of a bf16 one) on every shape
+    for d_out, d_in in set(STACK_SHAPES.values()):
+        code = per_row[d_in] * d_out
+        assert 32 * code == 4 * d_out * d_in and 16 * code == 2 * d_out * d_in
+    for d_out, d_in in ((4096, 4096), (3, 8), (5, 1032)):
+        code = _sign_bytes_written(o, d_out, d_in)
+        assert 32 * code == 4 * d_out * d_in and 16 * code == 2 * d_out * d_in
 
 
 # --------------------------------------------------------------- similarity

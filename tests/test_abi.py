@@ -309,3 +309,24 @@ def test_similarity_delta_validation(bd):
     assert call(gram=None) == bd.BD_EINVAL and call(cos=None) == bd.BD_EINVAL and call(ws=None) == bd.BD_EINVAL
     assert call(wb=FAKE_ODD) == bd.BD_EALIGN and call(wft=ctypes.c_void_p(4104)) == bd.BD_EALIGN
     assert call(gram=ctypes.c_void_p(4100)) == bd.BD_EALIGN and call(ws=ctypes.c_void_p(4100)) == bd.BD_EALIGN
+
+
+def test_probe_validation(bd):
+    """The measurement probes check their sizes, pointers and alignment on the
+    host; the read probe's sink holds one word per wave of 8 runs of 1 KB."""
+    L = bd.lib
+    words = L.bitdelta_probe_read_sink_words
+    assert words(16) == 4 and words(32 * 1024) == 4 and words(32 * 1024 + 16) == 8
+    assert words(34 * 2 ** 20) == 4 * -(-34 * 1024 // 32)
+    for bad in (0, 8, 24, -16, 2 ** 31):
+        assert words(bad) == 0
+        assert L.bitdelta_probe_read(FAKE, bad, FAKE, None) == bd.BD_ESHAPE
+    assert L.bitdelta_probe_read(None, 1024, FAKE, None) == bd.BD_EINVAL
+    assert L.bitdelta_probe_read(FAKE, 1024, None, None) == bd.BD_EINVAL
+    assert L.bitdelta_probe_read(FAKE_ODD, 1024, FAKE, None) == bd.BD_EALIGN
+    assert L.bitdelta_probe_read(FAKE, 1024, FAKE_ODD, None) == bd.BD_EALIGN
+    m = L.bitdelta_probe_mfma
+    for blocks, iters in ((0, 1), (1, 0), (2 ** 20 + 1, 1), (1, 2 ** 20 + 1), (-1, 5)):
+        assert m(blocks, iters, 1.0, 1.0, FAKE, None) == bd.BD_ESHAPE
+    assert m(1, 1, 1.0, 1.0, None, None) == bd.BD_EINVAL
+    assert m(1, 1, 1.0, 1.0, FAKE_ODD, None) == bd.BD_EALIGN
