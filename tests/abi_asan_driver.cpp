@@ -122,6 +122,18 @@ int main()
         EXPECT(bitdelta_linear_grouped_noalloc(F, 100, I, 3, F, S, A, 0, 64, 64, F, nullptr), BD_EDEVICE);
     }
 
+    // measurement probes
+    for (int64_t n : {(int64_t)0, (int64_t)16, (int64_t)1040, (int64_t)1 << 30, ((int64_t)1 << 31) - 16,
+                      (int64_t)1 << 31, INT64_MAX, -(int64_t)16})
+        (void)bitdelta_probe_read_sink_words(n);
+    EXPECT(bitdelta_probe_read(F, 24, (uint32_t *)F, nullptr), BD_ESHAPE);
+    EXPECT(bitdelta_probe_read(F, (int64_t)1 << 31, (uint32_t *)F, nullptr), BD_ESHAPE);
+    EXPECT(bitdelta_probe_read(nullptr, 1024, (uint32_t *)F, nullptr), BD_EINVAL);
+    EXPECT(bitdelta_probe_read(ODD, 1024, (uint32_t *)F, nullptr), BD_EALIGN);
+    EXPECT(bitdelta_probe_mfma(0, 1, 1.0f, 1.0f, (uint32_t *)F, nullptr), BD_ESHAPE);
+    EXPECT(bitdelta_probe_mfma(1, INT32_MAX, 1.0f, 1.0f, (uint32_t *)F, nullptr), BD_ESHAPE);
+    EXPECT(bitdelta_probe_mfma(1, 1, 1.0f, 1.0f, nullptr, nullptr), BD_EINVAL);
+
     // delta cache host bookkeeping
     std::vector<unsigned char> region(4 * 256);
     bd_delta_cache *c = nullptr;
