@@ -122,6 +122,8 @@ def parse():
                    help="no GPU: turn the counter_collection CSVs of a FETCH_SIZE run and a WRITE_SIZE run (each "
                         "made with --copy-probe-mb) into HBM bytes per launch of each decode-step kernel; writes "
                         "profiles/traffic.json and prints a table")
+    p.add_argument("--summarize-wave-states", nargs=2, metavar=("CSV_A", "CSV_B"),
+                   help="wave-state fractions per kernel from the two WAVE_STATE_COUNTERS --pmc runs")
     p.add_argument("--summarize-stack", metavar="TRACE_CSV",
                    help="per-linear decode durations of the 70B-shaped stack from a kernel trace of --stack")
     p.add_argument("--summarize-trace", metavar="TRACE_CSV",
@@ -1357,6 +1359,51 @@ def summarize_stack(trace_csv, n_layers=80):
             print(f"{k[:44]:44s} {g:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f}")
 
 
+WAVE_STATE_COUNTERS = (("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+                        "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"),
+                       ("SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+                        "SQ_INST_LEVEL_LDS", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_LDS",
+                        "GRBM_GUI_ACTIVE"))
+
+
+def summarize_wave_states(csv_a, csv_b, pattern="gemm_tiles|splitk_reduce|gemv|compress|reconstruct"):
+    """Where the waves of each library kernel spend their time, from two
+    rocprofv3 --pmc runs of WAVE_STATE_COUNTERS (one per tuple): per (kernel,
+    grid), the median per dispatch of each wave-state counter as a fraction
+    of SQ_WAVE_CYCLES (waiting for a dependency or barrier, waiting to issue,
+    issuing VALU / LDS / VMEM), MFMA busy over the SIMD cycles, and the LDS
+    FIFO-full cycles over SQ_BUSY_CYCLES."""
+    import csv
+    import re
+
+    def load(path):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            n = _short(r["Kernel_Name"])
+            if not re.search(pattern, n):
+                continue
+            per.setdefault((n, int(r["Grid_Size"])), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return {k: {c: statistics.median(v) for c, v in d.items()} for k, d in per.items()}
+
+    a, b = load(csv_a), load(csv_b)
+    print(f"{'kernel':46s} {'threads':>9s} {'wait dep':>8s} {'wait iss':>8s} {'wait LDS':>8s} {'issue':>6s} "
+          f"{'VALU':>6s} {'LDS':>6s} {'VMEM':>6s} {'MFMA bz':>7s} {'LDS fifo':>8s}")
+    for k, ca in a.items():
+        cb = b.get(k, {})
+        wc = ca.get("SQ_WAVE_CYCLES", 0.0)
+        if not wc:
+            continue
+        f = lambda c: ca.get(c, 0.0) / wc
+        simd = cb.get("GRBM_GUI_ACTIVE", 0.0) / 8 * 1024
+        mb = cb.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / simd if simd else 0.0
+        bz = cb.get("SQ_BUSY_CYCLES", 0.0)
+        fifo = (cb.get("SQ_LDS_DATA_FIFO_FULL", 0.0) + cb.get("SQ_LDS_CMD_FIFO_FULL", 0.0)) / bz if bz else 0.0
+        print(f"{k[0][:46]:46s} {k[1]:9d} {f('SQ_WAIT_ANY'):8.3f} {f('SQ_WAIT_INST_ANY'):8.3f} "
+              f"{f('SQ_WAIT_INST_LDS'):8.3f} {f('SQ_ACTIVE_INST_ANY'):6.3f} {f('SQ_ACTIVE_INST_VALU'):6.3f} "
+              f"{f('SQ_ACTIVE_INST_LDS'):6.3f} {f('SQ_ACTIVE_INST_VMEM'):6.3f} {mb:7.3f} {fifo:8.3f}")
+
+
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
                  "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU",
                  "GRBM_GUI_ACTIVE")
@@ -1418,6 +1465,9 @@ def main():
         return
     if args.summarize_stack:
         summarize_stack(args.summarize_stack, args.stack_layers)
+        return
+    if args.summarize_wave_states:
+        summarize_wave_states(*args.summarize_wave_states)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

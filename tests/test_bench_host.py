@@ -243,3 +243,22 @@ def test_summarize_stack_assigns_linears_by_order(tmp_path, capsys):
     assert f"{tot_b * n_layers / pass_us / 1e3:.1f} GB/s" in out[2 + len(LAYER_SHAPES)]
     with pytest.raises(SystemExit):
         bench.summarize_stack(str(path), n_layers + 2)
+
+
+def test_summarize_wave_states(tmp_path, capsys):
+    """Wave-state counters over SQ_WAVE_CYCLES, MFMA busy over the SIMD cycles
+    (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), LDS FIFO-full over busy cycles."""
+    name = "void bd::(anonymous namespace)::gemm_tiles_w8<false, false, false, 256>(int)"
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    a = [{"Kernel_Name": name, "Grid_Size": 131072, "Counter_Name": c, "Counter_Value": v}
+         for c, v in (("SQ_WAVE_CYCLES", 1000), ("SQ_WAIT_ANY", 250), ("SQ_WAIT_INST_ANY", 400),
+                      ("SQ_WAIT_INST_LDS", 70), ("SQ_ACTIVE_INST_ANY", 330), ("SQ_ACTIVE_INST_VALU", 190),
+                      ("SQ_ACTIVE_INST_LDS", 75), ("SQ_ACTIVE_INST_VMEM", 40))]
+    b = [{"Kernel_Name": name, "Grid_Size": 131072, "Counter_Name": c, "Counter_Value": v}
+         for c, v in (("SQ_BUSY_CYCLES", 200), ("SQ_VALU_MFMA_BUSY_CYCLES", 6144),
+                      ("SQ_LDS_DATA_FIFO_FULL", 40), ("SQ_LDS_CMD_FIFO_FULL", 30), ("GRBM_GUI_ACTIVE", 80))]
+    _write_csv(tmp_path / "a.csv", fields, a)
+    _write_csv(tmp_path / "b.csv", fields, b)
+    bench.summarize_wave_states(str(tmp_path / "a.csv"), str(tmp_path / "b.csv"))
+    row = capsys.readouterr().out.splitlines()[1].split()
+    assert row[-9:] == ["0.250", "0.400", "0.070", "0.330", "0.190", "0.075", "0.040", "0.600", "0.350"]
