@@ -1366,7 +1366,7 @@ WAVE_STATE_COUNTERS = (("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ
                         "GRBM_GUI_ACTIVE"))
 
 
-def summarize_wave_states(csv_a, csv_b, pattern="gemm_tiles|splitk_reduce|gemv|compress|reconstruct"):
+def summarize_wave_states(csv_a, csv_b, pattern="gemm_tiles|splitk_reduce|gemv|reconstruct"):
     """Where the waves of each library kernel spend their time, from two
     rocprofv3 --pmc runs of WAVE_STATE_COUNTERS (one per tuple): per (kernel,
     grid), the median per dispatch of each wave-state counter as a fraction
@@ -1535,11 +1535,12 @@ def main():
     if context is not None:
         context["probes"] = pr = run_probes(torch, bd)
         # each roofline against what the chip sustains as well: HBM-bound
-        # entries over the read probe on the same 34 MiB rotation (decode
-        # sizes) or 1 GiB, MFMA-bound ones over the MFMA probe
+        # entries over the read probe on the same 34 MiB rotation (up to
+        # 64 MiB per launch: the decode linears) or on 1 GiB (compress,
+        # reconstruct), MFMA-bound ones over the MFMA probe
         for k, r in rooflines.items():
             if r["bound"] == "hbm":
-                ref = pr["read_34MiB" if r["algorithmic_bytes_per_launch"] < (256 << 20) else "read_1GiB"]
+                ref = pr["read_34MiB" if r["algorithmic_bytes_per_launch"] <= (64 << 20) else "read_1GiB"]
                 r["frac_of_read_probe"] = round(r["achieved"] / ref["GB/s"], 4)
             else:
                 r["frac_of_mfma_probe"] = round(r["achieved"] / pr["mfma_bf16"]["TFLOP/s"], 4)
