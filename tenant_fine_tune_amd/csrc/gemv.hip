@@ -380,15 +380,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 // without it).
 constexpr int kRowsWaves = 16;
 // Steps per barrier: W_eff of NB steps goes into LDS before one barrier, then
-// their NB MFMAs run (tile: 2 buffers x NB steps x 16 rows x 1 KB).
+// their NB MFMAs run (tile: NB steps x 16 rows x 1 KB, one buffer, so a later
+// group first waits for the previous group's reads).  Workgroup b walks its
+// row's steps starting at step b mod S, so the workgroups in flight read
+// different columns of x (and of their rows) at any moment instead of all the
+// same ones.
 constexpr int kRowsNB = 8;
-// Tile buffers: 2 (a group writes one while the previous group's reads of
-// the other may still run) or 1 (an extra barrier before each later group).
-constexpr int kRowsBufs = 1;
-// ROT: workgroup b walks its row's steps starting at step b mod S, so the
-// workgroups in flight read different columns of x (and of their rows) at
-// any moment instead of all the same ones.
-constexpr bool kRowsRot = true;
 
 template <int D, bool PER_MATRIX>
 __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__restrict__ x, int m,
@@ -401,8 +398,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     constexpr int NB = kRowsNB;
     static_assert(D % NB == 0, "the stage ring holds whole barrier groups");
     __shared__ __attribute__((aligned(16))) float sgn[64];
-    constexpr int NBUF = kRowsBufs;
-    __shared__ uint4 tile[NBUF][NB][NW][64];  // W_eff of NB steps: [buffer][step][row][chunk position]
+    __shared__ uint4 tile[NB][NW][64];  // W_eff of NB steps: [step][row][chunk position]
     fill_sign_table(sgn);
     __syncthreads();
     const int lane = threadIdx.x & 63;
@@ -412,7 +408,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     const int64_t row = n0 + wave;
     const int64_t G = K >> 3;
     const int S = (int)(G >> 6);  // 512-column steps (K % 512 == 0)
-    const int rot = kRowsRot ? (int)(blockIdx.x % (unsigned)S) : 0;
+    const int rot = (int)(blockIdx.x % (unsigned)S);
     const bool ok = row < R;
     const float a = PER_MATRIX ? alpha[0] : alpha[ok ? row : R - 1];
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
@@ -434,21 +430,18 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
         xq[d] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, (uint32_t)c * 1024u, 0));
     };
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // steps s .. s + NB - 1 held in stages d .. d + NB - 1, into tile buffer
-    // (s / NB) & 1: every row's W_eff, one barrier, then each wave's MFMAs.
-    // The other buffer was last read in the previous group, which every wave
-    // finished before this group's barrier.
+    // steps s .. s + NB - 1 held in stages d .. d + NB - 1: every row's W_eff
+    // into the tile, one barrier, then each wave's MFMAs.
     auto group = [&](int d, int s) {
-        const int buf = NBUF == 2 ? (s / NB) & 1 : 0;
-        if (NBUF == 1 && s > 0)
-            __syncthreads();  // the previous group's reads of the buffer are done
+        if (s > 0)
+            __syncthreads();  // the previous group's reads of the tile are done
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            tile[buf][i][wave][lane ^ wave] = weff8(sgn, sq[d + i], wq[d + i], a);
+            tile[i][wave][lane ^ wave] = weff8(sgn, sq[d + i], wq[d + i], a);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const uint4 b = tile[buf][i][j][(4 * wave + q) ^ j];
+            const uint4 b = tile[i][j][(4 * wave + q) ^ j];
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xq[d + i]),
                                                           __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
         }
@@ -473,10 +466,10 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     for (int d = 0; d < D; d += NB)
         group(d, S - D + d);
 
-    // sum the waves' partial tiles in wave order (tile buffer 0 holds them:
+    // sum the waves' partial tiles in wave order (the tile holds them:
     // every read of the last group is done after this barrier)
     __syncthreads();
-    f32x4 *red = reinterpret_cast<f32x4 *>(&tile[0][0][0][0]);
+    f32x4 *red = reinterpret_cast<f32x4 *>(&tile[0][0][0]);
     red[wave * 64 + lane] = acc;
     __syncthreads();
     if (threadIdx.x < 256) {
@@ -599,39 +592,11 @@ hipError_t launch_rows_d(const Args &g)
     return hipGetLastError();
 }
 
-// The stage ring depth of gemv_rows: the largest multiple of kRowsNB up to 8
-// that divides the step count; 0 when there is none (other kernel).
-int rows_depth(int64_t S)
-{
-    for (int d = 8; d >= kRowsNB; d -= kRowsNB)
-        if (S % d == 0)
-            return d;
-    return 0;
-}
-
-template <int D>
-hipError_t launch_rows_if(const Args &g)
-{
-    if constexpr (D % kRowsNB == 0)
-        return launch_rows_d<D>(g);
-    else
-        return hipErrorInvalidValue;
-}
-
-hipError_t launch_rows(const Args &g)
-{
-    switch (rows_depth(g.d_in / 512)) {
-    case 8: return launch_rows_if<8>(g);
-    case 7: return launch_rows_if<7>(g);
-    case 6: return launch_rows_if<6>(g);
-    case 5: return launch_rows_if<5>(g);
-    case 4: return launch_rows_if<4>(g);
-    case 3: return launch_rows_if<3>(g);
-    case 2: return launch_rows_if<2>(g);
-    case 1: return launch_rows_if<1>(g);
-    default: return hipErrorInvalidValue;
-    }
-}
+// gemv_rows takes d_in a multiple of 4096: whole rings of 8 stages of 512
+// columns (the ring holds whole barrier groups of kRowsNB = 8 steps).
+constexpr int kRowsDepth = 8;
+static_assert(kRowsDepth % kRowsNB == 0, "the stage ring holds whole barrier groups");
+bool rows_shape(int64_t d_in) { return d_in % (512 * kRowsDepth) == 0; }
 
 }  // namespace
 
@@ -653,8 +618,8 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
             e = dispatch_stream<2, 2>(g, 4);
         else if (m <= 4)
             e = dispatch_stream<4, 1>(g, 4);
-        else if (g.d_in % 512 == 0 && rows_depth(g.d_in / 512) > 0)  // d_in a multiple of 4096
-            e = launch_rows(g);
+        else if (rows_shape(g.d_in))
+            e = launch_rows_d<kRowsDepth>(g);
         else
             e = launch_mfma(g);
         if (e != hipSuccess)
