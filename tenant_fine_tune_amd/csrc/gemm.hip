@@ -327,7 +327,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
                    const uint8_t *__restrict__ signs_all, const float *__restrict__ alpha_all,
                    int64_t N, int64_t K, uint16_t *__restrict__ y, int64_t m_tiles,
                    const int32_t *__restrict__ table, int32_t n_variants,
-                   int64_t k_split, float *__restrict__ partial, int64_t tile0)
+                   int64_t k_split, float *__restrict__ partial, int64_t tile0, int64_t n_fast)
 {
     // sign table: its 256-byte alignment makes the compiler place it first,
     // at LDS address 0, so a lookup address is just the masked nibble (after
@@ -353,7 +353,11 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
     // this launch covers tiles tile0 .. tile0 + gridDim.x - 1
     const int64_t local = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t b = tile0 + local;
-    const int64_t mt = b % m_tiles, nt = b / m_tiles;
+    // tile order: token tiles fastest (each XCD's share holds few feature
+    // tiles, so W_base is fetched once and x once per XCD) or, with n_fast =
+    // the feature-tile count, feature tiles fastest (x once, W_base once per
+    // XCD): the smaller operand is the one fetched by every XCD
+    const int64_t mt = n_fast ? b / n_fast : b % m_tiles, nt = n_fast ? b % n_fast : b / m_tiles;
     const int64_t n0 = nt * TN;
 
     int64_t m0 = mt * BM;
@@ -613,7 +617,7 @@ void gemm_tiles_w8(const uint16_t *__restrict__ x, int64_t M, const uint16_t *__
 template <int TN>
 __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ partial, int splits, int64_t tiles,
                                                      int64_t tile0, int64_t m_tiles, int64_t M, int64_t N,
-                                                     uint16_t *__restrict__ y)
+                                                     uint16_t *__restrict__ y, int64_t n_fast)
 {
     constexpr int MB = kW8Mb<TN>, WN = kW8Wn<TN>;
     constexpr int kChunks = 8 * MB * 2 * 4;  // 256-float chunks per tile: [wave][mb][nb][quarter]
@@ -636,7 +640,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ p
         s.z += v.z;
         s.w += v.w;
     }
-    const int64_t mt = (tile0 + tile) % m_tiles, nt = (tile0 + tile) / m_tiles;
+    const int64_t bt = tile0 + tile;
+    const int64_t mt = n_fast ? bt / n_fast : bt % m_tiles, nt = n_fast ? bt % n_fast : bt / m_tiles;
     const int64_t j = nt * TN + (wave % WN) * 64 + nb * 32 + (lane & 31);
     const int64_t i0 = mt * BM + (wave / WN) * (32 * MB) + mb * 32 + 8 * q + 4 * (lane >> 5);
     if (j >= N)
@@ -743,13 +748,16 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
                      int64_t m_tiles, const int32_t *table, int32_t n_variants, int64_t tile0, int64_t count,
                      int splits, float *partial, hipStream_t s)
 {
+    // feature tiles fastest when W_base (d_out rows) is smaller than x (m
+    // rows): then every XCD fetches all of W_base and its own share of x
+    const int64_t n_fast = !GATHER && d_out < m ? (d_out + TN - 1) / TN : 0;
     const int64_t k_split = splits > 1 ? gemm_k_split(d_in, splits) : d_in;
     const int used = (int)((d_in + k_split - 1) / k_split);
     float *part = used > 1 ? partial : nullptr;
     const dim3 grid((unsigned)count, (unsigned)used);
 #define BD_W8(PM, SP)                                                                                      \
     hipLaunchKernelGGL((gemm_tiles_w8<PM, GATHER, SP, TN>), grid, dim3(kThreads8), 0, s, x, m, w_base, signs,   \
-                       alpha, d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0)
+                       alpha, d_out, d_in, y, m_tiles, table, n_variants, k_split, part, tile0, n_fast)
     if constexpr (GATHER) {  // the grouped GEMM never splits K
         if (per_matrix) BD_W8(true, false);
         else BD_W8(false, false);
@@ -766,7 +774,7 @@ hipError_t launch_w8(const uint16_t *x, int64_t m, const uint16_t *w_base, const
         return e;
     const int64_t threads = count * (8 * kW8Mb<TN> * 2 * 4) * 64;
     hipLaunchKernelGGL(splitk_reduce<TN>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part, used,
-                       count, tile0, m_tiles, m, d_out, y);
+                       count, tile0, m_tiles, m, d_out, y, n_fast);
     return hipGetLastError();
 }
 
