@@ -255,13 +255,15 @@ def test_narrow_tiles_dyadic_exact(bd, case):
     assert torch.equal(bd.linear(x2, wd, sd, ad), bd.linear(x2, wd, sd, ad))
 
 
-@pytest.mark.parametrize("case", [((4128, 4096), 4000), ((4352, 8192), 4096)],
+@pytest.mark.parametrize("case", [((4128, 4096), 4000), ((4352, 8192), 4096), ((4096, 4096), 4608)],
                          ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}")
 def test_last_wave_split_dyadic_exact(bd, case):
-    """More tiles than CUs with a last partial wave (16 or 17 tiles of 272):
-    that wave runs as a second launch with K cut in ranges.  Exact-arithmetic
-    inputs: sampled output features, every one of the last tile column,
-    bit for bit; repeated calls give the same bits."""
+    """More tiles than CUs with a last partial wave (16, 17 or 32 tiles of 272
+    or 288): that wave runs as a second launch with K cut in ranges (the last
+    case has d_out < m, so its tiles are numbered feature tiles fastest and the
+    split wave is the last two token tiles).  Exact-arithmetic inputs: sampled
+    output features, every one of the last tile column, bit for bit; repeated
+    calls give the same bits."""
     (R, C), M = case
     tile = 256 * 256 * 4
     assert bd.lib.bitdelta_linear_workspace(M, R, C) >= 2 * 16 * tile
