@@ -33,12 +33,14 @@
 //   ms_gram         fp64 X^T X of a [n, 64] fp32 matrix, at most 256 partials
 //                   of consecutive rows (fp32 products are exact in fp64);
 //                   ms_gram_reduce sums the partials in a fixed order.
-//   ms_whiten       one workgroup of 1024: the pivoted-Cholesky whitening
-//                   factor T of a 64 x 64 Gram matrix (fp64).
-//   ms_solve        one workgroup of 1024: T of Y's Gram, then a cyclic Jacobi
-//                   eigensolve of T^T H T (fp64, 64x64, round-robin parallel
-//                   ordering, one 2x2 block update per thread and round) and
-//                   P = T U_r.
+//   ms_whiten       one workgroup of 512: the pivoted-Cholesky whitening
+//                   factor T of a 64 x 64 Gram matrix (fp64; one wave factors
+//                   with the rows in registers, then 8 lanes per column invert
+//                   the triangle).
+//   ms_solve        one workgroup of 512: T of Y's Gram, T^T H T, its
+//                   eigenvectors by one-sided Jacobi (fp64, columns held in
+//                   registers, 2 per group of 16 lanes, a ring ordering that
+//                   moves one column per pair and round) and P = T U_r.
 //   ms_apply        X T for a [n, 64] matrix and a 64 x ncols fp64 factor,
 //                   fp64 accumulation, fp32 result into a strided destination.
 //   ms_merge        f32(W_base) + U W^T, 64x64 tiles, v_mfma_f32_32x32x2_f32.
@@ -230,23 +232,83 @@ __global__ __launch_bounds__(256) void ms_gram_reduce(const double *__restrict__
         G[ck * kL * kL + e] = pair + other;
 }
 
-// The small solvers run one workgroup of kSolveThreads per checkpoint.
-constexpr int kSolveThreads = 1024;
-constexpr int kSolveWaves = kSolveThreads / 64;
+// The small solvers run one workgroup of kSolveThreads (8 waves) per
+// checkpoint.  They keep their matrices in registers where the algorithm
+// allows it; LDS carries only what has to change lanes or waves.
+constexpr int kSolveThreads = 512;
+// lanes per column in the triangle inversion, rows per thread block in the
+// 64 x 64 products, lanes per column pair in the eigensolver
+constexpr int kInvLanes = kSolveThreads / 64;
+constexpr int kMmRows = 1024 / kSolveThreads;
+constexpr int kJacLanes = kSolveThreads / 32;
+constexpr int kJacRows = kL / kJacLanes;
 
-// Workgroup-wide fp64 sum, fixed order.
-__device__ double block_sum(double v, double *red)
+// Keeps the compiler from moving memory operations across this point; a
+// wave's own LDS instructions execute in issue order, so this orders the
+// wave's LDS writes and reads without a workgroup barrier.
+__device__ __forceinline__ void wave_sync()
 {
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s = 0.0;
-    for (int w = 0; w < kSolveWaves; ++w)
-        s += red[w];
-    __syncthreads();
-    return s;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Lane moves within rows of 16 lanes (DPP): quad_perm xor 1 (0xB1), quad_perm
+// xor 2 (0x4E), mirror within each half row (0x141), rotate a row by 4 / 8
+// lanes (0x124 / 0x128); fp64 moved as two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over aligned groups of 4 / 8 lanes; every lane of a group gets the same
+// bits (each level adds the same two partial sums in either order).
+__device__ __forceinline__ double sum4(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    return v + dpp_f64<0x4E>(v);
+}
+__device__ __forceinline__ double sum8(double v)
+{
+    v = sum4(v);
+    return v + dpp_f64<0x141>(v);
+}
+__device__ __forceinline__ double sum16(double v)
+{
+    v = sum8(v);
+    return v + dpp_f64<0x128>(v);
+}
+template <int N>
+__device__ __forceinline__ double sum_lanes(double v)
+{
+    static_assert(N == 4 || N == 8 || N == 16, "aligned groups of 4, 8 or 16 lanes");
+    if constexpr (N == 4)
+        return sum4(v);
+    else if constexpr (N == 8)
+        return sum8(v);
+    else
+        return sum16(v);
+}
+
+__device__ __forceinline__ double lane_f64(double v, int lane)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane), hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Largest value over the wave (fmax, NaN ignored), the same in every lane.
+__device__ __forceinline__ double max64(double v)
+{
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x124>(v));
+    v = fmax(v, dpp_f64<0x128>(v));
+    return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
 }
 
 __device__ void load_64x64(const double *__restrict__ g, double (*A)[kPitch])
@@ -256,106 +318,154 @@ __device__ void load_64x64(const double *__restrict__ g, double (*A)[kPitch])
     __syncthreads();
 }
 
+// C = X Y (TX false) or X^T Y (TX true) for 64 x 64 fp64 LDS matrices, each
+// sum in increasing order of the contraction index; thread (rg, cg) forms the
+// kMmRows x 4 block at rows kMmRows rg, columns 4 cg.  The caller
+// synchronises before C is read.
+template <bool TX>
+__device__ void mm64(const double (*X)[kPitch], const double (*Y)[kPitch], double (*C)[kPitch])
+{
+    constexpr int RB = kMmRows;
+    const int rg = threadIdx.x >> 4, cg = threadIdx.x & 15;
+    double acc[RB][4];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.0;
+    for (int m = 0; m < kL; ++m) {
+        double xv[RB], yv[4];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            xv[i] = TX ? X[m][RB * rg + i] : X[RB * rg + i][m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            yv[j] = Y[m][4 * cg + j];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = fma(xv[i], yv[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            C[RB * rg + i][4 * cg + j] = acc[i][j];
+}
+
 // Whitening factor of a Gram matrix by pivoted Cholesky (the rank-revealing
 // form: each step eliminates the largest remaining diagonal; it stops when
 // that is at most 1e-12 of the largest initial one, or not positive).  With
 // the rho chosen indices perm[0..rho) and G restricted to them = M M^T (M
 // lower triangular in pivot order), T[perm[a]][b] = (M^-T)[a][b] for a, b <
 // rho and 0 elsewhere, so that T^T G T = I_rho and X T has orthonormal
-// columns on the numerical range of X (the rest dropped).  S is overwritten
-// (Schur complement), Lf receives the pivot columns, Xi is scratch; T is
-// written through `put(i, j, value)` for every entry.  Returns rho.
+// columns on the numerical range of X (the rest dropped).
 struct CholScratch {
     int perm[kL];
-    int chosen[kL];
-    double piv_d;
-    int piv;
+    int rho;
 };
 
-template <typename Put>
-__device__ int pivoted_whiten(double (*S)[kPitch], double (*Lf)[kPitch], double (*Xi)[kPitch], CholScratch &cs,
-                              Put put)
+// The factorisation, by wave 0 alone: lane i keeps row i of the Schur
+// complement in registers and its diagonal entry.  A step picks the largest
+// remaining diagonal p (ties to the lower index), forms the pivot column
+// l = S[:, p] / sqrt(S[p][p]) (0 in rows already chosen), stores it as
+// Lf[:, j] and subtracts l l^T.  Column p is row p (S is symmetric): lane p
+// stages its row in `buf`, and l reaches every lane through `buf` too.
+// S is only read.
+__device__ void pchol_wave(const double (*S)[kPitch], double (*Lf)[kPitch], double *buf, CholScratch &cs)
 {
-    const int tid = threadIdx.x;
-    if (tid < kL)
-        cs.chosen[tid] = 0;
-    double d0 = tid < kL ? S[tid][tid] : 0.0;
-    if (tid < 64) {   // wave 0: largest initial diagonal
-        for (int o = 32; o > 0; o >>= 1)
-            d0 = fmax(d0, __shfl_xor(d0, o));
-        if (tid == 0)
-            cs.piv_d = d0;
-    }
-    __syncthreads();
-    const double dmax0 = cs.piv_d;
-    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    double s[kL];
+#pragma unroll
+    for (int m = 0; m < kL; ++m)
+        s[m] = S[lane][m];
+    double d = S[lane][lane];
+    const double dmax0 = max64(d);
+    bool chosen = false;
     int rho = 0;
     for (int j = 0; j < kL; ++j) {
-        if (tid < 64) {   // wave 0: argmax of the remaining diagonal, ties to the lower index
-            double v = cs.chosen[tid] ? -1.0 : S[tid][tid];
-            int idx = tid;
-            for (int o = 32; o > 0; o >>= 1) {
-                const double v2 = __shfl_xor(v, o);
-                const int i2 = __shfl_xor(idx, o);
-                if (v2 > v || (v2 == v && i2 < idx)) {
-                    v = v2;
-                    idx = i2;
-                }
-            }
-            if (tid == 0) {
-                cs.piv_d = v;
-                cs.piv = idx;
-            }
-        }
-        __syncthreads();
-        const double dp = cs.piv_d;
-        const int p = cs.piv;
-        if (!(dp > 1e-12 * dmax0) || !(dp > 0.0))
+        // the largest remaining diagonal, the lowest lane holding it
+        const double v = chosen ? -1.0 : d;
+        const double dp = max64(v);
+        const uint64_t at = __ballot(v == dp);
+        if (at == 0 || !(dp > 1e-12 * dmax0) || !(dp > 0.0))
             break;
+        const int p = __builtin_ctzll(at);
         const double sd = sqrt(dp);
-        if (tid < kL)
-            Lf[tid][j] = tid == p ? sd : (cs.chosen[tid] ? 0.0 : S[tid][p] / sd);
-        __syncthreads();
-        if (tid == 0) {
-            cs.chosen[p] = 1;
+        if (lane == p) {
+#pragma unroll
+            for (int m = 0; m < kL; ++m)
+                buf[m] = s[m];
+        }
+        wave_sync();
+        const double l = lane == p ? sd : (chosen ? 0.0 : buf[lane] / sd);
+        Lf[lane][j] = l;
+        if (lane == p) {
+            chosen = true;
             cs.perm[j] = p;
         }
-        for (int e = tid; e < kL * kL; e += kSolveThreads) {
-            const int i = e >> 6, m = e & 63;
-            S[i][m] -= Lf[i][j] * Lf[m][j];
-        }
+        d -= l * l;
+        wave_sync();   // every lane has read buf
+        buf[lane] = l;
+        wave_sync();
+#pragma unroll
+        for (int m = 0; m < kL; ++m)
+            s[m] -= l * buf[m];
+        wave_sync();   // before buf is written again
         rho = j + 1;
-        __syncthreads();
     }
-    // Xi = M^-1 row by row, M[a][b] = Lf[perm[a]][b]: Xi[a][c] = (delta_ac -
-    // sum_{c <= m < a} M[a][m] Xi[m][c]) / M[a][a]; 16 lanes per column c
-    const int c = tid >> 4, part = tid & 15;
-    for (int a = 0; a < rho; ++a) {
-        const int pa = cs.perm[a];
-        double s = 0.0;
-        for (int m = c + part; m < a; m += 16)
-            s += Lf[pa][m] * Xi[m][c];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (part == 0)
-            Xi[a][c] = c <= a ? ((c == a ? 1.0 : 0.0) - s) / Lf[pa][a] : 0.0;
-        __syncthreads();
+    if (lane == 0)
+        cs.rho = rho;
+}
+
+// T from the factorisation (every thread of the workgroup; after a barrier
+// that follows pchol_wave): Xi = M^-1 with M[a][m] = Lf[perm[a]][m], by
+// forward substitution Xi[a][c] = (delta_ac - sum_{c <= m < a} M[a][m]
+// Xi[m][c]) / M[a][a]; column c by the kInvLanes lanes (c, part), lane part
+// keeping Xi[m][c] for m = part + kInvLanes k in registers.
+// Then T[perm[a]][b] = Xi[b][a] for a, b < rho and 0 elsewhere, written
+// through `put(i, j, value)` for every entry.
+template <typename Put>
+__device__ void whiten_factor(const double (*Lf)[kPitch], const CholScratch &cs, Put put)
+{
+    constexpr int NL = kInvLanes;
+    const int tid = threadIdx.x, c = tid / NL, part = tid % NL;
+    const int rho = cs.rho;
+    double x[kL / NL];
+#pragma unroll
+    for (int k = 0; k < kL / NL; ++k)
+        x[k] = 0.0;
+#pragma unroll
+    for (int a = 0; a < kL; ++a) {
+        if (a < rho) {
+            const int pa = cs.perm[a];
+            double s = 0.0;
+#pragma unroll
+            for (int k = 0; NL * k < a; ++k) {
+                const int m = part + NL * k;
+                if (m < a && m >= c)
+                    s += Lf[pa][m] * x[k];
+            }
+            s = sum_lanes<NL>(s);
+            const double xa = c <= a ? ((c == a ? 1.0 : 0.0) - s) / Lf[pa][a] : 0.0;
+            if (part == a % NL)
+                x[a / NL] = xa;
+        }
     }
-    // T[perm[a]][b] = Xi[b][a] (a, b < rho); every other entry 0
-    for (int e = tid; e < kL * kL; e += kSolveThreads) {
-        const int i = e >> 6, b = e & 63;
-        put(i, b, 0.0);
+    for (int e = tid; e < kL * kL; e += kSolveThreads)
+        put(e >> 6, e & 63, 0.0);
+    __syncthreads();
+    if (c < rho) {
+        const int pc = cs.perm[c];
+#pragma unroll
+        for (int k = 0; k < kL / NL; ++k) {
+            const int m = part + NL * k;
+            if (m < rho)
+                put(pc, m, x[k]);
+        }
     }
     __syncthreads();
-    for (int e = tid; e < kL * kL; e += kSolveThreads) {
-        const int a = e >> 6, b = e & 63;
-        if (a < rho && b < rho)
-            put(cs.perm[a], b, Xi[b][a]);
-    }
-    __syncthreads();
-    return rho;
 }
 
 // T (global, [ck][64][64]) = the pivoted-Cholesky whitening factor of G[ck].
@@ -363,108 +473,199 @@ __global__ __launch_bounds__(kSolveThreads) void ms_whiten(const double *__restr
 {
     __shared__ double S[kL][kPitch];
     __shared__ double Lf[kL][kPitch];
-    __shared__ double Xi[kL][kPitch];
+    __shared__ double buf[kL];
     __shared__ CholScratch cs;
     const int64_t ck = blockIdx.x;
     double *t_ck = T + ck * kL * kL;
     load_64x64(G + ck * kL * kL, S);
-    pivoted_whiten(S, Lf, Xi, cs, [&](int i, int j, double v) { t_ck[i * kL + j] = v; });
+    if (threadIdx.x < 64)
+        pchol_wave(S, Lf, buf, cs);
+    __syncthreads();
+    whiten_factor(Lf, cs, [&](int i, int j, double v) { t_ck[i * kL + j] = v; });
 }
 
-// Cyclic Jacobi on the symmetric A (64 x 64, LDS); V receives the
-// eigenvectors (columns), diag(A) the eigenvalues.  Each sweep visits all
-// pairs in 63 rounds of 32 disjoint rotations (round-robin ordering, index
-// 63 fixed); the rotation of a pair is the symmetric Schur decomposition of
-// its 2 x 2 block (Golub and Van Loan, "Matrix Computations"), with
-// t = sign(d) e / (|d| + sqrt(d^2 + e^2)), d = a_qq - a_pp, e = 2 a_pq.
-// Within a round, A <- J^T A J is applied as independent 2 x 2 block
-// updates, one per thread (row pair x column pair), and V <- V J alongside.
-// Stops when the off-diagonal mass is below 1e-22 of the diagonal's.
-__device__ __forceinline__ void round_pair(int step, int m, int &p, int &q)
+// The rotation (c, s) that zeroes the off-diagonal entry of the symmetric
+// 2 x 2 block [[a_pp, a_pq], [a_pq, a_qq]] (its symmetric Schur
+// decomposition, Golub and Van Loan, "Matrix Computations": t = s / c the
+// root of t^2 + 2 tau t - 1 = 0 of smaller magnitude, tau = (a_qq - a_pp) /
+// (2 a_pq)), written with the half angle: with d = a_qq - a_pp, e = 2 a_pq
+// and r = sqrt(d^2 + e^2), c^2 = (1 + |d| / r) / 2 and s = sign(d) e / (2 r c)
+// (sign(0) = +1).  Two reciprocal square roots, each refined by two Newton
+// steps (quadratic: from the instructions' half precision to full fp64), and
+// no division; the caller skips a_pq = 0.
+__device__ __forceinline__ double2 half_angle_rotation(double app, double aqq, double apq)
 {
-    if (m == 0) {
-        p = step;
-        q = kL - 1;
-    } else {
-        p = (step + m) % (kL - 1);
-        q = (step - m + (kL - 1)) % (kL - 1);
-    }
-}
-
-// The rotation (c, s) of one pair, t = sign(d) e / (|d| + sqrt(d^2 + e^2)),
-// c = 1 / sqrt(1 + t^2), s = t c, from the hardware reciprocal and reciprocal
-// square root, each refined by two Newton steps (quadratic: from the
-// instructions' half precision to full fp64), so c^2 + s^2 = 1 to rounding.
-__device__ __forceinline__ double2 jacobi_rotation(double app, double aqq, double apq)
-{
-    if (apq == 0.0)
-        return make_double2(1.0, 0.0);
     const double d = aqq - app, e = 2.0 * apq;
     const double x = fma(d, d, e * e);
     double y = __builtin_amdgcn_rsq(x);
     y = y * fma(-0.5 * x * y, y, 1.5);
     y = y * fma(-0.5 * x * y, y, 1.5);
-    const double den = fabs(d) + x * y;
-    double z = __builtin_amdgcn_rcp(den);
-    z = z * fma(-den, z, 2.0);
-    z = z * fma(-den, z, 2.0);
-    const double t = (d >= 0.0 ? e : -e) * z;
-    const double u = fma(t, t, 1.0);
-    double c = __builtin_amdgcn_rsq(u);
-    c = c * fma(-0.5 * u * c, c, 1.5);
-    c = c * fma(-0.5 * u * c, c, 1.5);
-    return make_double2(c, t * c);
+    const double w = fma(0.5 * fabs(d), y, 0.5);
+    double q = __builtin_amdgcn_rsq(w);
+    q = q * fma(-0.5 * w * q, q, 1.5);
+    q = q * fma(-0.5 * w * q, q, 1.5);
+    return make_double2(w * q, (d >= 0.0 ? e : -e) * y * 0.5 * q);
 }
 
-__device__ void jacobi_eig(double (*A)[kPitch], double (*V)[kPitch], double2 *rot, double *red)
+// Exchange buffers of the eigensolver: per buffer 32 slots of one column of
+// G and one of V (64 rows each) plus 2 doubles of padding.
+constexpr int kXSlot = 2 * kL + 2;
+constexpr int kXBuf = 32 * kXSlot;   // = kL * kPitch: one [kL][kPitch] array per buffer
+static_assert(kXBuf == kL * kPitch, "an exchange buffer fills one 64 x 65 array");
+
+// Eigen-decomposition of the symmetric positive semi-definite M (64 x 64,
+// LDS) by one-sided Jacobi (Hestenes): the columns of G = M are rotated in
+// pairs, G <- G J and V <- V J, by the rotation that zeroes the pair's inner
+// product (the symmetric Schur rotation of the pair's 2 x 2 Gram), until all
+// columns are orthogonal.  Then G = M V with orthogonal columns, so V^T M^2 V
+// is diagonal: V holds eigenvectors of M, and the column norms of G are its
+// eigenvalues (M is positive semi-definite).
+//
+// Parallel ordering: 32 groups of kJacLanes lanes; a group holds two columns
+// (a stationary and a moving slot), each lane keeping kJacRows of the 64 rows
+// of both, of G and of V, in registers.  A sweep has phases of 32, 16, 8, 4,
+// 2 and 1 rounds.  In a phase with rings of Q groups, each round every group
+// rotates its two columns and then hands its moving column to the previous
+// group of its ring (cyclically), so every stationary column of a ring meets
+// every moving column of it.  Before the next phase, in each block of 2Q
+// groups, the lower half's moving columns trade places with the upper half's
+// stationary ones and the upper half's moving columns become stationary, so
+// that the next phase pairs columns that have not met yet.  Each of the 2016
+// pairs meets exactly once per sweep (63 rounds).  Columns change groups
+// through LDS (the lanes of a group move contiguous bytes, 16 each, per
+// instruction), two buffers used in turn, one workgroup barrier per exchange.
+// Stops after a sweep whose largest relative inner product |g_p . g_q| /
+// (|g_p| |g_q|) was at most 1e-9 (the quadratic convergence of cyclic Jacobi
+// leaves the columns orthogonal to rounding after that sweep's rotations), or
+// after kJacobiSweeps sweeps.  Output: Vout[:, j] = the eigenvector of
+// original column j, mu[j] its eigenvalue.  Every thread of the workgroup
+// takes part; Vout may alias M.
+__device__ void jacobi_onesided(const double (*M)[kPitch], double *xb, int *xid, int *red,
+                                double (*Vout)[kPitch], double *mu)
 {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kL * kL; e += kSolveThreads)
-        V[e >> 6][e & 63] = (e >> 6) == (e & 63) ? 1.0 : 0.0;
-    __syncthreads();
-    const int m1 = tid >> 5, m2 = tid & 31;          // the block (row pair m1, column pair m2)
-    const int vi = tid & 63, vm = tid >> 6;          // V rows: pairs vm and vm + 16
-    for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
-        double off = 0.0, dg = 0.0;
-        for (int e = tid; e < kL * kL; e += kSolveThreads) {
-            const double a = A[e >> 6][e & 63];
-            if ((e >> 6) == (e & 63))
-                dg += a * a;
-            else
-                off += a * a;
-        }
-        off = block_sum(off, red);
-        dg = block_sum(dg, red);
-        if (off <= 1e-22 * dg || off == 0.0)
-            break;
-        for (int step = 0; step < kL - 1; ++step) {
-            if (tid < kL / 2) {
-                int p, q;
-                round_pair(step, tid, p, q);
-                rot[tid] = jacobi_rotation(A[p][p], A[q][q], A[p][q]);
-            }
-            int p1, q1, p2, q2, pa, qa, pb, qb;
-            round_pair(step, m1, p1, q1);
-            round_pair(step, m2, p2, q2);
-            round_pair(step, vm, pa, qa);
-            round_pair(step, vm + 16, pb, qb);
-            __syncthreads();
-            const double2 r1 = rot[m1], r2 = rot[m2], ra = rot[vm], rb = rot[vm + 16];
-            const double a = A[p1][p2], b = A[p1][q2], c = A[q1][p2], d = A[q1][q2];
-            const double va = V[vi][pa], wa = V[vi][qa], vb = V[vi][pb], wb = V[vi][qb];
-            const double rpp = r1.x * a - r1.y * c, rpq = r1.x * b - r1.y * d;   // rows of J1^T X
-            const double rqp = r1.y * a + r1.x * c, rqq = r1.y * b + r1.x * d;
-            A[p1][p2] = r2.x * rpp - r2.y * rpq;                                // columns of (J1^T X) J2
-            A[p1][q2] = r2.y * rpp + r2.x * rpq;
-            A[q1][p2] = r2.x * rqp - r2.y * rqq;
-            A[q1][q2] = r2.y * rqp + r2.x * rqq;
-            V[vi][pa] = ra.x * va - ra.y * wa;
-            V[vi][qa] = ra.y * va + ra.x * wa;
-            V[vi][pb] = rb.x * vb - rb.y * wb;
-            V[vi][qb] = rb.y * vb + rb.x * wb;
-            __syncthreads();
-        }
+    constexpr int NL = kJacLanes, NR = kJacRows;
+    const int tid = threadIdx.x, g = tid / NL, sub = tid % NL;
+    // lane `sub` of a group keeps rows 2 sub + 2 NL u + e (e < 2) as entries
+    // t = 2 u + e, so that the group's lanes move contiguous bytes of a
+    // column per LDS instruction
+    auto row = [&](int t) { return 2 * sub + 2 * NL * (t >> 1) + (t & 1); };
+    double gs[NR], gm[NR], vs[NR], vm[NR];
+    int ids = g, idm = 32 + g;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        gs[t] = M[row(t)][ids];
+        gm[t] = M[row(t)][idm];
+        vs[t] = row(t) == ids ? 1.0 : 0.0;
+        vm[t] = row(t) == idm ? 1.0 : 0.0;
     }
+    int cur = 0;
+    auto put = [&](int slot, const double (&gc)[NR], const double (&vc)[NR], int id) {
+        double *p = xb + cur * kXBuf + slot * kXSlot;
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            p[row(t)] = gc[t];
+            p[kL + row(t)] = vc[t];
+        }
+        if (sub == 0)
+            xid[cur * 32 + slot] = id;
+    };
+    auto take = [&](int slot, double (&gc)[NR], double (&vc)[NR], int &id) {
+        const double *p = xb + cur * kXBuf + slot * kXSlot;
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            gc[t] = p[row(t)];
+            vc[t] = p[kL + row(t)];
+        }
+        id = xid[cur * 32 + slot];
+    };
+    // the group's two column norms squared and inner product, summed over
+    // its lanes (every lane gets the same bits)
+    auto gram2 = [&](double &al, double &be, double &ga) {
+        al = 0.0;
+        be = 0.0;
+        ga = 0.0;
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            al = fma(gs[t], gs[t], al);
+            be = fma(gm[t], gm[t], be);
+            ga = fma(gs[t], gm[t], ga);
+        }
+        al = sum_lanes<NL>(al);
+        be = sum_lanes<NL>(be);
+        ga = sum_lanes<NL>(ga);
+    };
+    for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+        bool more = false;   // a pair of this sweep had |g_p . g_q| > 1e-9 |g_p| |g_q|
+        for (int Q = 32; Q >= 1; Q >>= 1) {
+            if (Q < 32) {
+                const bool upper = (g & Q) != 0;
+                if (upper)
+                    put(g, gs, vs, ids);
+                else
+                    put(g, gm, vm, idm);
+                __syncthreads();
+                if (upper) {
+#pragma unroll
+                    for (int t = 0; t < NR; ++t) {
+                        gs[t] = gm[t];
+                        vs[t] = vm[t];
+                    }
+                    ids = idm;
+                    take(g - Q, gm, vm, idm);
+                } else {
+                    take(g + Q, gm, vm, idm);
+                }
+                cur ^= 1;
+            }
+            for (int r = 0; r < Q; ++r) {
+                double al, be, ga;
+                gram2(al, be, ga);
+                const double g2 = ga * ga, ab = al * be;
+                more |= g2 > 1e-18 * ab;
+                if (g2 > 1e-30 * ab) {
+                    const double2 cs = half_angle_rotation(al, be, ga);
+#pragma unroll
+                    for (int t = 0; t < NR; ++t) {
+                        const double a = gs[t], b = gm[t];
+                        gs[t] = cs.x * a - cs.y * b;
+                        gm[t] = cs.y * a + cs.x * b;
+                        const double va = vs[t], vb = vm[t];
+                        vs[t] = cs.x * va - cs.y * vb;
+                        vm[t] = cs.y * va + cs.x * vb;
+                    }
+                }
+                if (Q > 1) {
+                    put(g, gm, vm, idm);
+                    __syncthreads();
+                    take((g & ~(Q - 1)) | ((g + 1) & (Q - 1)), gm, vm, idm);
+                    cur ^= 1;
+                }
+            }
+        }
+        // any such pair in the workgroup
+        const bool wave_more = __ballot(more) != 0;
+        if ((tid & 63) == 0)
+            red[tid >> 6] = wave_more ? 1 : 0;
+        __syncthreads();
+        int w = 0;
+        for (int i = 0; i < kSolveThreads / 64; ++i)
+            w |= red[i];
+        if (!w)
+            break;
+    }
+    double al, be, ga;
+    gram2(al, be, ga);
+    __syncthreads();   // every read of M is done (Vout may alias it)
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        Vout[row(t)][ids] = vs[t];
+        Vout[row(t)][idm] = vm[t];
+    }
+    if (sub == 0) {
+        mu[ids] = sqrt(al);
+        mu[idm] = sqrt(be);
+    }
+    __syncthreads();
 }
 
 // Per checkpoint: P [64][64] fp64 (columns >= r zero) and sigma[r].
@@ -475,39 +676,29 @@ __global__ __launch_bounds__(kSolveThreads) void ms_solve(const double *__restri
                                                           const double *__restrict__ Gz, int r,
                                                           double *__restrict__ P, double *__restrict__ sigma)
 {
-    __shared__ double A[kL][kPitch];
-    __shared__ double V[kL][kPitch];
-    __shared__ double W3[kL][kPitch];
-    __shared__ double Tm[kL][kPitch];
-    __shared__ CholScratch cs;
-    __shared__ double2 rot[kL / 2];
-    __shared__ double red[kSolveWaves];
+    __shared__ double A[kL][kPitch];       // Gy, then H, then T^T H T, then its eigenvectors
+    __shared__ double Tm[kL][kPitch];      // T
+    __shared__ double W2[2][kL][kPitch];   // Lf and H T; the eigensolver's exchange buffers
+    __shared__ double buf[kL];
+    __shared__ double mu[kL];
+    __shared__ int red[kSolveThreads / 64];
+    __shared__ int xid[2 * 32];
     __shared__ int order[kL];
+    __shared__ CholScratch cs;
     const int tid = threadIdx.x;
     const int64_t ck = blockIdx.x;
 
     load_64x64(Gy + ck * kL * kL, A);
-    pivoted_whiten(A, V, W3, cs, [&](int i, int j, double v) { Tm[i][j] = v; });
-
-    // A <- H, V <- H T, A <- T^T (H T), symmetrised
-    load_64x64(Gz + ck * kL * kL, A);
-    for (int e = tid; e < kL * kL; e += kSolveThreads) {
-        const int i = e >> 6, j = e & 63;
-        double s = 0.0;
-#pragma unroll 4
-        for (int m = 0; m < kL; ++m)
-            s += A[i][m] * Tm[m][j];
-        V[i][j] = s;
-    }
+    if (tid < 64)
+        pchol_wave(A, W2[0], buf, cs);
     __syncthreads();
-    for (int e = tid; e < kL * kL; e += kSolveThreads) {
-        const int i = e >> 6, j = e & 63;
-        double s = 0.0;
-#pragma unroll 4
-        for (int m = 0; m < kL; ++m)
-            s += Tm[m][i] * V[m][j];
-        A[i][j] = s;
-    }
+    whiten_factor(W2[0], cs, [&](int i, int j, double v) { Tm[i][j] = v; });
+
+    // A <- H, W2[1] <- H T, A <- T^T (H T), symmetrised
+    load_64x64(Gz + ck * kL * kL, A);
+    mm64<false>(A, Tm, W2[1]);
+    __syncthreads();
+    mm64<true>(Tm, W2[1], A);
     __syncthreads();
     for (int e = tid; e < kL * kL; e += kSolveThreads) {
         const int i = e >> 6, j = e & 63;
@@ -518,35 +709,56 @@ __global__ __launch_bounds__(kSolveThreads) void ms_solve(const double *__restri
         }
     }
     __syncthreads();
-    jacobi_eig(A, V, rot, red);
+    jacobi_onesided(A, &W2[0][0][0], xid, red, A, mu);
 
     // order the eigenvalues mu decreasing (ties to the lower index)
     if (tid < kL) {
-        const double mu = A[tid][tid];
+        const double m0 = mu[tid];
         int rank = 0;
         for (int j = 0; j < kL; ++j) {
-            const double o = A[j][j];
-            rank += (o > mu) || (o == mu && j < tid);
+            const double o = mu[j];
+            rank += (o > m0) || (o == m0 && j < tid);
         }
         order[rank] = tid;
     }
     __syncthreads();
+    // P = T U_r: thread (rg, cg) forms rows kMmRows rg .., columns 4 cg .. + 3
     double *p_ck = P + ck * kL * kL;
-    for (int e = tid; e < kL * kL; e += kSolveThreads) {
-        const int a = e >> 6, t = e & 63;
-        double s = 0.0;
-        if (t < r) {
-            const int j = order[t];
-#pragma unroll 4
-            for (int b = 0; b < kL; ++b)
-                s += Tm[a][b] * V[b][j];
+    {
+        constexpr int RB = kMmRows;
+        const int rg = tid >> 4, cg = tid & 15;
+        int oc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            oc[j] = order[4 * cg + j];
+        double acc[RB][4];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = 0.0;
+        for (int b = 0; b < kL; ++b) {
+            double tv[RB], uv[4];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+                tv[i] = Tm[RB * rg + i][b];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                uv[j] = A[b][oc[j]];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = fma(tv[i], uv[j], acc[i][j]);
         }
-        p_ck[e] = s;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p_ck[(RB * rg + i) * kL + 4 * cg + j] = 4 * cg + j < r ? acc[i][j] : 0.0;
     }
-    if (sigma && tid < r) {
-        const double mu = A[order[tid]][order[tid]];
-        sigma[ck * r + tid] = sqrt(mu > 0.0 ? mu : 0.0);
-    }
+    if (sigma && tid < r)
+        sigma[ck * r + tid] = sqrt(mu[order[tid]]);
 }
 
 // dst[ck][row][c] (row stride dst_row, checkpoint stride dst_ck) =
