@@ -22,10 +22,12 @@
 //    tile pair of variants (NT tiles of 4 variants; NT (NT + 1) / 2 waves).
 //    Per 512-column step the workgroup stages Delta of every variant for the
 //    step into LDS once (each W_ft byte and each W_base byte read once from
-//    HBM, streamed), double-buffered, the loads of step s + 1 in flight while
-//    step s is consumed; lane l of every wave owns group 64 s + l of the
-//    step, which is exactly partial l of the fixed order, and keeps the 16
-//    fp64 partials of its block's pairs.  The lane halving tree then runs by
+//    HBM, streamed, every load instruction 1 KB contiguous), double-buffered,
+//    the loads of step s + 1 in flight while step s is consumed; lane l of
+//    every wave owns group 64 s + l of the step, which is exactly partial l
+//    of the fixed order, and keeps the fp64 partials of its block's pairs (a
+//    diagonal block only those with i <= j; the blocks are ordered so that
+//    the SIMDs carry near-equal shares).  The lane halving tree then runs by
 //    shuffles and lane 0 writes each pair's row term (fp64 [pairs][R], the
 //    caller's workspace).
 //  simdelta_gram: one workgroup per pair a <= b sums the row terms of
@@ -49,6 +51,31 @@ __host__ __device__ constexpr int sd_waves(int nt) { return nt * (nt + 1) / 2; }
 // Packed index of pair a <= b: row a of the upper triangle, diagonal included.
 __host__ __device__ constexpr int sd_pair(int a, int b, int V) { return a * V - a * (a - 1) / 2 + (b - a); }
 
+// Tile pair (ti, tj), ti <= tj, of wave w.  The waves of a workgroup are
+// spread over the CU's 4 SIMDs in turn (wave w on SIMD w mod 4), and a
+// diagonal block forms 10 products per column against 16 for the others, so
+// at NT = 4 (10 waves) the order puts one off-diagonal and two diagonal
+// blocks on each of the SIMDs that hold three waves: 36, 36, 32, 32 products
+// per column against 48, 48, 32, 32 in row order.  Otherwise, row order.
+template <int NT>
+__device__ __forceinline__ void sd_block(int w, int &ti, int &tj)
+{
+    if constexpr (NT == 4) {
+        constexpr int8_t kI[10] = {0, 0, 0, 1, 0, 1, 1, 2, 2, 3};
+        constexpr int8_t kJ[10] = {1, 2, 3, 2, 0, 1, 3, 3, 2, 3};
+        ti = kI[w];
+        tj = kJ[w];
+    } else {
+        int i = 0, idx = w;
+        while (idx >= NT - i) {
+            idx -= NT - i;
+            ++i;
+        }
+        ti = i;
+        tj = i + idx;
+    }
+}
+
 template <int NT, bool FT_F32>
 __global__ __launch_bounds__(64 * sd_waves(NT)) void simdelta_rows(const uint16_t *__restrict__ w_base,
                                                                    const void *__restrict__ w_ft, int V, int64_t R,
@@ -69,53 +96,62 @@ __global__ __launch_bounds__(64 * sd_waves(NT)) void simdelta_rows(const uint16_
     const int S = (int)((G + 63) >> 6);
     const uint16_t *brow = w_base + r * C;
 
-    // block of this wave: tile pair (ti, tj), ti <= tj, in row order
-    int ti = 0, idx = wave;
-    while (idx >= NT - ti) {
-        idx -= NT - ti;
-        ++ti;
-    }
-    const int tj = ti + idx;
+    // block of this wave: tile pair (ti, tj), ti <= tj
+    int ti, tj;
+    sd_block<NT>(wave, ti, tj);
+    const bool diag = ti == tj;   // a diagonal block forms only its i <= j products
 
-    // staging item k of this thread: variant slot v, group 64 s + gl
+    // staging item k of this thread: variant slot v = (tid + k 64 NW) / 64 and
+    // lane gl = tid % 64 (the same for every k, 64 NW being a multiple of 64).
+    // bf16 W_ft: lane gl loads the 8 columns of group 64 s + gl (16 bytes of
+    // W_ft and of W_base: each load instruction 1 KB contiguous).  fp32 W_ft:
+    // lane gl loads columns 512 s + 4 gl .. + 3 and 512 s + 256 + 4 gl .. + 3
+    // (two 16-byte loads, each instruction again 1 KB contiguous; W_base by
+    // two 8-byte loads), which are the halves gl % 2 of groups 64 s + gl / 2
+    // and 64 s + 32 + gl / 2 in LDS.
+    const int gl = (int)threadIdx.x & 63;
     struct Raw {
         uint4 f[FT_F32 ? 2 : 1];
-        uint4 b;
+        uint4 b;   // W_base: bf16 -> 8 columns; fp32 -> x, y = quarter 0, z, w = quarter 1
     };
     Raw raw[ITEMS];
     auto load = [&](int s) {
+        if constexpr (FT_F32) {
+            const int64_t c0 = (int64_t)s * 512 + 4 * gl, c1 = c0 + 256;
+            const bool ok0 = c0 < C, ok1 = c1 < C;
+            const uint2 b0 = ok0 ? *reinterpret_cast<const uint2 *>(brow + c0) : make_uint2(0, 0);
+            const uint2 b1 = ok1 ? *reinterpret_cast<const uint2 *>(brow + c1) : make_uint2(0, 0);
 #pragma unroll
-        for (int k = 0; k < ITEMS; ++k) {
-            const int item = (int)threadIdx.x + k * 64 * NW;
-            const int v = item >> 6, gl = item & 63;
-            const int64_t g = (int64_t)s * 64 + gl;
-            const bool ok = v < V && g < G;
-            if (ok) {
-                raw[k].b = *reinterpret_cast<const uint4 *>(brow + 8 * g);
-                const int64_t e = ((int64_t)v * R + r) * C + 8 * g;
-                if constexpr (FT_F32) {
-                    const float *f = static_cast<const float *>(w_ft) + e;
-                    raw[k].f[0] = ld_stream16(f);
-                    raw[k].f[1] = ld_stream16(f + 4);
+            for (int k = 0; k < ITEMS; ++k) {
+                const int v = ((int)threadIdx.x + k * 64 * NW) >> 6;
+                raw[k].b = make_uint4(b0.x, b0.y, b1.x, b1.y);
+                const float *f = static_cast<const float *>(w_ft) + ((int64_t)v * R + r) * C;
+                raw[k].f[0] = v < V && ok0 ? ld_stream16(f + c0) : make_uint4(0, 0, 0, 0);
+                raw[k].f[1] = v < V && ok1 ? ld_stream16(f + c1) : make_uint4(0, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ITEMS; ++k) {
+                const int v = ((int)threadIdx.x + k * 64 * NW) >> 6;
+                const int64_t g = (int64_t)s * 64 + gl;
+                const bool ok = v < V && g < G;
+                if (ok) {
+                    raw[k].b = *reinterpret_cast<const uint4 *>(brow + 8 * g);
+                    raw[k].f[0] = ld_stream16(static_cast<const uint16_t *>(w_ft) + ((int64_t)v * R + r) * C + 8 * g);
                 } else {
-                    raw[k].f[0] = ld_stream16(static_cast<const uint16_t *>(w_ft) + e);
+                    raw[k].b = make_uint4(0, 0, 0, 0);
+                    raw[k].f[0] = make_uint4(0, 0, 0, 0);
                 }
-            } else {
-                raw[k].b = make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int h = 0; h < (FT_F32 ? 2 : 1); ++h)
-                    raw[k].f[h] = make_uint4(0, 0, 0, 0);
             }
         }
     };
     // Delta = fl32(W_ft - W_base) of each staged item into LDS (zeros for
-    // variant slots past V and groups past the row: zero products, which
+    // variant slots past V and columns past the row: zero products, which
     // leave a partial unchanged)
     auto store = [&](int buf) {
 #pragma unroll
         for (int k = 0; k < ITEMS; ++k) {
-            const int item = (int)threadIdx.x + k * 64 * NW;
-            const int v = item >> 6, gl = item & 63;
+            const int v = ((int)threadIdx.x + k * 64 * NW) >> 6;
             if (v >= NV)
                 continue;
             const uint4 b = raw[k].b;
@@ -137,10 +173,17 @@ __global__ __launch_bounds__(64 * sd_waves(NT)) void simdelta_rows(const uint16_
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 d[i] = ft[i] - base[i];
-            dl[buf][v][0][gl] = make_uint4(__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
-                                           __float_as_uint(d[3]));
-            dl[buf][v][1][gl] = make_uint4(__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]),
-                                           __float_as_uint(d[7]));
+            const uint4 q0 = make_uint4(__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
+                                        __float_as_uint(d[3]));
+            const uint4 q1 = make_uint4(__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]),
+                                        __float_as_uint(d[7]));
+            if constexpr (FT_F32) {
+                dl[buf][v][gl & 1][gl >> 1] = q0;
+                dl[buf][v][gl & 1][32 + (gl >> 1)] = q1;
+            } else {
+                dl[buf][v][0][gl] = q0;
+                dl[buf][v][1][gl] = q1;
+            }
         }
     };
 
@@ -151,6 +194,54 @@ __global__ __launch_bounds__(64 * sd_waves(NT)) void simdelta_rows(const uint16_
         for (int j = 0; j < kSdTile; ++j)
             acc[i][j] = 0.0;
 
+    // this lane's group 64 s + lane of the step in LDS buffer buf, columns in
+    // increasing order, half by half
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint4 qa[kSdTile], qb[kSdTile];
+#pragma unroll
+            for (int i = 0; i < kSdTile; ++i)
+                qa[i] = dl[buf][ti * kSdTile + i][h][lane];
+            if (!diag) {
+#pragma unroll
+                for (int i = 0; i < kSdTile; ++i)
+                    qb[i] = dl[buf][tj * kSdTile + i][h][lane];
+            }
+            if (diag) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    double da[kSdTile];
+#pragma unroll
+                    for (int i = 0; i < kSdTile; ++i)
+                        da[i] = (double)__uint_as_float(c == 0 ? qa[i].x : c == 1 ? qa[i].y : c == 2 ? qa[i].z : qa[i].w);
+#pragma unroll
+                    for (int i = 0; i < kSdTile; ++i)
+#pragma unroll
+                        for (int j = i; j < kSdTile; ++j)
+                            acc[i][j] = __builtin_fma(da[i], da[j], acc[i][j]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    double da[kSdTile], db[kSdTile];
+#pragma unroll
+                    for (int i = 0; i < kSdTile; ++i) {
+                        const uint32_t ua = c == 0 ? qa[i].x : c == 1 ? qa[i].y : c == 2 ? qa[i].z : qa[i].w;
+                        const uint32_t ub = c == 0 ? qb[i].x : c == 1 ? qb[i].y : c == 2 ? qb[i].z : qb[i].w;
+                        da[i] = (double)__uint_as_float(ua);
+                        db[i] = (double)__uint_as_float(ub);
+                    }
+#pragma unroll
+                    for (int i = 0; i < kSdTile; ++i)
+#pragma unroll
+                        for (int j = 0; j < kSdTile; ++j)
+                            acc[i][j] = __builtin_fma(da[i], db[j], acc[i][j]);
+                }
+            }
+        }
+    };
+
     load(0);
     for (int s = 0; s < S; ++s) {
         const int buf = s & 1;
@@ -158,32 +249,7 @@ __global__ __launch_bounds__(64 * sd_waves(NT)) void simdelta_rows(const uint16_
         __syncthreads();
         if (s + 1 < S)
             load(s + 1);
-        // this lane's group 64 s + lane, columns in increasing order, half by half
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4 qa[kSdTile], qb[kSdTile];
-#pragma unroll
-            for (int i = 0; i < kSdTile; ++i) {
-                qa[i] = dl[buf][ti * kSdTile + i][h][lane];
-                qb[i] = dl[buf][tj * kSdTile + i][h][lane];
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                double da[kSdTile], db[kSdTile];
-#pragma unroll
-                for (int i = 0; i < kSdTile; ++i) {
-                    const uint32_t ua = c == 0 ? qa[i].x : c == 1 ? qa[i].y : c == 2 ? qa[i].z : qa[i].w;
-                    const uint32_t ub = c == 0 ? qb[i].x : c == 1 ? qb[i].y : c == 2 ? qb[i].z : qb[i].w;
-                    da[i] = (double)__uint_as_float(ua);
-                    db[i] = (double)__uint_as_float(ub);
-                }
-#pragma unroll
-                for (int i = 0; i < kSdTile; ++i)
-#pragma unroll
-                    for (int j = 0; j < kSdTile; ++j)
-                        acc[i][j] = __builtin_fma(da[i], db[j], acc[i][j]);
-            }
-        }
+        compute(buf);
         // the next store writes the other buffer, last read in step s - 1,
         // which every wave finished before this step's barrier
     }
