@@ -810,27 +810,33 @@ __global__ __launch_bounds__(256) void ms_apply(const float *__restrict__ X, int
 }
 
 // out[R, C] = f32(W_base) + U[R, K] W[C, K]^T, K a multiple of 16 (0 allowed).
-// The accumulator is computed transposed (A operand = W, B operand = U), so
-// each lane holds four consecutive output columns of one row: one 16-byte
-// store and one 8-byte W_base load per group of four.
+// The 64 x 64 tile's products (v_mfma_f32_32x32x2_f32, four waves) pass
+// through LDS to the epilogue, where 16 lanes cover one tile row: each W_base
+// load instruction reads 4 rows x 128 contiguous bytes and each store writes
+// 4 rows x 256 contiguous bytes.
+constexpr int kMergePitch = 68;   // floats per row of the output tile in LDS (16-byte rows)
+
 __global__ __launch_bounds__(256) void ms_merge(const uint16_t *__restrict__ wb, const float *__restrict__ U,
                                                 const float *__restrict__ W, int64_t R, int64_t C, int K,
                                                 float *__restrict__ out)
 {
-    __shared__ float Us[kTile][kPitch];   // [kk][row]
-    __shared__ float Ws[kTile][kPitch];   // [kk][col]
+    // Us [kk][row] and Ws [kk][col], then the output tile [row][col] over both
+    __shared__ __attribute__((aligned(16))) float smem[2 * kTile * kPitch];
+    static_assert(2 * kTile * kPitch >= kTile * kMergePitch, "the output tile fits over Us and Ws");
+    float(*Us)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem);
+    float(*Ws)[kPitch] = reinterpret_cast<float(*)[kPitch]>(smem + kTile * kPitch);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lk = lane >> 5, wi = wave >> 1, wj = wave & 1;
     const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
     const int rr0 = tid >> 4, kq = (tid & 15) * 4;
 
-    // the W_base groups of the epilogue, loaded before the MFMAs so they arrive meanwhile
-    const int64_t row = r0 + 32 * wj + li;
+    // the epilogue's W_base groups (rows rr0 + 16 it, columns kq .. kq + 3),
+    // loaded before the MFMAs so they arrive meanwhile
     uint2 bb[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int64_t c = c0 + 32 * wi + 8 * g + 4 * lk;
-        bb[g] = (row < R && c < C) ? *reinterpret_cast<const uint2 *>(wb + row * C + c) : make_uint2(0u, 0u);
+    for (int it = 0; it < 4; ++it) {
+        const int64_t row = r0 + rr0 + 16 * it, c = c0 + kq;
+        bb[it] = (row < R && c < C) ? *reinterpret_cast<const uint2 *>(wb + row * C + c) : make_uint2(0u, 0u);
     }
 
     f32x16_t acc;
@@ -861,20 +867,30 @@ __global__ __launch_bounds__(256) void ms_merge(const uint16_t *__restrict__ wb,
         }
         __syncthreads();
     }
-    // acc[v]: column c0 + 32 wi + 8 (v / 4) + 4 lk + v % 4, row r0 + 32 wj + li
-    if (row < R) {
+    // acc[v]: column 32 wi + 8 (v / 4) + 4 lk + v % 4, row 32 wj + li of the tile
+    float(*T)[kMergePitch] = reinterpret_cast<float(*)[kMergePitch]>(smem);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t c = c0 + 32 * wi + 8 * g + 4 * lk;
-            if (c < C) {   // C % 4 == 0: the group of four is whole
-                const uint2 b = bb[g];
-                f32x4 o;
-                o[0] = lo_f32(b.x) + acc[4 * g + 0];
-                o[1] = hi_f32(b.x) + acc[4 * g + 1];
-                o[2] = lo_f32(b.y) + acc[4 * g + 2];
-                o[3] = hi_f32(b.y) + acc[4 * g + 3];
-                *reinterpret_cast<f32x4 *>(out + row * C + c) = o;
-            }
+    for (int g = 0; g < 4; ++g) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = acc[4 * g + e];
+        *reinterpret_cast<f32x4 *>(&T[32 * wj + li][32 * wi + 8 * g + 4 * lk]) = o;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int row = rr0 + 16 * it;
+        const int64_t gr = r0 + row, gc = c0 + kq;
+        if (gr < R && gc < C) {   // C % 4 == 0: the group of four is whole
+            const f32x4 p = *reinterpret_cast<const f32x4 *>(&T[row][kq]);
+            const uint2 b = bb[it];
+            f32x4 o;
+            o[0] = lo_f32(b.x) + p[0];
+            o[1] = hi_f32(b.x) + p[1];
+            o[2] = lo_f32(b.y) + p[2];
+            o[3] = hi_f32(b.y) + p[3];
+            *reinterpret_cast<f32x4 *>(out + gr * C + gc) = o;
         }
     }
 }
