@@ -742,8 +742,8 @@ def run_unfused(torch, bd, synth, fused, reps=10, only=""):
                       "fused_overhead_us": round(t_f - t_m, 1), "unfused_overhead_us": round(t_u - t_m, 1),
                       "weight_bytes_fused": N * K * 2 + N * K // 8,
                       "weight_bytes_unfused": N * K * 2 + N * K // 8 + 2 * (N * K * 2)}
-        log(f"unfused {label} [{N},{K}] m={PREFILL_M}: reconstruct {t_r:.1f} us + plain GEMM {t_m:.1f} us "
-            f"= {t_u:.1f} us back to back; fused {t_f:.1f} us (overhead over the plain GEMM: fused "
+        log(f"unfused {label} [{N},{K}] m={PREFILL_M}: reconstruct {t_r:.1f} us, plain GEMM {t_m:.1f} us (each "
+            f"alone), the two back to back {t_u:.1f} us; fused {t_f:.1f} us (overhead over the plain GEMM: fused "
             f"{t_f - t_m:+.1f} us, unfused {t_u - t_m:+.1f} us)")
         del sets, x, y
         torch.cuda.empty_cache()
