@@ -219,9 +219,9 @@ def test_monosoup_validation(bd):
     def a256(x):
         return (x + 255) // 256 * 256
 
-    # 8192 x 8192, k = 2, r = 32: 256 blocks of 64 per pass -> 8 splits of 16 steps
+    # 8192 x 8192, k = 2, r = 32: 256 blocks of 64 per pass -> 4 splits of 32 steps
     R = C = 8192
-    expect = (a256(2 * 64 * 8 * R * 4) + a256(2 * R * 64 * 4) + a256(2 * C * 64 * 4) + a256(2 * R * 64 * 4)
+    expect = (a256(2 * 64 * 4 * R * 4) + a256(2 * R * 64 * 4) + a256(2 * C * 64 * 4) + a256(2 * R * 64 * 4)
               + 2 * a256(2 * 64 * 64 * 64 * 8) + 4 * a256(2 * 64 * 64 * 8) + a256(R * 64 * 4) + a256(C * 64 * 4))
     assert W(R, C, 2, 32) == expect
     need = W(100, 96, 2, 8)
