@@ -624,7 +624,8 @@ def run_probes(torch, bd, reps=125):
     layer's weight size (34 MiB, 544 MiB in all, over the MALL) launched back
     to back from a HIP graph like the decode kernels, and on one 1 GiB
     buffer; and the dense bf16 MFMA rate of back-to-back register-operand
-    MFMAs on every CU (2 waves per SIMD)."""
+    MFMAs on every CU (2 waves per SIMD); and the LDS read, write and
+    direct-copy rates per CU."""
     dev = torch.device("cuda")
     P = ctypes.c_void_p
     out = {}
@@ -685,6 +686,31 @@ def run_probes(torch, bd, reps=125):
                         "frac_mfma": round(flop / us / 1e6 / BF16_PEAK_TFLOPS, 4), "flop": flop,
                         "kernel": "probe_mfma (v_mfma_f32_32x32x16_bf16 on registers, 2 waves per SIMD)"}
     log(f"context: MFMA probe: {flop / us / 1e6:.1f} TFLOP/s bf16 dense ({us:.1f} us)")
+    del sink
+    # LDS: one 16-wave workgroup per CU, every wave moving conflict-free
+    # contiguous blocks (reads of 16 / 8 bytes per lane, writes of 16, and
+    # direct-to-LDS copies of 16 from a 1 MiB L2-resident buffer); the rate
+    # per CU is each workgroup's bytes over its own shader-clock cycles
+    # (median over the workgroups), the whole-chip rate from the events
+    src = torch.empty((1 << 20) // 4, dtype=torch.int32, device=dev).random_()
+    blocks, iters = 256, 2048
+    lds = {}
+    for mode, name, unit in ((0, "read_b128", 1024), (1, "read_b64", 512), (2, "write_b128", 1024),
+                             (3, "copy_to_lds", 1024)):
+        sink, cycles = bd.probe_lds(blocks, 8, mode, 17, src if mode == 3 else None)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        sink, cycles = bd.probe_lds(blocks, iters, mode, 17, src if mode == 3 else None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        per_wg = 16 * iters * 8 * unit
+        cyc = float(cycles.cpu().double().median())
+        lds[name] = {"B/clk per CU": round(per_wg / cyc, 1), "TB/s": round(per_wg * blocks / us / 1e6, 2),
+                     "us": round(us, 1)}
+        log(f"context: LDS probe {name}: {per_wg / cyc:.1f} B/clock per CU, {per_wg * blocks / us / 1e6:.2f} TB/s")
+    out["lds"] = dict(lds, kernel="probe_lds (16 waves, one workgroup per CU, conflict-free blocks; clock "
+                                  "cycles from the shader clock counter)")
     return out
 
 

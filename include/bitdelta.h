@@ -281,9 +281,9 @@ BD_API bd_status bitdelta_monosoup(const bd_bf16 *w_base, const float *w_ft, con
 
 /* -------------------------------------------------------------- probes
  * Measurement utilities with no counterpart in the method: they give the
- * practical streaming-read rate and dense bf16 MFMA rate of the device, so
- * the method's kernels can be read against what the chip sustains as well as
- * against its published peaks.
+ * practical streaming-read rate, dense bf16 MFMA rate and LDS rates of the
+ * device, so the method's kernels can be read against what the chip sustains
+ * as well as against its published peaks.
  *
  * bitdelta_probe_read: reads `bytes` bytes at `src` once (16-byte streaming
  * loads, one 1 KB contiguous run per 64-lane instruction) and writes one
@@ -306,6 +306,31 @@ BD_API int64_t bitdelta_probe_read_sink_words(int64_t bytes);
 BD_API bd_status bitdelta_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 BD_API bd_status bitdelta_probe_mfma(int32_t blocks, int32_t iters, float a, float b, uint32_t *sink,
                                      void *stream);
+
+/* bitdelta_probe_lds: the LDS rates the kernels' on-chip staging is made of.
+ * `blocks` workgroups of 16 waves, one per CU (each declares 96 KB of LDS);
+ * each fills 64 KB of LDS with word i = i * 0x9E3779B1 (mod 2^32), then every
+ * wave w issues 8 * iters operations u = 0, 1, ..., each moving one
+ * contiguous block without bank conflicts:
+ *   mode 0: ds_read_b128 of the 1 KB block (u * stride + w) mod 64;
+ *   mode 1: ds_read_b64 of the 512-byte block (u * stride + w) mod 128;
+ *   mode 2: ds_write_b128 of 1 KB into block 4w + (u mod 4), lane l writing
+ *           the words u * 0x9E3779B1 + l, (u << 8) ^ l, u + l * 0x01000193,
+ *           ~(u ^ (l << 16)) (all mod 2^32);
+ *   mode 3: a direct-to-LDS copy (16 bytes per lane) of the 1 KB block
+ *           (u * stride + w) mod (src_bytes / 1024) of src into block
+ *           4w + (u mod 4).
+ * cycles[b] = shader-clock cycles of workgroup b between a barrier before the
+ * first operation and one after the last has completed;
+ * sink[b * 16 + w] = the XOR of every 32-bit word wave w read (modes 0, 1) or
+ * of the final content of its blocks 4w .. 4w + 3 (modes 2, 3).
+ *   mode in [0, 3] (BD_EINVAL); blocks in [1, 2^20], iters in [1, 2^16],
+ *   stride in [1, 2^20] (BD_ESHAPE); mode 3: src device, 16-byte aligned,
+ *   src_bytes a power of two in [1024, 2^30] (BD_ESHAPE), otherwise unused.
+ *   sink: device, 4-byte aligned, blocks * 16 words; cycles: device,
+ *   8-byte aligned, blocks words. */
+BD_API bd_status bitdelta_probe_lds(int32_t blocks, int32_t iters, int32_t mode, int32_t stride, const void *src,
+                                    int64_t src_bytes, uint32_t *sink, uint64_t *cycles, void *stream);
 
 #ifdef __cplusplus
 }

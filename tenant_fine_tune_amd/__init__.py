@@ -19,7 +19,7 @@ import ctypes
 import os
 
 __all__ = ["lib", "lib_path", "BitDeltaError", "compress", "reconstruct", "linear", "linear_grouped", "similarity",
-           "probe_read", "probe_mfma",
+           "probe_read", "probe_mfma", "probe_lds",
            "linear_grouped_noalloc", "similarity_delta", "monosoup", "MONOSOUP_SKETCH", "DeltaCache", "LOADER",
            "BD_OK", "BD_EINVAL", "BD_ESHAPE", "BD_EALIGN", "BD_EWORKSPACE", "BD_EDEVICE", "BD_EBUSY",
            "BD_CACHE_HIT", "BD_CACHE_MISS", "BD_CACHE_JOINED",
@@ -62,6 +62,7 @@ EXPORTS = {
     "bitdelta_probe_read_sink_words": (_I64, [_I64]),
     "bitdelta_probe_read": (_INT, [_P, _I64, _P, _P]),
     "bitdelta_probe_mfma": (_INT, [_I32, _I32, ctypes.c_float, ctypes.c_float, _P, _P]),
+    "bitdelta_probe_lds": (_INT, [_I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P]),
     # include/bitdelta_cache.h
     "bitdelta_cache_create": (_INT, [_I32, _I32, _I32, _I64, _P, _SZ, _P, _P, _P]),
     "bitdelta_cache_destroy": (None, [_P]),
@@ -372,6 +373,23 @@ def probe_mfma(blocks: int, iters: int, a: float = 1.0, b: float = 1.0, sink=Non
         sink = torch.empty((blocks * 4,), dtype=torch.float32, device=dev)
     check(lib.bitdelta_probe_mfma(blocks, iters, a, b, _ptr(sink), _stream(dev)))
     return sink
+
+
+def probe_lds(blocks: int, iters: int, mode: int, stride: int = 17, src=None, device=None):
+    """Measurement probe (no part of the method): LDS reads of 16 bytes per
+    lane (mode 0), of 8 bytes (mode 1), writes of 16 bytes (mode 2) or
+    direct-to-LDS copies of the device tensor `src` (mode 3, a power of two
+    from 1 KB to 1 GiB), each wave of `blocks` 16-wave workgroups moving
+    iters x 8 contiguous blocks (include/bitdelta.h).  Returns (sink int32
+    [blocks * 16], cycles int64 [blocks])."""
+    torch = _torch()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    sink = torch.empty((blocks * 16,), dtype=torch.int32, device=dev)
+    cycles = torch.empty((blocks,), dtype=torch.int64, device=dev)
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    check(lib.bitdelta_probe_lds(blocks, iters, mode, stride, _ptr(src) if src is not None else None, nbytes,
+                                 _ptr(sink), _ptr(cycles), _stream(dev)))
+    return sink, cycles
 
 
 class DeltaCache:

@@ -470,4 +470,27 @@ bd_status bitdelta_probe_mfma(int32_t blocks, int32_t iters, float a, float b, u
     return device(bd::launch_probe_mfma(blocks, iters, a, b, sink, (hipStream_t)stream), "bitdelta_probe_mfma");
 }
 
+bd_status bitdelta_probe_lds(int32_t blocks, int32_t iters, int32_t mode, int32_t stride, const void *src,
+                             int64_t src_bytes, uint32_t *sink, uint64_t *cycles, void *stream)
+{
+    if (mode < 0 || mode > 3)
+        return fail(BD_EINVAL, "probe_lds mode must be 0..3 (got %d)", mode);
+    if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 16) || stride < 1 || stride > (1 << 20))
+        return fail(BD_ESHAPE, "probe_lds needs blocks in [1, 2^20], iters in [1, 2^16], stride in [1, 2^20] "
+                               "(got %d, %d, %d)", blocks, iters, stride);
+    if (mode == 3) {
+        if (src_bytes < 1024 || src_bytes > ((int64_t)1 << 30) || (src_bytes & (src_bytes - 1)) != 0)
+            return fail(BD_ESHAPE, "probe_lds mode 3 needs src_bytes a power of two in [1 KB, 1 GiB] (got %lld)",
+                        (long long)src_bytes);
+        BD_NONNULL(src);
+        BD_ALIGNED(src, 16);
+    }
+    BD_NONNULL(sink);
+    BD_NONNULL(cycles);
+    BD_ALIGNED(sink, 4);
+    BD_ALIGNED(cycles, 8);
+    return device(bd::launch_probe_lds(blocks, iters, mode, stride, src, src_bytes, sink, cycles, (hipStream_t)stream),
+                  "bitdelta_probe_lds");
+}
+
 }  // extern "C"

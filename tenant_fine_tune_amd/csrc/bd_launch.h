@@ -92,5 +92,9 @@ hipError_t launch_monosoup(const uint16_t *w_base, const float *w_ft, const floa
 int64_t probe_read_sink_words(int64_t bytes);
 hipError_t launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma(int32_t blocks, int32_t iters, float a, float b, uint32_t *sink, hipStream_t s);
+// probe_lds writes blocks * 16 sink words and blocks cycle counts; mode 3
+// reads src (src_bytes a power of two from 1 KB to 1 GiB).
+hipError_t launch_probe_lds(int32_t blocks, int32_t iters, int32_t mode, int32_t stride, const void *src,
+                            int64_t src_bytes, uint32_t *sink, uint64_t *cycles, hipStream_t s);
 
 }  // namespace bd

@@ -330,3 +330,17 @@ def test_probe_validation(bd):
         assert m(blocks, iters, 1.0, 1.0, FAKE, None) == bd.BD_ESHAPE
     assert m(1, 1, 1.0, 1.0, None, None) == bd.BD_EINVAL
     assert m(1, 1, 1.0, 1.0, FAKE_ODD, None) == bd.BD_EALIGN
+    p = L.bitdelta_probe_lds
+    for mode in (-1, 4):
+        assert p(1, 1, mode, 1, FAKE, 1024, FAKE, FAKE, None) == bd.BD_EINVAL
+    for blocks, iters, stride in ((0, 1, 1), (2 ** 20 + 1, 1, 1), (1, 0, 1), (1, 2 ** 16 + 1, 1), (1, 1, 0),
+                                  (1, 1, 2 ** 20 + 1)):
+        assert p(blocks, iters, 0, stride, None, 0, FAKE, FAKE, None) == bd.BD_ESHAPE
+    for nbytes in (0, 512, 1536, 3 * 1024, 2 ** 31):
+        assert p(1, 1, 3, 1, FAKE, nbytes, FAKE, FAKE, None) == bd.BD_ESHAPE
+    assert p(1, 1, 3, 1, None, 1024, FAKE, FAKE, None) == bd.BD_EINVAL
+    assert p(1, 1, 3, 1, ctypes.c_void_p(4104), 1024, FAKE, FAKE, None) == bd.BD_EALIGN
+    assert p(1, 1, 0, 1, None, 0, None, FAKE, None) == bd.BD_EINVAL
+    assert p(1, 1, 0, 1, None, 0, FAKE, None, None) == bd.BD_EINVAL
+    assert p(1, 1, 0, 1, None, 0, FAKE_ODD, FAKE, None) == bd.BD_EALIGN
+    assert p(1, 1, 0, 1, None, 0, FAKE, ctypes.c_void_p(4100), None) == bd.BD_EALIGN
