@@ -837,7 +837,7 @@ def run_stack(torch, bd, synth, n_layers):
                         "frac_hbm": round(comp_bytes / comp_ms / 1e6 / HBM_PEAK_GBS, 4)}}
     widths = {name: d_in for name, _, d_in in st.shapes}
     outs = {name: d_out for name, d_out, _ in st.shapes}
-    for label, m, reps in (("prefill", 512, 3), ("decode", 1, 10)):
+    for label, m, reps in (("prefill", 512, 3), ("decode", 1, 10), ("decode_m4", 4, 10), ("decode_m16", 16, 10)):
         xs = {name: synth.device_activations(m, widths[name], seed=4, index=m + i) for i, name in enumerate(widths)}
         ys = {name: torch.empty((m, outs[name]), dtype=torch.bfloat16, device=dev) for name in outs}
         g = capture(torch, lambda s: st.forward(0, xs, ys, s))
@@ -1373,6 +1373,16 @@ def summarize_stack(trace_csv, n_layers=80):
               f"{statistics.median(v):8.2f} {b:11d} {b / avg / 1e3:7.1f}")
     print(f"pass: {tot_us / passes / 1e3:.3f} ms of kernel time for {tot_b / passes / 1e9:.2f} GB: "
           f"{tot_b / tot_us / 1e3:.1f} GB/s ({tot_b / tot_us / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
+    more = {}
+    for r in rows:
+        if re.search(r"gemv_rows|gemv_stream<[2-4], ", r["Kernel_Name"]):
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+            more.setdefault(k, []).append(dur(r))
+    if more:
+        print("decode m = 4 and m = 16 kernels, per (kernel, grid) (the grid tells the shape):")
+        print(f"{'kernel':44s} {'threads':>9s} {'n':>6s} {'avg us':>9s} {'median':>9s}")
+        for (k, g), v in more.items():
+            print(f"{k[:44]:44s} {g:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f}")
     pre = {}
     for r in rows:
         if re.search(r"gemm_tiles|splitk_reduce", r["Kernel_Name"]):

@@ -143,6 +143,8 @@ class Oracle:
         if w_base.shape[1] != C:
             raise ValueError("x / w_base width mismatch")
         rr = None if rows is None else _c(np.asarray(rows, dtype=np.int64), np.int64)
+        if rr is not None and rr.size and (rr.min() < 0 or rr.max() >= R):
+            raise ValueError(f"rows must lie in [0, {R})")
         n = R if rr is None else rr.shape[0]
         y = np.zeros((M, n), dtype=np.float64)
         sc = np.zeros((M, n), dtype=np.float64)
@@ -164,6 +166,8 @@ class Oracle:
         R = w_base.shape[0]
         V = signs.shape[0]
         rr = None if rows is None else _c(np.asarray(rows, dtype=np.int64), np.int64)
+        if rr is not None and rr.size and (rr.min() < 0 or rr.max() >= R):
+            raise ValueError(f"rows must lie in [0, {R})")
         n = R if rr is None else rr.shape[0]
         y = np.zeros((M, n), dtype=np.float64)
         sc = np.zeros((M, n), dtype=np.float64)

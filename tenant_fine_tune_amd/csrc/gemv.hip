@@ -19,8 +19,10 @@
 //    columns per step; lane l loads the 16 bytes of columns 8l..8l+7 of each
 //    row (every load instruction is 1 KB of one row, streamed past the
 //    caches), its sign byte, and the same columns of each token of x (L2
-//    hits; at m = 2..4 with x of at most 56 KB, from a copy of x made once
-//    per workgroup in LDS).  A ring of D register stages keeps D steps of
+//    hits; at m = 2..4 with x of at most 64 KB, from a copy of x made once
+//    per workgroup in LDS; at m = 3..4 with a larger x and d_in a multiple
+//    of 4096, gemv_rows instead: read from L2 per wave, x would cost 4 times
+//    the weights' bytes).  A ring of D register stages keeps D steps of
 //    loads in flight;
 //    the loop is a steady part (consume a stage, refill it D steps ahead) and
 //    a drain, every address valid or deliberately out of range, so no load
@@ -29,10 +31,11 @@
 //    packed W_eff pair meets every token in one v_dot2_f32_bf16; the RW * m
 //    per-lane sums are reduced across the wave by a reduce-scatter.
 //
-//  gemv_rows (m in 5..16, d_in a multiple of 4096, matrix cores): the memory
-//    side of gemv_stream at m = 1 -- each of 16 waves streams one whole row,
-//    1 KB per load -- with the token products on MFMA after a transpose of
-//    the workgroup's 16 rows of W_eff through LDS (its own comment below).
+//  gemv_rows (m in 5..16, and 3..4 with x above 64 KB; d_in a multiple of
+//    4096; matrix cores): the memory side of gemv_stream at m = 1 -- each of
+//    16 waves streams one or two whole rows, 1 KB per load -- with the token
+//    products on MFMA after a transpose of the workgroup's 16 or 32 rows of
+//    W_eff through LDS (its own comment below).
 //
 //  gemv_mfma (m in 5..16, other d_in): one workgroup of 8 waves per block of
 //    16 rows; the columns are cut into super-blocks of 128 and wave w takes
@@ -127,8 +130,8 @@ __global__ __launch_bounds__(512) void gemv_stream(const uint16_t *__restrict__ 
     if constexpr (XL) {
         // 1 KB chunk c of x (flat [m, K], a whole number of chunks since K is
         // a multiple of 512) -> LDS bytes [1024 c, +1024): wave w copies
-        // chunks w, w + kWaves, ...  The host bounds m * K * 2 by 56 KB, so
-        // a wave has at most 56 / kWaves of these in flight.
+        // chunks w, w + kWaves, ...  The host bounds m * K * 2 by 64 KB, so
+        // a wave has at most 64 / kWaves of these in flight.
         const int chunks = (int)(((int64_t)m * K * 2) >> 10);
         for (int c = wave; c < chunks; c += kWaves)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xs + c * 1024), 16, (uint32_t)(16 * lane),
@@ -362,32 +365,40 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 
 // ------------------------------------------------- m in 5..16, whole rows
 // gemv_rows (d_in a multiple of 4096): the memory side of gemv_stream at
-// m = 1 -- each of the 16 waves of a workgroup streams one row, 1 KB of
-// W_base per load instruction, a ring of 8 register stages of 512 columns --
-// with the token products on the matrix cores.  Every wave forms W_eff for
-// its row (lane l: columns 8l .. 8l + 7 of each step) and writes it to an
-// LDS tile of the workgroup's 16 rows, NB steps at a time; after one barrier
-// wave w reads, for each of those steps, the MFMA B operand of its 32-column
-// slice (lane (j, q): row j, columns 32w + 8q .. +7) and runs one
+// m = 1 -- each of the 16 waves of a workgroup streams RW whole rows (rows
+// w, w + 16, ...), 1 KB of W_base per load instruction, a ring of D register
+// stages of 512 columns -- with the token products on the matrix cores.
+// Every wave forms W_eff for its rows (lane l: columns 8l .. 8l + 7 of each
+// step) and writes it to an LDS tile of the workgroup's 16 RW rows, NB steps
+// at a time; after one barrier wave w reads, for each of those steps and each
+// block of 16 rows, the MFMA B operand of its 32-column slice (lane (j, q):
+// row j of the block, columns 32w + 8q .. +7) and runs one
 // v_mfma_f32_16x16x32_bf16 with A = the same columns of the 16 tokens (L2
-// reads, prefetched with the stage).  16-byte chunk c of row j sits at LDS
-// position c ^ j, so the tile's writes (one row per wave) and the fragment
-// reads (16 rows per read) are both free of bank conflicts.  The 16 waves'
-// partial 16 x 16 tiles (disjoint column slices) are summed through LDS in
-// wave order.  Measured on 4096 x 4096 at m = 16 (same box, the previous
-// kernel 10.85 us): one barrier per step 10.45 us, per 2 steps 10.0, per 4
-// steps 9.75, per 8 steps 9.6 with the rotated step order below (10.0
-// without it).
+// reads, prefetched with the stage, shared by the RW blocks).  16-byte chunk
+// c of row j sits at LDS position c ^ (j mod 16), so the tile's writes (one
+// row per wave) and the fragment reads (16 rows per read) are both free of
+// bank conflicts.  The 16 waves' partial 16 x 16 tiles (disjoint column
+// slices) are summed through LDS in wave order.  Two plans:
+//  - rows of 4096 (one ring of D = 8 stages holds the row): RW = 1, the
+//    whole ring in one barrier group (NB = 8) and one tile buffer.  Measured
+//    on 4096 x 4096 at m = 16 (same box): one barrier per step 10.45 us, per
+//    2 steps 10.0, per 4 steps 9.75, per 8 steps 9.6 with the rotated step
+//    order below (10.0 without it).
+//  - longer rows, at least kRowsPairMin of them: RW = 2 (x read once per 32
+//    rows instead of 16), D = 4, groups of NB = 2 steps into two tile
+//    buffers, so one barrier per group and the other half of the ring's
+//    loads in flight while a group is formed and multiplied.  At m = 16 (same
+//    box, us): 8192 x 8192 40.5 -> 31.1, 28672 x 8192 128 -> 106, 8192 x
+//    28672 123 -> 93 (32-row blocks alone: 33.6 / 117 / 114).
 constexpr int kRowsWaves = 16;
-// Steps per barrier: W_eff of NB steps goes into LDS before one barrier, then
-// their NB MFMAs run (tile: NB steps x 16 rows x 1 KB, one buffer, so a later
-// group first waits for the previous group's reads).  Workgroup b walks its
-// row's steps starting at step b mod S, so the workgroups in flight read
-// different columns of x (and of their rows) at any moment instead of all the
-// same ones.
+// Workgroup b walks its rows' steps starting at step b mod S, so the
+// workgroups in flight read different columns of x (and of their rows) at
+// any moment instead of all the same ones.
 constexpr int kRowsNB = 8;
+// Rows from which the two-row plan still gives every CU a workgroup.
+constexpr int64_t kRowsPairMin = 32 * 256;
 
-template <int D, bool PER_MATRIX>
+template <int D, int NB, int RW, int NBUF, bool PER_MATRIX>
 __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__restrict__ x, int m,
                                                              const uint16_t *__restrict__ w_base,
                                                              const uint8_t *__restrict__ signs,
@@ -395,56 +406,81 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
                                                              int64_t K, uint16_t *__restrict__ y, int64_t ldy)
 {
     constexpr int NW = kRowsWaves;
-    constexpr int NB = kRowsNB;
     static_assert(D % NB == 0, "the stage ring holds whole barrier groups");
+    static_assert(NBUF == 1 || NBUF == 2, "one tile buffer, or two used in turn");
     __shared__ __attribute__((aligned(16))) float sgn[64];
-    __shared__ uint4 tile[NB][NW][64];  // W_eff of NB steps: [step][row][chunk position]
+    // W_eff of NB steps: [buffer][step][row][chunk position]
+    __shared__ uint4 tile[NBUF][NB][NW * RW][64];
     fill_sign_table(sgn);
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15, q = lane >> 4;  // fragment lane: row / token j, k-chunk q
-    const int64_t n0 = (int64_t)blockIdx.x * NW;
-    const int64_t row = n0 + wave;
+    const int64_t n0 = (int64_t)blockIdx.x * NW * RW;
     const int64_t G = K >> 3;
     const int S = (int)(G >> 6);  // 512-column steps (K % 512 == 0)
     const int rot = (int)(blockIdx.x % (unsigned)S);
-    const bool ok = row < R;
-    const float a = PER_MATRIX ? alpha[0] : alpha[ok ? row : R - 1];
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);
     // rows past R and tokens past m use the out-of-range lane offset (zeros);
     // the scalar offset (the step) stays inside a valid row
-    const uint32_t wrow = ok ? (uint32_t)(row * K * 2 + 16 * lane) : kInvalidOffset;
-    const uint32_t srow = ok ? (uint32_t)(row * G + lane) : kInvalidOffset;
+    uint32_t wrow[RW], srow[RW];
+    float a[RW];
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+        const int64_t row = n0 + wave + 16 * k;
+        const bool ok = row < R;
+        a[k] = PER_MATRIX ? alpha[0] : alpha[ok ? row : R - 1];
+        wrow[k] = ok ? (uint32_t)(row * K * 2 + 16 * lane) : kInvalidOffset;
+        srow[k] = ok ? (uint32_t)(row * G + lane) : kInvalidOffset;
+    }
     const uint32_t xoff = j < m ? (uint32_t)(j * K * 2 + (32 * wave + 8 * q) * 2) : kInvalidOffset;
 
-    uint4 wq[D], xq[D];
-    uint32_t sq[D];
+    uint4 wq[D][RW], xq[D];
+    uint32_t sq[D][RW];
     auto load = [&](int d, int s) {
         int c = s + rot;  // the step's columns
         c = c >= S ? c - S : c;
-        wq[d] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wrow, (uint32_t)c * 1024u, kStream));
-        sq[d] = __builtin_amdgcn_raw_buffer_load_b8(rs, srow, (uint32_t)c * 64u, kStream);
+#pragma unroll
+        for (int k = 0; k < RW; ++k) {
+            wq[d][k] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, wrow[k], (uint32_t)c * 1024u, kStream));
+            sq[d][k] = __builtin_amdgcn_raw_buffer_load_b8(rs, srow[k], (uint32_t)c * 64u, kStream);
+        }
         xq[d] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, (uint32_t)c * 1024u, 0));
     };
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[RW];
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+        acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // steps s .. s + NB - 1 held in stages d .. d + NB - 1: every row's W_eff
     // into the tile, one barrier, then each wave's MFMAs.
     auto group = [&](int d, int s) {
-        if (s > 0)
-            __syncthreads();  // the previous group's reads of the tile are done
+        int buf = 0;
+        if constexpr (NBUF == 1) {
+            if (s > 0)
+                __syncthreads();  // the previous group's reads of the tile are done
+        } else {
+            // group s / NB takes buffer (s / NB) mod 2, last read by the group
+            // before the previous one: every wave finished those reads before
+            // it passed the previous group's barrier
+            buf = (s / NB) & 1;
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            tile[i][wave][lane ^ wave] = weff8(sgn, sq[d + i], wq[d + i], a);
+#pragma unroll
+            for (int k = 0; k < RW; ++k)
+                tile[buf][i][wave + 16 * k][lane ^ wave] = weff8(sgn, sq[d + i][k], wq[d + i][k], a[k]);
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const uint4 b = tile[i][j][(4 * wave + q) ^ j];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xq[d + i]),
-                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-        }
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int k = 0; k < RW; ++k) {
+                const uint4 b = tile[buf][i][16 * k + j][(4 * wave + q) ^ j];
+                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xq[d + i]),
+                                                                 __builtin_bit_cast(bf16x8, b), acc[k], 0, 0, 0);
+            }
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -468,19 +504,24 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
 
     // sum the waves' partial tiles in wave order (the tile holds them:
     // every read of the last group is done after this barrier)
+    static_assert(NBUF * NB >= 1, "the tile holds the NW * RW partial tiles");
     __syncthreads();
-    f32x4 *red = reinterpret_cast<f32x4 *>(&tile[0][0][0]);
-    red[wave * 64 + lane] = acc;
+    f32x4 *red = reinterpret_cast<f32x4 *>(&tile[0][0][0][0]);
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+        red[(wave * RW + k) * 64 + lane] = acc[k];
     __syncthreads();
-    if (threadIdx.x < 256) {
-        // D layout of the 16 x 16 tile: lane l holds tokens 4 (l / 16) + r of row l % 16
-        const int src = threadIdx.x >> 2, r = threadIdx.x & 3;
+    if (threadIdx.x < 256 * RW) {
+        // block k = threadIdx / 256; D layout of its 16 x 16 tile: lane l holds
+        // tokens 4 (l / 16) + r of row l % 16
+        const int k = threadIdx.x >> 8, t = threadIdx.x & 255;
+        const int src = t >> 2, r = t & 3;
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            v += red[w * 64 + src][r];
+            v += red[(w * RW + k) * 64 + src][r];
         const int tok = 4 * (src >> 4) + r;
-        const int64_t rr = n0 + (src & 15);
+        const int64_t rr = n0 + 16 * k + (src & 15);
         if (tok < m && rr < R)
             y[(int64_t)tok * ldy + rr] = to_bf16(v);
     }
@@ -511,7 +552,7 @@ struct Args {
 // x goes through LDS for MT >= kXLdsMinM tokens and at most kXLdsMax bytes.
 constexpr int kXLdsMinM = 2;
 // Largest x (m * d_in bf16) the m <= 4 kernels keep in LDS.
-constexpr int64_t kXLdsMax = 56 * 1024;
+constexpr int64_t kXLdsMax = 64 * 1024;
 
 template <int MT, int RW, int D>
 hipError_t launch_stream(const Args &g)
@@ -579,24 +620,33 @@ hipError_t launch_mfma(const Args &g)
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_rows_d(const Args &g)
-{
-    const dim3 grid((unsigned)((g.rows + kRowsWaves - 1) / kRowsWaves)), block(64 * kRowsWaves);
-    if (g.pm)
-        hipLaunchKernelGGL((gemv_rows<D, true>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, g.d_in, g.y,
-                           g.ldy);
-    else
-        hipLaunchKernelGGL((gemv_rows<D, false>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, g.rows, g.d_in, g.y,
-                           g.ldy);
-    return hipGetLastError();
-}
-
 // gemv_rows takes d_in a multiple of 4096: whole rings of 8 stages of 512
-// columns (the ring holds whole barrier groups of kRowsNB = 8 steps).
+// columns (the ring holds whole barrier groups of kRowsNB = 8 steps), or of 4
+// stages in the two-row plan.
 constexpr int kRowsDepth = 8;
 static_assert(kRowsDepth % kRowsNB == 0, "the stage ring holds whole barrier groups");
 bool rows_shape(int64_t d_in) { return d_in % (512 * kRowsDepth) == 0; }
+
+hipError_t launch_rows(const Args &g)
+{
+    const dim3 block(64 * kRowsWaves);
+#define BD_ROWS(D, NB, RW, NBUF)                                                                                   \
+    do {                                                                                                            \
+        const dim3 grid((unsigned)((g.rows + kRowsWaves * RW - 1) / (kRowsWaves * RW)));                           \
+        if (g.pm)                                                                                                   \
+            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, true>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a,  \
+                               g.rows, g.d_in, g.y, g.ldy);                                                         \
+        else                                                                                                        \
+            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, false>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, \
+                               g.rows, g.d_in, g.y, g.ldy);                                                         \
+    } while (0)
+    if (g.d_in > 512 * kRowsDepth && g.rows >= kRowsPairMin)
+        BD_ROWS(4, 2, 2, 2);
+    else
+        BD_ROWS(kRowsDepth, kRowsNB, 1, 1);
+#undef BD_ROWS
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -616,10 +666,10 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
             e = dispatch_stream<1, 1>(g, 8);
         else if (m <= 2)
             e = dispatch_stream<2, 2>(g, 4);
-        else if (m <= 4)
-            e = dispatch_stream<4, 1>(g, 4);
+        else if (m <= 4 && !((int64_t)m * g.d_in * 2 > kXLdsMax && rows_shape(g.d_in)))
+            e = dispatch_stream<4, 1>(g, 4);  // x in LDS, or a width the whole-row kernel does not take
         else if (rows_shape(g.d_in))
-            e = launch_rows_d<kRowsDepth>(g);
+            e = launch_rows(g);
         else
             e = launch_mfma(g);
         if (e != hipSuccess)

@@ -86,35 +86,53 @@ def gemv_mfma_accesses(R, K, m, even):
     return out
 
 
-def gemv_rows_accesses(R, K, m):
-    """gemv_rows (d_in a multiple of 4096): 16 waves per 16-row workgroup,
-    wave w streams row n0 + w in 512-column steps (1 KB per instruction),
-    starting at step b mod S; lane (j, q) reads x[j][32 w + 8 q ..] of the
-    step's columns."""
+def gemv_rows_accesses(R, K, m, RW=1):
+    """gemv_rows (d_in a multiple of 4096): 16 waves per workgroup of 16 RW
+    rows, wave w streams rows n0 + w + 16 k (k < RW) in 512-column steps (1 KB
+    per instruction), starting at step b mod S; lane (j, q) reads
+    x[j][32 w + 8 q ..] of the step's columns."""
     assert K % 4096 == 0
     G, S = K // 8, K // 512
-    blocks = -(-R // 16)
+    blocks = -(-R // (16 * RW))
     b, w, l = np.meshgrid(np.arange(blocks), np.arange(16), np.arange(64), indexing="ij")
-    row = b * 16 + w
-    ok = row < R
-    wrow = np.where(ok, row * K * 2 + 16 * l, INV)
-    srow = np.where(ok, row * G + l, INV)
     j, q = l & 15, l >> 4
     xoff = np.where(j < m, j * K * 2 + (32 * w + 8 * q) * 2, INV)
     out = []
+    for k in range(RW):
+        row = b * 16 * RW + w + 16 * k
+        ok = row < R
+        wrow = np.where(ok, row * K * 2 + 16 * l, INV)
+        srow = np.where(ok, row * G + l, INV)
+        for s in range(S):
+            c = (s + b % S) % S
+            out.append(("W_base", wrow, c * 1024, 16, R * K * 2))
+            out.append(("signs", srow, c * 64, 1, R * G))
     for s in range(S):
         c = (s + b % S) % S
-        out.append(("W_base", wrow, c * 1024, 16, R * K * 2))
-        out.append(("signs", srow, c * 64, 1, R * G))
         out.append(("x", xoff, c * 1024, 16, m * K * 2))
     return out
 
 
-@pytest.mark.parametrize("R,K", [(1000, 4096), (33, 8192), (24, 4096), (7, 12288), (16, 4096), (1, 4096)])
-@pytest.mark.parametrize("m", [5, 13, 16])
+def gemv_rows_plan(R, K):
+    """Rows per wave the launcher picks: 2 for rows longer than one ring (4096)
+    when there are at least 8192 of them, else 1."""
+    return 2 if K > 4096 and R >= 32 * 256 else 1
+
+
+@pytest.mark.parametrize("R,K", [(1000, 4096), (33, 8192), (24, 4096), (7, 12288), (16, 4096), (1, 4096),
+                                 (8208, 8192), (8192, 12288), (8200, 8192)])
+@pytest.mark.parametrize("m", [3, 5, 13, 16])
 def test_gemv_rows_stays_in_bounds(R, K, m):
-    for name, vo, so, width, size in gemv_rows_accesses(R, K, m):
-        assert _violations(vo, so, width, size) == 0, (name, R, K, m)
+    RW = gemv_rows_plan(R, K)
+    for name, vo, so, width, size in gemv_rows_accesses(R, K, m, RW):
+        assert _violations(vo, so, width, size) == 0, (name, R, K, m, RW)
+
+
+@pytest.mark.parametrize("R,K", [(33, 8192), (7, 12288), (17, 8192), (1, 8192)])
+def test_gemv_rows_two_row_plan_stays_in_bounds_on_ragged_rows(R, K):
+    """The two-row addressing on row counts that leave partial 32-row blocks."""
+    for name, vo, so, width, size in gemv_rows_accesses(R, K, 16, 2):
+        assert _violations(vo, so, width, size) == 0, (name, R, K)
 
 
 @pytest.mark.parametrize("R,K", [(1, 8), (3, 520), (17, 1032), (5, 4096), (33, 1544), (64, 4104), (7, 24)])

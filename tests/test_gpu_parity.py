@@ -315,7 +315,7 @@ def _sample_rows(R, fixed, tag):
     smaller)."""
     if R <= SAMPLED_ROWS:
         return np.arange(R, dtype=np.int64)
-    chosen = set(int(r) for r in fixed)
+    chosen = set(int(r) for r in fixed if 0 <= r < R)
     extra = synth.u64(4 * SAMPLED_ROWS, 0, tag) % np.uint64(R)
     for r in extra:
         if len(chosen) >= SAMPLED_ROWS:
@@ -352,6 +352,50 @@ def test_identity_prefill_8192(bd):
     eye = torch.eye(C, dtype=torch.bfloat16, device="cuda")
     y = host_bits(bd.linear(eye, wd, sd, ad))
     assert same_bits_pm0(y, weff.T)
+
+
+# ------------------------------------------------- decode on long rows, full size
+
+# Decode plans that only long rows reach: x of m = 4 tokens up to 64 KB in LDS (8192 wide); m = 3..4
+# with a larger x on the whole-row MFMA kernel; at least 8192 rows of a width above 4096 on its two-row
+# plan (32-row workgroups, two tile buffers), whose last workgroup holds only 16 rows at 8208.
+LONG_DECODE = [((8208, 8192), 16, False), ((8208, 8192), 5, True), ((8192, 12288), 3, False),
+               ((8208, 8192), 4, True), ((8192, 12288), 4, False)]
+
+
+@pytest.mark.parametrize("case", LONG_DECODE, ids=lambda c: f"{c[0][0]}x{c[0][1]}_m{c[1]}_{'matrix' if c[2] else 'row'}")
+def test_linear_decode_long_rows(bd, case):
+    (R, C), M, per_matrix = case
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=5, index=M, per_matrix=per_matrix)
+    x = synth.activations(M, C, seed=5, index=M)
+    y = host_bits(bd.linear(bf16_dev(x), wd, sd, ad, per_matrix=per_matrix))
+    rows = _sample_rows(R, [0, 1, 15, 16, 31, 32, 33, 8191, 8192, R - 1, *range(0, R, R // 8)], 7000 + R + M)
+    y64, sc = oracle.linear(x, w_base, so, ao, per_matrix=per_matrix, rows=rows)
+    check_linear(y[:, rows], y64, sc, f"decode {R}x{C} m={M}")
+
+
+def test_dyadic_exact_two_row_plan(bd):
+    """Exact-arithmetic inputs through the two-row plan, bit for bit on the
+    sampled rows (the partial last workgroup included)."""
+    R, C, M = 8208, 8192, 16
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=77)
+    y = host_bits(bd.linear(bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])))
+    rows = _sample_rows(R, [0, 15, 16, 31, 32, 8191, 8192, 8207], 7777)
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0], rows=rows)
+    assert np.array_equal(synth.bf16_bits_to_f32(y[:, rows]).astype(np.float64), y64)
+
+
+@pytest.mark.parametrize("M,C", [(16, 8192), (4, 12288)], ids=lambda v: str(v))
+def test_identity_decode_two_row_plan(bd, M, C):
+    """One-hot x through the two-row plan: y[t, r] = W_eff[r, j_t] bit for bit on every row."""
+    R = 8208
+    w_base, so, ao, (wd, sd, ad) = _layer_dev(R, C, seed=8)
+    weff = oracle.reconstruct(w_base, so, ao)
+    cols = np.linspace(0, C - 1, M).astype(int)
+    x = np.zeros((M, C), dtype=np.float32)
+    x[np.arange(M), cols] = 1.0
+    y = host_bits(bd.linear(bf16_dev(synth.to_bf16_bits(x)), wd, sd, ad))
+    assert same_bits_pm0(y, weff[:, cols].T)
 
 
 # ------------------------------------------------------------------- grouped
@@ -517,10 +561,11 @@ def test_stack_full_80_layers(bd):
     14 packed delta sets, 257 GB, as the post's memory arithmetic has it):
     variant 0 compressed matrix by matrix from streamed fine-tuned weights,
     the other 13 random packed codes.  Compress is bit-exact on sampled rows of
-    layers 0 and 79; the fused linear at m = 512 (prefill) and m = 1 (decode)
-    matches the oracle on sampled output features of every matrix of layers 0
-    and 79, for variant 0 and for variant 9; a full pass through all 560
-    linears runs and gives finite outputs."""
+    layers 0 and 79; the fused linear at m = 512 (prefill) and m = 1, 4, 16
+    (decode: the stream, x-in-LDS and two-row plans on these shapes) matches
+    the oracle on sampled output features of every matrix of layers 0 and 79,
+    for variant 0 and for variant 9; a full pass through all 560 linears runs
+    and gives finite outputs."""
     from tenant_fine_tune_amd.stack import LinearStack
 
     torch.cuda.empty_cache()
@@ -564,7 +609,7 @@ def test_stack_full_80_layers(bd):
             print(f"stack 80 layers: layer {l + 1} filled and compressed", flush=True)
     widths = {name: d_in for name, _, d_in in st.shapes}
     outs = {name: d_out for name, d_out, _ in st.shapes}
-    for m in (512, 1):
+    for m in (512, 1, 4, 16):
         xs_h = {name: synth.activations(m, widths[name], seed=5, index=m + i) for i, name in enumerate(widths)}
         xs = {name: bf16_dev(a) for name, a in xs_h.items()}
         ys = {name: torch.empty((m, outs[name]), dtype=torch.bfloat16, device=dev) for name in outs}
