@@ -665,7 +665,10 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
         if (m <= 1)
             e = dispatch_stream<1, 1>(g, 8);
         else if (m <= 2)
-            e = dispatch_stream<2, 2>(g, 4);
+            // one row per wave when x sits in LDS; two when x comes from L2
+            // (its reads per weight byte halve)
+            e = (G % 64 == 0 && (int64_t)m * g.d_in * 2 <= kXLdsMax) ? dispatch_stream<2, 1>(g, 4)
+                                                                     : dispatch_stream<2, 2>(g, 4);
         else if (m <= 4 && !((int64_t)m * g.d_in * 2 > kXLdsMax && rows_shape(g.d_in)))
             e = dispatch_stream<4, 1>(g, 4);  // x in LDS, or a width the whole-row kernel does not take
         else if (rows_shape(g.d_in))

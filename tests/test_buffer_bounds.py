@@ -140,6 +140,8 @@ def test_gemv_rows_two_row_plan_stays_in_bounds_on_ragged_rows(R, K):
 def test_gemv_stream_stays_in_bounds(R, K, m):
     MT, RW, waves = {1: (1, 1, 4), 2: (2, 2, 8), 3: (4, 1, 8), 4: (4, 1, 8)}[m]
     even = (K // 8) % 64 == 0
+    if m == 2 and even and m * K * 2 <= 64 * 1024:
+        RW = 1  # x in LDS: one row per wave
     for name, vo, so, width, size in gemv_stream_accesses(R, K, m, MT, RW, waves, even):
         assert _violations(vo, so, width, size) == 0, (name, R, K, m)
 
