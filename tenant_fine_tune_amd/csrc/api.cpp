@@ -166,8 +166,14 @@ bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *signs, cons
 
 size_t bitdelta_linear_workspace(int64_t m, int64_t d_out, int64_t d_in)
 {
+    if (d_out <= 0 || d_in <= 0 || d_in % 8 != 0 || m < 1)
+        return 0;
+    // decode: only few rows of long width need one (split row steps); shapes
+    // the decode path rejects need none
+    if (m <= bd::kGemvMaxM)
+        return (int64_t)bd::kGemvMaxM * d_in * 2 >= ((int64_t)1 << 31) ? 0 : bd::gemv_workspace_bytes((int)m, d_out, d_in);
     // shapes the prefill path rejects need no workspace
-    if (m <= bd::kGemvMaxM || d_out <= 0 || d_in <= 0 || d_in % 8 != 0 || !operands_fit(m, d_out, d_in))
+    if (!operands_fit(m, d_out, d_in))
         return 0;
     return bd::gemm_workspace_bytes(m, d_out, d_in);
 }
@@ -205,7 +211,7 @@ bd_status bitdelta_linear(const bd_bf16 *x, int64_t m, const bd_bf16 *w_base, co
         // least 16 rows) through 32-bit buffer offsets.
         if ((int64_t)bd::kGemvMaxM * d_in * 2 >= ((int64_t)1 << 31))
             return fail(BD_ESHAPE, "decode linear needs 16 rows of W_base below 2 GiB (d_in=%lld)", (long long)d_in);
-        return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, s),
+        return device(bd::launch_gemv(x, (int)m, w_base, signs, alpha, per_matrix, d_out, d_in, y, workspace, s),
                       "bitdelta_linear (decode)");
     }
     if (!operands_fit(m, d_out, d_in))

@@ -19,9 +19,13 @@ hipError_t launch_reconstruct(const uint16_t *w_base, const uint8_t *signs, cons
 
 // gemv.hip: m in [1, 16]
 constexpr int kGemvMaxM = 16;
+// Few rows of long width split the row's steps over more workgroups; their
+// fp32 partial sums need gemv_workspace_bytes() of workspace (0 otherwise).
+int gemv_splits(int m, int64_t rows, int64_t d_in);
+size_t gemv_workspace_bytes(int m, int64_t rows, int64_t d_in);
 hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
-                       uint16_t *y, hipStream_t s);
+                       uint16_t *y, void *workspace, hipStream_t s);
 
 // gemm.hip: dense prefill GEMM and the grouped variant
 constexpr int kGemmBM = 256;

@@ -390,6 +390,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 //    loads in flight while a group is formed and multiplied.  At m = 16 (same
 //    box, us): 8192 x 8192 40.5 -> 31.1, 28672 x 8192 128 -> 106, 8192 x
 //    28672 123 -> 93 (32-row blocks alone: 33.6 / 117 / 114).
+//  - few rows (512 .. 2048, so at most 128 workgroups of 16) of at least
+//    8192 columns: the row's steps are cut into `splits` parts of whole
+//    4-stage rings, one workgroup per (row block, part), each writing fp32
+//    sums to the workspace; gemv_split_reduce adds the parts in part order.
 constexpr int kRowsWaves = 16;
 // Workgroup b walks its rows' steps starting at step b mod S, so the
 // workgroups in flight read different columns of x (and of their rows) at
@@ -398,12 +402,13 @@ constexpr int kRowsNB = 8;
 // Rows from which the two-row plan still gives every CU a workgroup.
 constexpr int64_t kRowsPairMin = 32 * 256;
 
-template <int D, int NB, int RW, int NBUF, bool PER_MATRIX>
+template <int D, int NB, int RW, int NBUF, bool SPLIT, bool PER_MATRIX>
 __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__restrict__ x, int m,
                                                              const uint16_t *__restrict__ w_base,
                                                              const uint8_t *__restrict__ signs,
                                                              const float *__restrict__ alpha, int64_t R,
-                                                             int64_t K, uint16_t *__restrict__ y, int64_t ldy)
+                                                             int64_t K, uint16_t *__restrict__ y, int64_t ldy,
+                                                             float *__restrict__ partial, int splits)
 {
     constexpr int NW = kRowsWaves;
     static_assert(D % NB == 0, "the stage ring holds whole barrier groups");
@@ -416,10 +421,16 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = lane & 15, q = lane >> 4;  // fragment lane: row / token j, k-chunk q
-    const int64_t n0 = (int64_t)blockIdx.x * NW * RW;
+    // SPLIT: workgroup b takes row block b mod nblk and the part b / nblk of
+    // the row's steps (the host makes every part a whole number of rings)
+    const int nblk = SPLIT ? (int)gridDim.x / splits : (int)gridDim.x;
+    const int blk = SPLIT ? (int)blockIdx.x % nblk : (int)blockIdx.x;
+    const int part = SPLIT ? (int)blockIdx.x / nblk : 0;
+    const int64_t n0 = (int64_t)blk * NW * RW;
     const int64_t G = K >> 3;
-    const int S = (int)(G >> 6);  // 512-column steps (K % 512 == 0)
-    const int rot = (int)(blockIdx.x % (unsigned)S);
+    const int S = (int)(G >> 6) / (SPLIT ? splits : 1);  // this workgroup's 512-column steps
+    const int s_first = part * S;
+    const int rot = blk % S;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     uint32_t sq[D][RW];
     auto load = [&](int d, int s) {
         int c = s + rot;  // the step's columns
-        c = c >= S ? c - S : c;
+        c = (c >= S ? c - S : c) + s_first;
 #pragma unroll
         for (int k = 0; k < RW; ++k) {
             wq[d][k] = __builtin_bit_cast(
@@ -522,9 +533,28 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
             v += red[(w * RW + k) * 64 + src][r];
         const int tok = 4 * (src >> 4) + r;
         const int64_t rr = n0 + 16 * k + (src & 15);
-        if (tok < m && rr < R)
-            y[(int64_t)tok * ldy + rr] = to_bf16(v);
+        if (tok < m && rr < R) {
+            if constexpr (SPLIT)
+                partial[((int64_t)part * m + tok) * R + rr] = v;
+            else
+                y[(int64_t)tok * ldy + rr] = to_bf16(v);
+        }
     }
+}
+
+// y[t][r] = bf16(sum over the parts, in part order, of partial[part][t][r]).
+__global__ __launch_bounds__(256) void gemv_split_reduce(const float *__restrict__ partial, int splits, int m,
+                                                         int64_t R, uint16_t *__restrict__ y, int64_t ldy)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)m * R)
+        return;
+    const int tok = (int)(i / R);
+    const int64_t r = i - (int64_t)tok * R;
+    float v = 0.0f;
+    for (int p = 0; p < splits; ++p)
+        v += partial[((int64_t)p * m + tok) * R + r];
+    y[(int64_t)tok * ldy + r] = to_bf16(v);
 }
 
 // ---------------------------------------------------------------- launch
@@ -627,34 +657,77 @@ constexpr int kRowsDepth = 8;
 static_assert(kRowsDepth % kRowsNB == 0, "the stage ring holds whole barrier groups");
 bool rows_shape(int64_t d_in) { return d_in % (512 * kRowsDepth) == 0; }
 
-hipError_t launch_rows(const Args &g)
+hipError_t launch_rows(const Args &g, int splits, float *partial)
 {
     const dim3 block(64 * kRowsWaves);
-#define BD_ROWS(D, NB, RW, NBUF)                                                                                   \
+#define BD_ROWS(D, NB, RW, NBUF, SPLIT, NSPLIT)                                                                    \
     do {                                                                                                            \
-        const dim3 grid((unsigned)((g.rows + kRowsWaves * RW - 1) / (kRowsWaves * RW)));                           \
+        const dim3 grid((unsigned)((g.rows + kRowsWaves * RW - 1) / (kRowsWaves * RW) * NSPLIT));                  \
         if (g.pm)                                                                                                   \
-            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, true>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a,  \
-                               g.rows, g.d_in, g.y, g.ldy);                                                         \
+            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, SPLIT, true>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, \
+                               g.a, g.rows, g.d_in, g.y, g.ldy, partial, NSPLIT);                                   \
         else                                                                                                        \
-            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, false>), grid, block, 0, g.s, g.x, g.m, g.w, g.sg, g.a, \
-                               g.rows, g.d_in, g.y, g.ldy);                                                         \
+            hipLaunchKernelGGL((gemv_rows<D, NB, RW, NBUF, SPLIT, false>), grid, block, 0, g.s, g.x, g.m, g.w,      \
+                               g.sg, g.a, g.rows, g.d_in, g.y, g.ldy, partial, NSPLIT);                             \
     } while (0)
-    if (g.d_in > 512 * kRowsDepth && g.rows >= kRowsPairMin)
-        BD_ROWS(4, 2, 2, 2);
-    else
-        BD_ROWS(kRowsDepth, kRowsNB, 1, 1);
+    if (splits > 1) {
+        BD_ROWS(4, 4, 1, 1, true, splits);
+        const int64_t n = (int64_t)g.m * g.rows;
+        hipLaunchKernelGGL(gemv_split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, g.s, partial, splits,
+                           g.m, g.rows, g.y, g.ldy);
+    } else if (g.d_in > 512 * kRowsDepth && g.rows >= kRowsPairMin) {
+        BD_ROWS(4, 2, 2, 2, false, 1);
+    } else {
+        BD_ROWS(kRowsDepth, kRowsNB, 1, 1, false, 1);
+    }
 #undef BD_ROWS
     return hipGetLastError();
+}
+
+// Does launch_gemv take the whole-row kernel for this m and width?
+bool uses_rows(int m, int64_t d_in)
+{
+    if (m <= 2 || !rows_shape(d_in))
+        return false;
+    return m > 4 || (int64_t)m * d_in * 2 > kXLdsMax;
 }
 
 }  // namespace
 
 // Rows are launched in chunks whose W_base stays below 2 GiB (the kernels
 // address it with 32-bit buffer offsets); y keeps its full row stride.
+int gemv_splits(int m, int64_t rows, int64_t d_in)
+{
+    if (m < 1 || m > kGemvMaxM || !uses_rows(m, d_in) || d_in < 8192)
+        return 1;
+    const int64_t blocks = (rows + kRowsWaves - 1) / kRowsWaves;
+    // (and one launch chunk: W_base well below 2 GiB)
+    if (rows < 512 || blocks > 128 || rows * d_in * 2 >= ((int64_t)1 << 30))
+        return 1;
+    // the fewest parts that give about one workgroup per CU, each part a whole
+    // number of 4-stage rings
+    const int S = (int)(d_in / 512);
+    const int target = (int)((256 + blocks - 1) / blocks);
+    int best = 1;
+    for (int sp = 2; sp <= S / 4; ++sp) {
+        if (S % sp != 0 || (S / sp) % 4 != 0)
+            continue;
+        best = sp;
+        if (sp >= target)
+            break;
+    }
+    return best;
+}
+
+size_t gemv_workspace_bytes(int m, int64_t rows, int64_t d_in)
+{
+    const int sp = gemv_splits(m, rows, d_in);
+    return sp > 1 ? (size_t)sp * (size_t)m * (size_t)rows * sizeof(float) : 0;
+}
+
 hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
-                       uint16_t *y, hipStream_t s)
+                       uint16_t *y, void *workspace, hipStream_t s)
 {
     const int64_t G = d_in >> 3;
     const int64_t max_rows = std::max<int64_t>(16, (((int64_t)1 << 31) - 1) / (d_in * 2) / 16 * 16);
@@ -672,7 +745,7 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
         else if (m <= 4 && !((int64_t)m * g.d_in * 2 > kXLdsMax && rows_shape(g.d_in)))
             e = dispatch_stream<4, 1>(g, 4);  // x in LDS, or a width the whole-row kernel does not take
         else if (rows_shape(g.d_in))
-            e = launch_rows(g);
+            e = launch_rows(g, gemv_splits(m, g.rows, d_in), static_cast<float *>(workspace));
         else
             e = launch_mfma(g);
         if (e != hipSuccess)

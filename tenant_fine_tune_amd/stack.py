@@ -60,8 +60,10 @@ class LinearStack:
         self._lin_ws = torch.empty((1,), dtype=torch.uint8, device=self.device)
 
     def reserve(self, m: int) -> None:
-        """Size the linear workspace (split-K partials) for inputs of up to m rows."""
-        need = max(lib.bitdelta_linear_workspace(mm, d_out, d_in) for mm in (m,) for _, d_out, d_in in self.shapes)
+        """Size the linear workspace (split partial sums) for inputs of up to m
+        rows and for every decode width (1..16 rows)."""
+        need = max(lib.bitdelta_linear_workspace(mm, d_out, d_in) for mm in (m, *range(1, 17))
+                   for _, d_out, d_in in self.shapes)
         if need > self._lin_ws.numel():
             self._lin_ws = self.torch.empty((need,), dtype=self.torch.uint8, device=self.device)
 

@@ -125,7 +125,16 @@ def test_linear_split_k_workspace(bd):
     W = bd.lib.bitdelta_linear_workspace
     tile = 256 * 256 * 4
     narrow = 256 * 128 * 4
-    assert W(16, 64, 4096) == 0                    # decode path
+    assert W(16, 64, 4096) == 0                    # decode path: few rows of short width
+    # decode on 512..2048 rows of at least 8192 columns: the row's steps in parts, fp32 sums per part
+    assert W(16, 1024, 8192) == 4 * 16 * 1024 * 4
+    assert W(8, 2048, 8192) == 2 * 8 * 2048 * 4
+    assert W(16, 1000, 28672) == 7 * 16 * 1000 * 4
+    assert W(3, 1024, 28672) == 7 * 3 * 1024 * 4   # m = 3 with x above 64 KB: the whole-row kernel
+    assert W(4, 1024, 8192) == 0 and W(2, 1024, 8192) == 0 and W(1, 1024, 8192) == 0   # stream kernels
+    assert W(16, 511, 8192) == 0 and W(16, 2049, 8192) == 0 and W(16, 1024, 4096) == 0
+    f = bd.lib.bitdelta_linear
+    assert f(FAKE, 16, FAKE, FAKE, FAKE, 0, 1024, 8192, FAKE, None, 0, None) == bd.BD_EWORKSPACE
     assert W(2048, 8192, 8192) == 0                # 256 tiles fill the chip
     assert W(2048, 8192, 28672) == 0
     assert W(2048, 28672, 8192) == 2 * 128 * tile  # 896 tiles: last 128 in 2 K ranges

@@ -86,31 +86,52 @@ def gemv_mfma_accesses(R, K, m, even):
     return out
 
 
-def gemv_rows_accesses(R, K, m, RW=1):
+def gemv_rows_accesses(R, K, m, RW=1, splits=1):
     """gemv_rows (d_in a multiple of 4096): 16 waves per workgroup of 16 RW
     rows, wave w streams rows n0 + w + 16 k (k < RW) in 512-column steps (1 KB
     per instruction), starting at step b mod S; lane (j, q) reads
-    x[j][32 w + 8 q ..] of the step's columns."""
+    x[j][32 w + 8 q ..] of the step's columns.  With splits > 1, workgroup
+    (block b, part p) walks steps p S' .. p S' + S' - 1 (S' = S / splits)
+    starting at p S' + b mod S'."""
     assert K % 4096 == 0
     G, S = K // 8, K // 512
+    assert S % splits == 0
+    Sp = S // splits
     blocks = -(-R // (16 * RW))
     b, w, l = np.meshgrid(np.arange(blocks), np.arange(16), np.arange(64), indexing="ij")
     j, q = l & 15, l >> 4
     xoff = np.where(j < m, j * K * 2 + (32 * w + 8 * q) * 2, INV)
     out = []
-    for k in range(RW):
-        row = b * 16 * RW + w + 16 * k
-        ok = row < R
-        wrow = np.where(ok, row * K * 2 + 16 * l, INV)
-        srow = np.where(ok, row * G + l, INV)
-        for s in range(S):
-            c = (s + b % S) % S
-            out.append(("W_base", wrow, c * 1024, 16, R * K * 2))
-            out.append(("signs", srow, c * 64, 1, R * G))
-    for s in range(S):
-        c = (s + b % S) % S
-        out.append(("x", xoff, c * 1024, 16, m * K * 2))
+    for p in range(splits):
+        steps = [p * Sp + (s + b % Sp) % Sp for s in range(Sp)]
+        for k in range(RW):
+            row = b * 16 * RW + w + 16 * k
+            ok = row < R
+            wrow = np.where(ok, row * K * 2 + 16 * l, INV)
+            srow = np.where(ok, row * G + l, INV)
+            for c in steps:
+                out.append(("W_base", wrow, c * 1024, 16, R * K * 2))
+                out.append(("signs", srow, c * 64, 1, R * G))
+        for c in steps:
+            out.append(("x", xoff, c * 1024, 16, m * K * 2))
     return out
+
+
+def gemv_splits(m, R, K):
+    """The launcher's split count for few rows of long width (1 = none)."""
+    if not (m > 4 or (m > 2 and m * K * 2 > 64 * 1024)) or K % 4096 or K < 8192:
+        return 1
+    blocks = -(-R // 16)
+    if R < 512 or blocks > 128 or R * K * 2 >= 1 << 30:
+        return 1
+    S, target, best = K // 512, -(-256 // blocks), 1
+    for sp in range(2, S // 4 + 1):
+        if S % sp or (S // sp) % 4:
+            continue
+        best = sp
+        if sp >= target:
+            break
+    return best
 
 
 def gemv_rows_plan(R, K):
@@ -126,6 +147,16 @@ def test_gemv_rows_stays_in_bounds(R, K, m):
     RW = gemv_rows_plan(R, K)
     for name, vo, so, width, size in gemv_rows_accesses(R, K, m, RW):
         assert _violations(vo, so, width, size) == 0, (name, R, K, m, RW)
+
+
+@pytest.mark.parametrize("R,K,m,splits", [(1024, 8192, 16, 4), (1000, 28672, 16, 7), (512, 8192, 5, 4),
+                                          (2048, 8192, 8, 2), (1000, 28672, 3, 7), (1025, 12288, 16, 6)])
+def test_gemv_rows_split_stays_in_bounds(R, K, m, splits):
+    """Few rows: the row's steps in parts of whole rings, every part's scalar
+    offsets inside the row; the plan's split count is the one modelled."""
+    assert gemv_splits(m, R, K) == splits
+    for name, vo, so, width, size in gemv_rows_accesses(R, K, m, 1, splits):
+        assert _violations(vo, so, width, size) == 0, (name, R, K, m, splits)
 
 
 @pytest.mark.parametrize("R,K", [(33, 8192), (7, 12288), (17, 8192), (1, 8192)])

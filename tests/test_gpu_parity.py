@@ -119,7 +119,8 @@ DECODE_CASES = [((256, 512), m) for m in (1, 2, 3, 4, 5, 8, 9, 16)] + \
                [((300, 200), 3), ((7, 8), 16), ((1000, 1032), 7), ((33, 24), 1)] + \
                [((1000, 1024), 9), ((512, 8192), 16), ((1000, 28672), 16), ((300, 28672), 1),  # the kernels' steady loops, D = 1
                 ((300, 28672), 4), ((40, 8704), 2), ((1000, 6144), 12)] + \
-               [((1000, 4096), 13), ((33, 8192), 5), ((24, 4096), 16), ((7, 12288), 8)]  # whole-row MFMA kernel
+               [((1000, 4096), 13), ((33, 8192), 5), ((24, 4096), 16), ((7, 12288), 8)] + \
+               [((1024, 8192), 8), ((2048, 8192), 5), ((1000, 28672), 3), ((1025, 12288), 16)]  # row steps in parts
 
 
 @pytest.mark.parametrize("per_matrix", [False, True], ids=["alpha_row", "alpha_matrix"])
@@ -165,9 +166,10 @@ def test_linear_3d_input_and_determinism(bd):
     check_linear(host_bits(y1.view(300, R)), y64, sc, "3d input")
 
 
-# (m, d_in): d_in = 1032 takes the ragged-step kernels; the others, whole
-# 512-column steps with x small enough to sit in LDS (m = 2..4)
-@pytest.mark.parametrize("M,C", [(1, 1032), (16, 1032), (4, 4096), (2, 512), (3, 8704)],
+# (m, d_in): d_in = 1032 takes the ragged-step kernels; (4, 4096), (2, 512) and
+# (3, 8704), whole 512-column steps with x small enough to sit in LDS; (16, 8192)
+# and (3, 28672) on 1000 rows, the whole-row kernel with the row's steps in parts
+@pytest.mark.parametrize("M,C", [(1, 1032), (16, 1032), (4, 4096), (2, 512), (3, 8704), (16, 8192), (3, 28672)],
                          ids=lambda v: str(v))
 def test_identity_decode(bd, M, C):
     """One-hot x: y[t, r] must equal W_eff[r, j_t] bit for bit."""
@@ -372,6 +374,16 @@ def test_linear_decode_long_rows(bd, case):
     rows = _sample_rows(R, [0, 1, 15, 16, 31, 32, 33, 8191, 8192, R - 1, *range(0, R, R // 8)], 7000 + R + M)
     y64, sc = oracle.linear(x, w_base, so, ao, per_matrix=per_matrix, rows=rows)
     check_linear(y[:, rows], y64, sc, f"decode {R}x{C} m={M}")
+
+
+@pytest.mark.parametrize("R,C,M", [(1024, 8192, 16), (1000, 28672, 5)], ids=lambda v: str(v))
+def test_dyadic_exact_split_rows(bd, R, C, M):
+    """Exact-arithmetic inputs with the row's steps in parts (few rows, long
+    width): every output bit for bit."""
+    x, w_base, _, sb, alpha = pins.dyadic_case(M, R, C, seed=91)
+    y = host_bits(bd.linear(bf16_dev(x), bf16_dev(w_base), u8_dev(sb[0]), f32_dev(alpha[0])))
+    y64, _ = oracle.linear(x, w_base, sb[0], alpha[0])
+    assert np.array_equal(synth.bf16_bits_to_f32(y).astype(np.float64), y64)
 
 
 def test_dyadic_exact_two_row_plan(bd):
