@@ -121,9 +121,12 @@ BD_API bd_status bitdelta_reconstruct(const bd_bf16 *w_base, const uint8_t *sign
  * and y each below 2 GiB (BD_ESHAPE otherwise).
  * workspace: at least bitdelta_linear_workspace(m, d_out, d_in) bytes,
  * 16-byte aligned (may be NULL when that is 0).  It is non-zero only for
- * prefill shapes with few 256 x 256 output tiles, whose K loop is split:
- * fp32 partial sums (256 KB per tile and split) are kept there and summed in
- * split order, so the result does not depend on timing.  The caller owns it;
+ * prefill shapes with few 256 x 256 output tiles, whose K loop is split
+ * (fp32 partial sums, 256 KB per tile and split), and for decode on 512 to
+ * 2048 rows of at least 8192 columns with m >= 5 (or m = 3..4 with x above
+ * 64 KB), whose rows are walked in parts (fp32 sums, m * d_out * 4 bytes per
+ * part); either way the parts are summed in a fixed order, so the result
+ * does not depend on timing.  The caller owns it;
  * its contents are scratch on entry and undefined after the call, and two
  * calls in flight at once must not share one.  Too small: BD_EWORKSPACE; a
  * requirement of 2 GiB or more: BD_ESHAPE. */
