@@ -78,8 +78,8 @@ STEP_KERNELS = {
     "linear_m1_matrix": ("gemv.hip", [r"gemv_stream<1, 1, \d+, true, true, false>"]),
     "linear_m4_row": ("gemv.hip", [r"gemv_stream<4, 1, \d+, false, true, true>"]),
     "linear_m4_matrix": ("gemv.hip", [r"gemv_stream<4, 1, \d+, true, true, true>"]),
-    "linear_m16_row": ("gemv.hip", [r"gemv_rows<8, false>"]),
-    "linear_m16_matrix": ("gemv.hip", [r"gemv_rows<8, true>"]),
+    "linear_m16_row": ("gemv.hip", [r"gemv_rows<8, 8, 1, 1, false, false>"]),
+    "linear_m16_matrix": ("gemv.hip", [r"gemv_rows<8, 8, 1, 1, false, true>"]),
 }
 STEP = [f"linear_m{m}_{mode}" for mode in ("row", "matrix") for m in DECODE_M]
 OFFLINE = ["compress_row", "compress_matrix", "reconstruct"]
@@ -1373,16 +1373,39 @@ def summarize_stack(trace_csv, n_layers=80):
               f"{statistics.median(v):8.2f} {b:11d} {b / avg / 1e3:7.1f}")
     print(f"pass: {tot_us / passes / 1e3:.3f} ms of kernel time for {tot_b / passes / 1e9:.2f} GB: "
           f"{tot_b / tot_us / 1e3:.1f} GB/s ({tot_b / tot_us / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
-    more = {}
+    # the m = 4 and m = 16 passes: one call per linear, in the same order; a
+    # call on few long rows is the whole-row kernel plus gemv_split_reduce
+    calls = []
     for r in rows:
-        if re.search(r"gemv_rows|gemv_stream<[2-4], ", r["Kernel_Name"]):
-            k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))
-            more.setdefault(k, []).append(dur(r))
-    if more:
-        print("decode m = 4 and m = 16 kernels, per (kernel, grid) (the grid tells the shape):")
-        print(f"{'kernel':44s} {'threads':>9s} {'n':>6s} {'avg us':>9s} {'median':>9s}")
-        for (k, g), v in more.items():
-            print(f"{k[:44]:44s} {g:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f}")
+        name = r["Kernel_Name"]
+        if re.search(r"gemv_rows|gemv_stream<[2-4], ", name):
+            calls.append([_short(name), dur(r)])
+        elif "gemv_split_reduce" in name and calls:
+            calls[-1][0] += " + reduce"
+            calls[-1][1] += dur(r)
+    if calls and len(calls) % per_pass == 0:
+        by_m = {4: [], 16: []}
+        for p0 in range(0, len(calls), per_pass):
+            by_m[4 if "gemv_stream" in calls[p0][0] else 16].extend(calls[p0:p0 + per_pass])
+        for m, cs in by_m.items():
+            if not cs:
+                continue
+            passes_m = len(cs) // per_pass
+            print(f"decode m = {m}: {passes_m} passes x {per_pass} linears")
+            print(f"{'linear':8s} {'d_out':>6s} {'d_in':>6s} {'kernel':40s} {'n':>6s} {'avg us':>8s} {'median':>8s} "
+                  f"{'bytes':>11s} {'GB/s':>7s}")
+            t_us = t_b = 0.0
+            for j, (name, d_out, d_in) in enumerate(LAYER_SHAPES):
+                sel = cs[j::len(LAYER_SHAPES)]
+                v = [c[1] for c in sel]
+                b = d_out * d_in * 2 + d_out * d_in // 8 + 4 * d_out + 2 * m * d_in + 2 * m * d_out
+                avg = statistics.mean(v)
+                t_us += sum(v)
+                t_b += b * len(v)
+                print(f"{name:8s} {d_out:6d} {d_in:6d} {sel[0][0][:40]:40s} {len(v):6d} {avg:8.2f} "
+                      f"{statistics.median(v):8.2f} {b:11d} {b / avg / 1e3:7.1f}")
+            print(f"pass: {t_us / passes_m / 1e3:.3f} ms of kernel time for {t_b / passes_m / 1e9:.2f} GB: "
+                  f"{t_b / t_us / 1e3:.1f} GB/s ({t_b / t_us / 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
     pre = {}
     for r in rows:
         if re.search(r"gemm_tiles|splitk_reduce", r["Kernel_Name"]):

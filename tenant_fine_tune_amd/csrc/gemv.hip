@@ -551,9 +551,21 @@ __global__ __launch_bounds__(256) void gemv_split_reduce(const float *__restrict
         return;
     const int tok = (int)(i / R);
     const int64_t r = i - (int64_t)tok * R;
+    const float *src = partial + (int64_t)tok * R + r;
+    const int64_t stride = (int64_t)m * R;
+    // four parts' loads in flight at a time, added in part order
     float v = 0.0f;
-    for (int p = 0; p < splits; ++p)
-        v += partial[((int64_t)p * m + tok) * R + r];
+    int p = 0;
+    for (; p + 4 <= splits; p += 4) {
+        const float a0 = src[p * stride], a1 = src[(p + 1) * stride];
+        const float a2 = src[(p + 2) * stride], a3 = src[(p + 3) * stride];
+        v += a0;
+        v += a1;
+        v += a2;
+        v += a3;
+    }
+    for (; p < splits; ++p)
+        v += src[p * stride];
     y[(int64_t)tok * ldy + r] = to_bf16(v);
 }
 

@@ -104,8 +104,8 @@ def test_summarize_counters_scales_and_picks_the_step_grid(tmp_path):
              "linear_m1_matrix": ["gemv_stream<1, 1, 8, true, true, false>"],
              "linear_m4_row": ["gemv_stream<4, 1, 4, false, true, true>"],
              "linear_m4_matrix": ["gemv_stream<4, 1, 4, true, true, true>"],
-             "linear_m16_row": ["gemv_rows<8, false>"],
-             "linear_m16_matrix": ["gemv_rows<8, true>"]}
+             "linear_m16_row": ["gemv_rows<8, 8, 1, 1, false, false>"],
+             "linear_m16_matrix": ["gemv_rows<8, 8, 1, 1, false, true>"]}
     assert set(names) == set(bench.STEP_KERNELS)
     for entry, kernels in names.items():
         for k in kernels:
