@@ -706,8 +706,6 @@ bool uses_rows(int m, int64_t d_in)
 
 }  // namespace
 
-// Rows are launched in chunks whose W_base stays below 2 GiB (the kernels
-// address it with 32-bit buffer offsets); y keeps its full row stride.
 int gemv_splits(int m, int64_t rows, int64_t d_in)
 {
     if (m < 1 || m > kGemvMaxM || !uses_rows(m, d_in) || d_in < 8192)
@@ -737,12 +735,19 @@ size_t gemv_workspace_bytes(int m, int64_t rows, int64_t d_in)
     return sp > 1 ? (size_t)sp * (size_t)m * (size_t)rows * sizeof(float) : 0;
 }
 
+// Rows are launched in chunks whose W_base stays below 2 GiB (the kernels
+// address it with 32-bit buffer offsets); y keeps its full row stride.  The
+// split plan (and its workspace, sized for d_out) only ever applies to a
+// matrix launched whole.
 hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const uint8_t *signs,
                        const float *alpha, bool per_matrix, int64_t d_out, int64_t d_in,
                        uint16_t *y, void *workspace, hipStream_t s)
 {
     const int64_t G = d_in >> 3;
     const int64_t max_rows = std::max<int64_t>(16, (((int64_t)1 << 31) - 1) / (d_in * 2) / 16 * 16);
+    const int splits = d_out <= max_rows ? gemv_splits(m, d_out, d_in) : 1;
+    if (splits > 1 && workspace == nullptr)
+        return hipErrorInvalidValue;
     for (int64_t r0 = 0; r0 < d_out; r0 += max_rows) {
         Args g{x, m, w_base + r0 * d_in, signs + r0 * G, per_matrix ? alpha : alpha + r0, per_matrix,
                std::min(max_rows, d_out - r0), d_in, d_out, y + r0, s};
@@ -757,7 +762,7 @@ hipError_t launch_gemv(const uint16_t *x, int m, const uint16_t *w_base, const u
         else if (m <= 4 && !((int64_t)m * g.d_in * 2 > kXLdsMax && rows_shape(g.d_in)))
             e = dispatch_stream<4, 1>(g, 4);  // x in LDS, or a width the whole-row kernel does not take
         else if (rows_shape(g.d_in))
-            e = launch_rows(g, gemv_splits(m, g.rows, d_in), static_cast<float *>(workspace));
+            e = launch_rows(g, splits, static_cast<float *>(workspace));
         else
             e = launch_mfma(g);
         if (e != hipSuccess)
