@@ -539,9 +539,10 @@ static_assert(kXBuf == kL * kPitch, "an exchange buffer fills one 64 x 65 array"
 // through LDS (the lanes of a group move contiguous bytes, 16 each, per
 // instruction), two buffers used in turn, one workgroup barrier per exchange.
 // Stops after a sweep whose largest relative inner product |g_p . g_q| /
-// (|g_p| |g_q|) was at most 1e-9 (the quadratic convergence of cyclic Jacobi
-// leaves the columns orthogonal to rounding after that sweep's rotations), or
-// after kJacobiSweeps sweeps.  Output: Vout[:, j] = the eigenvector of
+// (|g_p| |g_q|) was at most 1e-6 (the quadratic convergence of cyclic Jacobi
+// leaves the columns orthogonal to about 1e-12 after that sweep's rotations;
+// a threshold of 1e-9 ran one more sweep, 2.5% of a merge at 8192 x 8192),
+// or after kJacobiSweeps sweeps.  Output: Vout[:, j] = the eigenvector of
 // original column j, mu[j] its eigenvalue.  Every thread of the workgroup
 // takes part; Vout may alias M.
 __device__ void jacobi_onesided(const double (*M)[kPitch], double *xb, int *xid, int *red,
@@ -599,7 +600,7 @@ __device__ void jacobi_onesided(const double (*M)[kPitch], double *xb, int *xid,
         ga = sum_lanes<NL>(ga);
     };
     for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
-        bool more = false;   // a pair of this sweep had |g_p . g_q| > 1e-9 |g_p| |g_q|
+        bool more = false;  // a pair of this sweep had |g_p . g_q| > 1e-6 |g_p| |g_q|
         for (int Q = 32; Q >= 1; Q >>= 1) {
             if (Q < 32) {
                 const bool upper = (g & Q) != 0;
@@ -625,7 +626,7 @@ __device__ void jacobi_onesided(const double (*M)[kPitch], double *xb, int *xid,
                 double al, be, ga;
                 gram2(al, be, ga);
                 const double g2 = ga * ga, ab = al * be;
-                more |= g2 > 1e-18 * ab;
+                more |= g2 > 1e-12 * ab;
                 if (g2 > 1e-30 * ab) {
                     const double2 cs = half_angle_rotation(al, be, ga);
 #pragma unroll
