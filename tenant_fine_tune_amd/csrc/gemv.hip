@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 // c of row j sits at LDS position c ^ (j mod 16), so the tile's writes (one
 // row per wave) and the fragment reads (16 rows per read) are both free of
 // bank conflicts.  The 16 waves' partial 16 x 16 tiles (disjoint column
-// slices) are summed through LDS in wave order.  Two plans:
+// slices) are summed through LDS in wave order.  Three plans:
 //  - rows of 4096 (one ring of D = 8 stages holds the row): RW = 1, the
 //    whole ring in one barrier group (NB = 8) and one tile buffer.  Measured
 //    on 4096 x 4096 at m = 16 (same box): one barrier per step 10.45 us, per
@@ -388,12 +388,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 //    rows instead of 16), D = 4, groups of NB = 2 steps into two tile
 //    buffers, so one barrier per group and the other half of the ring's
 //    loads in flight while a group is formed and multiplied.  At m = 16 (same
-//    box, us): 8192 x 8192 40.5 -> 31.1, 28672 x 8192 128 -> 106, 8192 x
-//    28672 123 -> 93 (32-row blocks alone: 33.6 / 117 / 114).
+//    box, graph-timed, us): 8192 x 8192 37.4 -> 27.5, 28672 x 8192 119 -> 96,
+//    8192 x 28672 114 -> 86.
 //  - few rows (512 .. 2048, so at most 128 workgroups of 16) of at least
 //    8192 columns: the row's steps are cut into `splits` parts of whole
 //    4-stage rings, one workgroup per (row block, part), each writing fp32
-//    sums to the workspace; gemv_split_reduce adds the parts in part order.
+//    sums to the workspace; gemv_split_reduce adds the parts in part order
+//    (1024 x 8192 at m = 16: 16.2 -> 8.5 us).
 constexpr int kRowsWaves = 16;
 // Workgroup b walks its rows' steps starting at step b mod S, so the
 // workgroups in flight read different columns of x (and of their rows) at
