@@ -1082,12 +1082,22 @@ def traffic_for(entry):
     return e.get("bytes_per_launch")
 
 
+def _code_only(text):
+    """Source text without its comments and blank lines (a comment edit does
+    not change a kernel, so it does not retire the counter runs)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha(src):
-    """Hash of a kernel source file and the device headers it includes."""
+    """Hash of the code of a kernel source file and the device headers it
+    includes (comments left out)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tenant_fine_tune_amd", "csrc")
     for f in (src, "bd_device.h", "bd_launch.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
