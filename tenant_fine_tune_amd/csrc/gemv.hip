@@ -396,9 +396,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma(const uint16_t *__r
 //    sums to the workspace; gemv_split_reduce adds the parts in part order
 //    (1024 x 8192 at m = 16: 16.2 -> 8.5 us).
 constexpr int kRowsWaves = 16;
-// Workgroup b walks its rows' steps starting at step b mod S, so the
+// Workgroup b walks its rows' steps starting at step rot(b), so the
 // workgroups in flight read different columns of x (and of their rows) at
-// any moment instead of all the same ones.
+// any moment instead of all the same ones.  Consecutive workgroups land on
+// different XCDs (8, round robin).  One ring per row: rot = b mod S.  The
+// two-row plan adds b / 8, so the workgroups of one XCD also start apart
+// (same box, graph-timed, us: m = 16 8192 x 8192 27.2 -> 25.5, 28672 x 8192
+// 97.7 -> 91.4; m = 8 26.7 -> 24.1, 93.7 -> 88.4; 8192 x 28672 unchanged).
+// On 4096 x 4096 at m = 16 the same spread costs 9.28 -> 9.52 us.
 constexpr int kRowsNB = 8;
 // Rows from which the two-row plan still gives every CU a workgroup.
 constexpr int64_t kRowsPairMin = 32 * 256;
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gemv_rows(const uint16_t *__r
     const int64_t G = K >> 3;
     const int S = (int)(G >> 6) / (SPLIT ? splits : 1);  // this workgroup's 512-column steps
     const int s_first = part * S;
-    const int rot = blk % S;
+    const int rot = RW == 1 ? blk % S : (blk + (blk >> 3)) % S;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_base, R * K * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(signs, R * G);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)m * K * 2);

@@ -89,10 +89,10 @@ def gemv_mfma_accesses(R, K, m, even):
 def gemv_rows_accesses(R, K, m, RW=1, splits=1):
     """gemv_rows (d_in a multiple of 4096): 16 waves per workgroup of 16 RW
     rows, wave w streams rows n0 + w + 16 k (k < RW) in 512-column steps (1 KB
-    per instruction), starting at step b mod S; lane (j, q) reads
-    x[j][32 w + 8 q ..] of the step's columns.  With splits > 1, workgroup
-    (block b, part p) walks steps p S' .. p S' + S' - 1 (S' = S / splits)
-    starting at p S' + b mod S'."""
+    per instruction), starting at step b mod S (RW = 1) or (b + b // 8) mod S
+    (RW = 2); lane (j, q) reads x[j][32 w + 8 q ..] of the step's columns.
+    With splits > 1, workgroup (block b, part p) walks steps
+    p S' .. p S' + S' - 1 (S' = S / splits) starting at p S' + b mod S'."""
     assert K % 4096 == 0
     G, S = K // 8, K // 512
     assert S % splits == 0
@@ -103,7 +103,11 @@ def gemv_rows_accesses(R, K, m, RW=1, splits=1):
     xoff = np.where(j < m, j * K * 2 + (32 * w + 8 * q) * 2, INV)
     out = []
     for p in range(splits):
-        steps = [p * Sp + (s + b % Sp) % Sp for s in range(Sp)]
+        rot = b % Sp if RW == 1 else (b + (b >> 3)) % Sp
+        steps = [p * Sp + (s + rot) % Sp for s in range(Sp)]
+        # every workgroup visits each of its part's steps once
+        assert np.array_equal(np.sort(np.stack([st[:, 0, 0] for st in steps]), axis=0),
+                              np.broadcast_to(p * Sp + np.arange(Sp)[:, None], (Sp, blocks)))
         for k in range(RW):
             row = b * 16 * RW + w + 16 * k
             ok = row < R
